@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for the LatentMoE layer forward.
+
+This package builds INPUTS ONLY (tokens, weights, router bias) from a
+counter-based SplitMix64 stream + Box-Muller normals, rounded to the storage
+dtype.  It holds none of the layer's arithmetic.  It is the one module that
+both the fp64 oracle (``oracle/``) and the GPU library's tests and benchmark
+use, so that both sides see bit-identical inputs.
+
+Tensor stream ids: x = 0, W_down = 1, W_router = 2, W1 = 3, W2 = 4, W_up = 5,
+router-bias permutation = 6.  Every weight ~ N(0, 1/fan_in); x ~ N(0, 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+from .workloads import LayerSpec, WORKLOADS, workload  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+_lock = threading.Lock()
+_lib = None
+
+TID_X, TID_WDOWN, TID_WROUTER, TID_W1, TID_W2, TID_WUP, TID_BIAS = range(7)
+
+
+def build(force: bool = True) -> str:
+    """Compile synth.c into libsynth.so (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-Wall",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+            u64, u32, i64, dbl, vp = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,
+                                      ctypes.c_double, ctypes.c_void_p)
+            for name in ("synth_normal_f64", "synth_normal_f32", "synth_normal_bf16"):
+                f = getattr(lib, name)
+                f.argtypes = [u64, u32, u64, i64, dbl, vp]
+                f.restype = None
+            lib.synth_normal_fp8_rows.argtypes = [u64, u32, u64, i64, i64, dbl, vp, vp]
+            lib.synth_normal_fp8_rows.restype = None
+            lib.synth_zipf_bias.argtypes = [u64, u32, i64, dbl, vp]
+            lib.synth_zipf_bias.restype = ctypes.c_int
+            lib.synth_permutation.argtypes = [u64, u32, i64, vp]
+            lib.synth_permutation.restype = None
+            lib.synth_raw_u64.argtypes = [u64, u32, u64]
+            lib.synth_raw_u64.restype = u64
+            lib.synth_f64_to_bf16.argtypes = [dbl]
+            lib.synth_f64_to_bf16.restype = ctypes.c_uint16
+            lib.synth_f64_to_e4m3.argtypes = [dbl]
+            lib.synth_f64_to_e4m3.restype = ctypes.c_uint8
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def normal(seed: int, tid: int, shape, std: float, dtype: str, offset: int = 0) -> np.ndarray:
+    """Normals N(0, std^2) for elements offset .. offset+prod(shape) of stream tid.
+
+    dtype: 'f64' -> float64, 'f32' -> float32, 'bf16' -> uint16 bit patterns.
+    """
+    lib = _load()
+    n = int(np.prod(shape))
+    if dtype == "f64":
+        out = np.empty(shape, np.float64)
+        lib.synth_normal_f64(seed, tid, offset, n, std, _ptr(out))
+    elif dtype == "f32":
+        out = np.empty(shape, np.float32)
+        lib.synth_normal_f32(seed, tid, offset, n, std, _ptr(out))
+    elif dtype == "bf16":
+        out = np.empty(shape, np.uint16)
+        lib.synth_normal_bf16(seed, tid, offset, n, std, _ptr(out))
+    else:
+        raise ValueError("dtype must be f64, f32 or bf16, got %r" % dtype)
+    return out
+
+
+def normal_fp8_rows(seed: int, tid: int, rows: int, cols: int, std: float, offset: int = 0):
+    """rows x cols normals quantised per row to OCP E4M3 bytes + fp32 row scales."""
+    lib = _load()
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows,), np.float32)
+    lib.synth_normal_fp8_rows(seed, tid, offset, rows, cols, std, _ptr(q), _ptr(s))
+    return q, s
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(_load().synth_f64_to_bf16(float(v)))
+
+
+def f64_to_e4m3(v: float) -> int:
+    return int(_load().synth_f64_to_e4m3(float(v)))
+
+
+def permutation(seed: int, tid: int, n: int) -> np.ndarray:
+    p = np.empty((n,), np.int32)
+    _load().synth_permutation(seed, tid, n, _ptr(p))
+    return p
+
+
+def zipf_bias(seed: int, tid: int, n: int, s: float) -> np.ndarray:
+    b = np.empty((n,), np.float32)
+    if _load().synth_zipf_bias(seed, tid, n, s, _ptr(b)) != 0:
+        raise ValueError("zipf_bias supports 1..4096 experts")
+    return b
+
+
+def make_tokens(spec: LayerSpec, T: int, seed: int = 0) -> np.ndarray:
+    """x[T][d] ~ N(0, 1) in the activation dtype (uint16 bits for bf16)."""
+    return normal(seed, TID_X, (T, spec.d), 1.0, spec.act_dtype)
+
+
+def make_weights(spec: LayerSpec, seed: int = 0) -> dict:
+    """All layer weights for `spec`, as numpy arrays in their storage dtypes.
+
+    Keys: w_down [l][d], w_up [d][l] (absent without projections; the
+    identity matrix when spec.identity_projections), w_router [N][d or l],
+    router_bias [N] (fp32, only with spec.has_router_bias), w1 [N][m][l],
+    w2 [N][l][m] (+ w1_scale [N][m], w2_scale [N][l] for fp8 experts).
+    """
+    d, l, m, N = spec.d, spec.l, spec.m, spec.n_experts
+    act = spec.act_dtype
+    w = {}
+    if spec.has_projections:
+        if spec.identity_projections:
+            if l != d:
+                raise ValueError("identity projections need l == d")
+            eye = np.eye(d, dtype=np.float64)
+            if act == "f32":
+                w["w_down"] = eye.astype(np.float32)
+            else:
+                w["w_down"] = np.where(eye == 1.0, np.uint16(0x3F80), np.uint16(0)).astype(np.uint16)
+            w["w_up"] = w["w_down"].copy()
+        else:
+            w["w_down"] = normal(seed, TID_WDOWN, (l, d), d ** -0.5, act)
+            w["w_up"] = normal(seed, TID_WUP, (d, l), l ** -0.5, act)
+    r_in = l if spec.router_on_latent else d
+    w["w_router"] = normal(seed, TID_WROUTER, (N, r_in), r_in ** -0.5, act)
+    if spec.has_router_bias:
+        w["router_bias"] = zipf_bias(seed, TID_BIAS, N, spec.zipf_s)
+    if spec.expert_dtype == "fp8_e4m3_rowscale":
+        q1, s1 = normal_fp8_rows(seed, TID_W1, N * m, l, l ** -0.5)
+        q2, s2 = normal_fp8_rows(seed, TID_W2, N * l, m, m ** -0.5)
+        w["w1"], w["w1_scale"] = q1.reshape(N, m, l), s1.reshape(N, m)
+        w["w2"], w["w2_scale"] = q2.reshape(N, l, m), s2.reshape(N, l)
+    else:
+        w["w1"] = normal(seed, TID_W1, (N, m, l), l ** -0.5, spec.expert_dtype)
+        w["w2"] = normal(seed, TID_W2, (N, l, m), m ** -0.5, spec.expert_dtype)
+    return w

@@ -1,0 +1,99 @@
+"""Layer shapes and input recipes of the synthetic workloads.
+
+Shapes follow the LatentMoE paper's running example and deployed models
+(LatentMoE: Toward Optimal Accuracy per FLOP and Parameter in Mixture of
+Experts, §2 running example: N=128, K=8, d=4096, m=1536; §3 Eq. (2): the
+iso-cost variant scales N and K by alpha = d/l) and the secondary article
+"Latent MoE 正在成为新的方向" (a 512-expert top-22 model with l = d/4 and an
+896-expert top-16 model).  Only shapes and distributions live here.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+
+GATINGS = ("softmax_all", "softmax_topk", "sigmoid_topk_norm")
+ACT_DTYPES = ("f32", "bf16")
+EXPERT_DTYPES = ("f32", "bf16", "fp8_e4m3_rowscale")
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    d: int
+    l: int
+    m: int
+    n_experts: int
+    top_k: int
+    gating: str = "softmax_all"
+    act_dtype: str = "bf16"
+    expert_dtype: str = "bf16"
+    has_projections: bool = True
+    router_on_latent: bool = False
+    has_router_bias: bool = False
+    identity_projections: bool = False   # W_down = W_up = I (needs l == d)
+    zipf_s: float = 1.1                  # exponent of the log-Zipf router bias
+
+    def __post_init__(self):
+        assert self.gating in GATINGS, self.gating
+        assert self.act_dtype in ACT_DTYPES, self.act_dtype
+        assert self.expert_dtype in EXPERT_DTYPES, self.expert_dtype
+
+    def replace(self, **kw) -> "LayerSpec":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def act_bytes(self) -> int:
+        return 4 if self.act_dtype == "f32" else 2
+
+    @property
+    def expert_bytes(self) -> float:
+        return {"f32": 4, "bf16": 2, "fp8_e4m3_rowscale": 1}[self.expert_dtype]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    spec: LayerSpec
+    T: int
+    regime: str          # 'tiny', 'decode' (HBM-bound) or 'prefill' (MFMA-bound)
+    description: str
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4, gating="softmax_topk",
+                          act_dtype="f32", expert_dtype="f32"),
+        64, "tiny", "tiny LatentMoE, fp32, router on x, softmax over the top-k"),
+    "tiny_identity": Workload(
+        "tiny_identity", LayerSpec(d=256, l=256, m=128, n_experts=16, top_k=4,
+                                   gating="softmax_topk", act_dtype="f32", expert_dtype="f32",
+                                   identity_projections=True),
+        64, "tiny", "tiny layer with l = d and identity W_down/W_up"),
+    "tiny_std": Workload(
+        "tiny_std", LayerSpec(d=256, l=256, m=128, n_experts=16, top_k=4, gating="softmax_topk",
+                              act_dtype="f32", expert_dtype="f32", has_projections=False),
+        64, "tiny", "tiny standard MoE (l = d, no projections)"),
+    "std_decode": Workload(
+        "std_decode", LayerSpec(d=4096, l=4096, m=1536, n_experts=128, top_k=8,
+                                gating="softmax_all", has_projections=False),
+        512, "decode", "standard MoE, Qwen3-235B-like shape, bf16, T=512"),
+    "latent_decode": Workload(
+        "latent_decode", LayerSpec(d=4096, l=1024, m=1536, n_experts=512, top_k=32,
+                                   gating="sigmoid_topk_norm"),
+        512, "decode", "LatentMoE at iso-cost (alpha=4), bf16, T=512"),
+    "latent_prefill_zipf": Workload(
+        "latent_prefill_zipf", LayerSpec(d=4096, l=1024, m=2048, n_experts=512, top_k=22,
+                                         gating="softmax_all", has_router_bias=True),
+        16384, "prefill", "512-expert top-22 LatentMoE, bf16, T=16384, log-Zipf(1.1) router bias"),
+    "latent_fp8_sparse": Workload(
+        "latent_fp8_sparse", LayerSpec(d=7168, l=1792, m=2048, n_experts=896, top_k=16,
+                                       gating="softmax_all", expert_dtype="fp8_e4m3_rowscale"),
+        4096, "decode", "896-expert top-16 LatentMoE, fp8 e4m3 per-row-scaled experts, bf16 act, T=4096"),
+}
+
+
+def workload(name: str) -> Workload:
+    try:
+        return WORKLOADS[name]
+    except KeyError:
+        raise KeyError("unknown workload %r; known: %s" % (name, ", ".join(WORKLOADS)))
