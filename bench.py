@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the LatentMoE layer forward on one MI355X.
+
+One step = one full layer forward (all stages: W_down + router GEMMs, top-k
+and gates, dispatch indices, grouped FC1 + squared ReLU, grouped FC2,
+combine, W_up) over one batch of synthetic tokens already resident in HBM.
+Prints one JSON line: tokens/s (value), ms per step, the roofline of the
+dominant kernel (from HIP events recorded on the launch stream around each
+stage) and the fp64 CPU oracle's throughput on a bounded token sample.
+
+Default workload: LatentMoE at iso-cost (d 4096, l 1024, m 1536, N 512,
+K 32, sigmoid gating, bf16), T = 512 tokens per call.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def expert_kernel_work(spec, T, counts, stage):
+    """Algorithmic bytes and FLOPs of one FC1 or FC2 launch.
+
+    FC1 reads the weights of every expert that received tokens, reads each
+    latent row once and writes the T*K activated rows; FC2 reads the same
+    amount of expert weights, the T*K activated rows, and writes T*K latent
+    rows.  FLOPs: 2 * T*K * l * m per launch.
+    """
+    touched = int((counts > 0).sum())
+    eb = spec.expert_bytes
+    ab = spec.act_bytes
+    l, m, K = spec.l, spec.m, spec.top_k
+    w = touched * l * m * eb
+    if spec.expert_dtype == "fp8_e4m3_rowscale":
+        w += touched * (m if stage == "fc1" else l) * 4
+    if stage == "fc1":
+        b = w + T * l * ab + T * K * m * ab
+    else:
+        b = w + T * K * m * ab + T * K * l * ab
+    return float(b), 2.0 * T * K * l * m
+
+
+def cpu_baseline(spec, w_np, x_np, budget_s=15.0):
+    import oracle
+    T = x_np.shape[0]
+    n = 4
+    t0 = time.perf_counter()
+    oracle.forward(spec, w_np, x_np, tokens=list(range(n)))
+    dt = time.perf_counter() - t0
+    per_tok = max(dt / n, 1e-6)
+    n2 = int(min(T, max(n, budget_s / per_tok)))
+    t0 = time.perf_counter()
+    oracle.forward(spec, w_np, x_np, tokens=list(range(n2)))
+    dt2 = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n2 / dt2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of the %d tokens of the same batch, full layer in fp64 "
+                      "(%.1f s)" % (n2, T, dt2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="latent_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mixture_experts_layer_32_amd as pkg
+    import synth
+
+    wl = synth.workload(args.workload)
+    spec, T = wl.spec, wl.T
+    dev = torch.device("cuda:0")
+    log("bench: workload %s T=%d: generating inputs" % (wl.name, T))
+    t0 = time.perf_counter()
+    w_np = synth.make_weights(spec, seed=0)
+    x_np = synth.make_tokens(spec, T, seed=0)
+    d_all = pkg.to_device(dict(w_np, x=x_np), dev)
+    torch.cuda.synchronize()
+    log("bench: inputs on device in %.1f s" % (time.perf_counter() - t0))
+
+    layer = pkg.LatentMoELayer(spec)
+    cw = layer.weights_struct(d_all)
+    x = d_all["x"]
+    act = torch.float32 if spec.act_dtype == "f32" else torch.bfloat16
+    out = torch.empty((T, spec.d), dtype=act, device=dev)
+    ws = torch.empty((layer.workspace_size(T),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(timer=None, debug=None):
+        layer.forward(x, None, out=out, workspace=ws, cweights=cw, stream=stream, timer=timer,
+                      debug=debug)
+
+    dbg = {"expert_counts": torch.empty((spec.n_experts,), dtype=torch.int32, device=dev)}
+    step(debug=dbg)
+    torch.cuda.synchronize()
+    counts = dbg["expert_counts"].cpu().numpy()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done (%d steps)" % args.warmup)
+
+    # timed region: K plain steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log("bench: %.3f ms/step" % ms)
+
+    # per-stage durations from HIP events recorded by the library on the launch stream
+    timer = pkg.StageTimer()
+    n_done, stage_ms = 0, {k: 0.0 for k in pkg.STAGE_NAMES}
+    while n_done < args.steps:
+        n = min(200, args.steps - n_done)
+        for _ in range(n):
+            step(timer=timer)
+        got, calls = timer.read()
+        for k in stage_ms:
+            stage_ms[k] += got[k]
+        n_done += calls
+    stage_avg = {k: v / n_done for k, v in stage_ms.items()}
+    timer.close()
+    log("bench: stages (ms) " + " ".join("%s=%.4f" % kv for kv in stage_avg.items()))
+
+    dom = "fc1" if stage_avg["fc1"] >= stage_avg["fc2"] else "fc2"
+    nbytes, nflops = expert_kernel_work(spec, T, counts, dom)
+    t_dom = stage_avg[dom] * 1e-3
+    if wl.regime == "prefill":
+        dt_peak = "fp8" if spec.expert_dtype == "fp8_e4m3_rowscale" else spec.act_dtype
+        achieved = nflops / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_PEAK_TFLOPS["bf16" if dt_peak != "f32" else "f32"],
+                "unit": "TFLOP/s"}
+    else:
+        achieved = nbytes / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "expert GEMM %s (%s kernel)" % (dom.upper(), layer.expert_regime(T))
+    roof["algorithmic_bytes_per_launch"] = nbytes
+    roof["algorithmic_flops_per_launch"] = nflops
+    roof["launch_ms"] = round(stage_avg[dom], 5)
+
+    res = {
+        "metric": "MoE-layer tokens/s @1 GPU",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16"}[spec.act_dtype] + (
+            "+fp8w" if spec.expert_dtype == "fp8_e4m3_rowscale" else ""),
+        "data": "synthetic (seeded normals, N(0,1/fan_in) weights)",
+        "config": {"workload": wl.name, "T": T, "d": spec.d, "l": spec.l, "m": spec.m,
+                   "n_experts": spec.n_experts, "top_k": spec.top_k, "gating": spec.gating,
+                   "expert_dtype": spec.expert_dtype, "parallelism": "single GPU"},
+        "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(spec, w_np, x_np, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

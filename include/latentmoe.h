@@ -1,0 +1,178 @@
+/*
+ * latentmoe.h -- C ABI of the MI355X (gfx950) LatentMoE layer forward.
+ *
+ * The operation (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter
+ * in Mixture of Experts, §3, Eq. (1) and Eq. (2), routed-expert term):
+ *
+ *   u   = W_down . x                    latent token, W_down in R^{l x d}
+ *   z   = W_r . x   (or W_r . u) [+ b]  router logits over N experts, fp32
+ *   T   = K experts with the largest z  ties go to the lower expert id
+ *   v   = sum_{i in T} g_i E_i(u; l)    E_i(u) = W2_i . (max(0, W1_i . u))^2,
+ *                                       W1_i in R^{m x l}, W2_i in R^{l x m}
+ *   out = W_up . v                      W_up in R^{d x l}
+ *
+ * With has_projections == 0 the layer is the standard MoE (l == d, u = x,
+ * out = v): the same code path with the two projections skipped.  The
+ * paper's shared experts (the second sum of Eq. (1)) are not part of this
+ * call.
+ *
+ * Conventions
+ *  - Every tensor is row-major "[out][in]" (y = W . x), dense, with the
+ *    shapes given on each field.  All data pointers are DEVICE pointers owned
+ *    by the caller; they must be 16-byte aligned.  bf16 values are raw
+ *    IEEE bfloat16 bit patterns (uint16), fp8 values raw OCP E4M3 bytes.
+ *  - The library owns only the handle (host memory).  A handle is immutable
+ *    after latentmoe_create and may be shared by concurrent forward calls on
+ *    different streams if each call has its own workspace and outputs.
+ *  - latentmoe_forward is asynchronous and stream-ordered: it enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ *    stream) and returns; it never synchronises the host, never allocates
+ *    device memory and never copies data to the host.
+ *  - Errors are returned as lmoe_status, never thrown; on a non-OK status
+ *    nothing has been enqueued except for LMOE_ERR_HIP (a launch failed
+ *    part-way; the stream's outputs are then undefined).
+ *    latentmoe_last_error() gives a message for the calling thread.
+ */
+#ifndef LATENTMOE_H
+#define LATENTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_ERR_INVALID_ARG = -1,  /* NULL pointer, bad shape, k > N, T < 0, ... */
+  LMOE_ERR_UNSUPPORTED = -2,  /* valid in principle but not implemented (e.g. fp8 activations) */
+  LMOE_ERR_WORKSPACE = -3,    /* workspace NULL or smaller than latentmoe_workspace_size() */
+  LMOE_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+  LMOE_ERR_ALLOC = -5         /* host allocation of the handle failed */
+} lmoe_status;
+
+typedef enum {
+  LMOE_F32 = 0,
+  LMOE_BF16 = 1,
+  LMOE_FP8_E4M3_ROWSCALE = 2  /* OCP E4M3 bytes + one fp32 scale per matrix row: w = q * s */
+} lmoe_dtype;
+
+typedef enum {
+  LMOE_ROUTER_ON_X = 0,       /* z = W_r . x, W_r in R^{N x d}  (§3, text after Eq. (1)) */
+  LMOE_ROUTER_ON_LATENT = 1   /* z = W_r . u, W_r in R^{N x l}  (routing "in the latent") */
+} lmoe_router_input;
+
+typedef enum {
+  LMOE_GATE_SOFTMAX_ALL = 0,      /* p = Softmax(z) over all N; g_i = p_i, no renormalisation (Eq. (1)) */
+  LMOE_GATE_SOFTMAX_TOPK = 1,     /* softmax over the K selected logits */
+  LMOE_GATE_SIGMOID_TOPK_NORM = 2 /* g_i = sigmoid(z_i) / sum_{j in T} sigmoid(z_j) */
+} lmoe_gating;
+
+typedef enum {
+  LMOE_ACT_SQRELU = 0             /* non-gated expert FFN with (max(0, a))^2 (Table 2: Squared-ReLU) */
+} lmoe_activation;
+
+typedef struct {
+  int64_t d;           /* model width */
+  int64_t l;           /* latent width (== d when has_projections == 0) */
+  int64_t m;           /* expert FFN width */
+  int64_t n_experts;   /* N, 1 .. 2048 */
+  int64_t top_k;       /* K, 1 .. min(N, 64) */
+  int32_t router_input;   /* lmoe_router_input */
+  int32_t gating;         /* lmoe_gating */
+  int32_t activation;     /* lmoe_activation */
+  int32_t act_dtype;      /* LMOE_F32 | LMOE_BF16: x, W_down, W_router, W_up, out */
+  int32_t expert_dtype;   /* LMOE_F32 | LMOE_BF16 | LMOE_FP8_E4M3_ROWSCALE: W1, W2.
+                             F32 experts need F32 activations; BF16/FP8 need BF16. */
+  int32_t has_projections;  /* 0: standard MoE (requires l == d) */
+  int32_t has_router_bias;  /* 1: z += b before selection and gating (fp32 b[N]) */
+} lmoe_config;
+
+/* Device pointers; shapes use the config's d, l, m, N. */
+typedef struct {
+  const void *w_down;       /* [l][d] act dtype; NULL without projections */
+  const void *w_router;     /* [N][d] (ROUTER_ON_X) or [N][l] (ROUTER_ON_LATENT), act dtype */
+  const float *router_bias; /* [N] fp32; only read when has_router_bias */
+  const void *w1;           /* [N][m][l] expert dtype */
+  const void *w2;           /* [N][l][m] expert dtype */
+  const float *w1_scale;    /* [N][m] fp32; FP8 experts only */
+  const float *w2_scale;    /* [N][l] fp32; FP8 experts only */
+  const void *w_up;         /* [d][l] act dtype; NULL without projections */
+} lmoe_weights;
+
+/* Per-stage GPU timing: an opaque object holding HIP events.  Attach one to
+ * a forward call through lmoe_debug_out.timer; the call then records an
+ * event before its first kernel and after each stage.  Reading synchronises
+ * on the last event and ADDS the stage durations to the accumulators. */
+typedef struct lmoe_timer lmoe_timer;
+
+enum {
+  LMOE_STAGE_DOWN_ROUTER = 0, /* W_down GEMM and router-logit GEMM */
+  LMOE_STAGE_TOPK = 1,        /* top-k + gating */
+  LMOE_STAGE_DISPATCH = 2,    /* expert histogram, prefix sum, stable slot assignment */
+  LMOE_STAGE_FC1 = 3,         /* grouped latent FC1 + squared ReLU (gathers u rows) */
+  LMOE_STAGE_FC2 = 4,         /* grouped latent FC2 */
+  LMOE_STAGE_COMBINE = 5,     /* gate-weighted sum of the K expert outputs per token */
+  LMOE_STAGE_UP = 6,          /* W_up GEMM */
+  LMOE_NUM_STAGES = 7
+};
+
+/* Optional device outputs of a forward call (any may be NULL). */
+typedef struct {
+  int32_t *topk_idx;       /* [T][K] selected expert ids, by (z desc, id asc) */
+  float *topk_gate;        /* [T][K] gate of topk_idx[t][j] */
+  int32_t *expert_counts;  /* [N] copies routed to each expert; sums to T*K */
+  int32_t *expert_offsets; /* [N+1] exclusive prefix sum of expert_counts */
+  int32_t *slot_of;        /* [T][K] row of copy (t, j) in the expert-grouped order */
+  int32_t *token_of;       /* [T*K] token of each expert-grouped row; within an
+                              expert, rows follow increasing token index */
+  float *logits;           /* [T][N] fp32 router logits W_r . x (or . u), before the bias */
+  void *latent;            /* [T][l] u in act dtype (projections only) */
+  lmoe_timer *timer;       /* host object from latentmoe_timer_create, or NULL */
+} lmoe_debug_out;
+
+typedef struct lmoe_handle lmoe_handle;
+
+/* Validate `cfg` and build a handle (host only; no HIP call).
+ * Returns INVALID_ARG for inconsistent shapes (k > N, l != d without
+ * projections, non-positive sizes), UNSUPPORTED for combinations this
+ * build does not implement (d, l, m not multiples of 16; N > 2048;
+ * K > 64; activation/expert dtype pairs other than f32/f32, bf16/bf16 and
+ * bf16/fp8). */
+lmoe_status latentmoe_create(const lmoe_config *cfg, lmoe_handle **out);
+
+/* Bytes of device workspace a forward call over T tokens needs. */
+lmoe_status latentmoe_workspace_size(const lmoe_handle *h, int64_t T, size_t *bytes);
+
+/* out[T][d] (act dtype) = layer(x[T][d]).  T == 0 is a no-op returning OK.
+ * `workspace` (device, >= latentmoe_workspace_size bytes, 256-byte aligned)
+ * is scratch owned by the caller for the duration of the call on `stream`.
+ * `dbg` may be NULL. */
+lmoe_status latentmoe_forward(const lmoe_handle *h, const lmoe_weights *w, const void *x,
+                              int64_t T, void *out, const lmoe_debug_out *dbg,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+lmoe_status latentmoe_destroy(lmoe_handle *h);
+
+/* Stage timer: create/destroy, and read the accumulated milliseconds per
+ * stage (LMOE_NUM_STAGES floats) and the number of recorded forward calls.
+ * Reading waits for the last recorded forward call to finish and resets. */
+lmoe_status latentmoe_timer_create(lmoe_timer **out);
+lmoe_status latentmoe_timer_read(lmoe_timer *t, float *stage_ms, int32_t n_stages,
+                                 int32_t *n_calls);
+lmoe_status latentmoe_timer_destroy(lmoe_timer *t);
+
+/* Static strings; never NULL. */
+const char *latentmoe_status_string(lmoe_status s);
+const char *latentmoe_last_error(void);
+
+/* Name of the expert-kernel regime the handle picks for T tokens:
+ * "stream" (weight-streaming skinny kernel, tokens per expert small) or
+ * "tiled" (LDS-tiled MFMA grouped GEMM).  For reports only. */
+const char *latentmoe_expert_regime(const lmoe_handle *h, int64_t T);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LATENTMOE_H */

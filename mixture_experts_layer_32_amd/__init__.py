@@ -1,0 +1,293 @@
+"""MI355X (gfx950) LatentMoE layer forward -- Python binding of liblatentmoe.so.
+
+The layer (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter in
+Mixture of Experts, §3 Eq. (1)/(2), routed-expert term) runs entirely in the
+HIP kernels behind the C ABI declared in ``include/latentmoe.h``.  This module
+only marshals arguments: it checks shapes/dtypes of torch tensors, passes
+their device pointers, the current HIP stream and a workspace tensor, and
+maps status codes to exceptions.  PyTorch is used for device memory and
+streams only.  There is no CPU fallback: if the library is missing the
+import of ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblatentmoe.so")
+
+LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE = 0, 1, 2
+ROUTER_ON_X, ROUTER_ON_LATENT = 0, 1
+GATE_SOFTMAX_ALL, GATE_SOFTMAX_TOPK, GATE_SIGMOID_TOPK_NORM = 0, 1, 2
+ACT_SQRELU = 0
+NUM_STAGES = 7
+STAGE_NAMES = ("down_router", "topk", "dispatch", "fc1", "fc2", "combine", "up")
+
+_DT = {"f32": LMOE_F32, "bf16": LMOE_BF16, "fp8_e4m3_rowscale": LMOE_FP8_E4M3_ROWSCALE}
+_GATE = {"softmax_all": GATE_SOFTMAX_ALL, "softmax_topk": GATE_SOFTMAX_TOPK,
+         "sigmoid_topk_norm": GATE_SIGMOID_TOPK_NORM}
+
+EXPORTED = ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
+            "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
+            "latentmoe_timer_destroy", "latentmoe_status_string", "latentmoe_last_error",
+            "latentmoe_expert_regime")
+
+
+class LmoeConfig(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("l", ctypes.c_int64), ("m", ctypes.c_int64),
+                ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
+                ("router_input", ctypes.c_int32), ("gating", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("expert_dtype", ctypes.c_int32), ("has_projections", ctypes.c_int32),
+                ("has_router_bias", ctypes.c_int32)]
+
+
+class LmoeWeights(ctypes.Structure):
+    _fields_ = [("w_down", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
+                ("router_bias", ctypes.c_void_p), ("w1", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p)]
+
+
+class LmoeDebug(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p),
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("slot_of", ctypes.c_void_p), ("token_of", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("latent", ctypes.c_void_p),
+                ("timer", ctypes.c_void_p)]
+
+
+class LatentMoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """The loaded liblatentmoe.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("liblatentmoe.so is not built (run __graft_entry__.build() or "
+                                   "python mixture_experts_layer_32_amd/build.py)")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+            L.latentmoe_create.argtypes = [ctypes.POINTER(LmoeConfig), ctypes.POINTER(vp)]
+            L.latentmoe_workspace_size.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_size_t)]
+            L.latentmoe_forward.argtypes = [vp, ctypes.POINTER(LmoeWeights), vp, i64, vp,
+                                            ctypes.POINTER(LmoeDebug), vp, ctypes.c_size_t, vp]
+            L.latentmoe_destroy.argtypes = [vp]
+            L.latentmoe_timer_create.argtypes = [ctypes.POINTER(vp)]
+            L.latentmoe_timer_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
+                                               ctypes.POINTER(i32)]
+            L.latentmoe_timer_destroy.argtypes = [vp]
+            L.latentmoe_status_string.argtypes = [ctypes.c_int]
+            L.latentmoe_status_string.restype = ctypes.c_char_p
+            L.latentmoe_last_error.argtypes = []
+            L.latentmoe_last_error.restype = ctypes.c_char_p
+            L.latentmoe_expert_regime.argtypes = [vp, i64]
+            L.latentmoe_expert_regime.restype = ctypes.c_char_p
+            for f in ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
+                      "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
+                      "latentmoe_timer_destroy"):
+                getattr(L, f).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise LatentMoEError(status, "%s: %s" % (L.latentmoe_status_string(status).decode(),
+                                                 L.latentmoe_last_error().decode()))
+
+
+def make_config(spec) -> LmoeConfig:
+    """C config from a LayerSpec-like object (d, l, m, n_experts, top_k, ...)."""
+    return LmoeConfig(spec.d, spec.l, spec.m, spec.n_experts, spec.top_k,
+                      ROUTER_ON_LATENT if spec.router_on_latent else ROUTER_ON_X,
+                      _GATE[spec.gating], ACT_SQRELU, _DT[spec.act_dtype], _DT[spec.expert_dtype],
+                      int(spec.has_projections), int(spec.has_router_bias))
+
+
+class StageTimer:
+    """Per-stage HIP-event timer attached to forward calls (ms per stage)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib().latentmoe_timer_create(ctypes.byref(h)))
+        self._h = h
+
+    def read(self):
+        """(dict stage -> accumulated ms, number of calls); resets the timer."""
+        buf = (ctypes.c_float * NUM_STAGES)()
+        n = ctypes.c_int32()
+        _check(lib().latentmoe_timer_read(self._h, buf, NUM_STAGES, ctypes.byref(n)))
+        return {k: float(buf[i]) for i, k in enumerate(STAGE_NAMES)}, int(n.value)
+
+    def close(self):
+        if self._h:
+            lib().latentmoe_timer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class LatentMoELayer:
+    """Handle on one layer configuration; weights are passed per call."""
+
+    def __init__(self, spec):
+        self.spec = spec
+        self._cfg = make_config(spec)
+        h = ctypes.c_void_p()
+        _check(lib().latentmoe_create(ctypes.byref(self._cfg), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().latentmoe_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().latentmoe_workspace_size(self._h, T, ctypes.byref(n)))
+        return int(n.value)
+
+    def expert_regime(self, T: int) -> str:
+        return lib().latentmoe_expert_regime(self._h, T).decode()
+
+    # ---- argument checks (shapes / dtypes of the device tensors)
+    def _expect(self, name, t, shape, dtypes):
+        torch = _torch()
+        if t is None:
+            raise ValueError("%s is required" % name)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        if t.dtype not in dtypes:
+            raise ValueError("%s: dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a device tensor" % name)
+        return t.data_ptr()
+
+    def weights_struct(self, w: dict) -> LmoeWeights:
+        torch = _torch()
+        s = self.spec
+        act = (torch.float32,) if s.act_dtype == "f32" else (torch.bfloat16,)
+        if s.expert_dtype == "f32":
+            edt = (torch.float32,)
+        elif s.expert_dtype == "bf16":
+            edt = (torch.bfloat16,)
+        else:
+            edt = (torch.uint8, torch.float8_e4m3fn)
+        r_in = s.l if s.router_on_latent else s.d
+        cw = LmoeWeights()
+        cw.w_router = self._expect("w_router", w.get("w_router"), (s.n_experts, r_in), act)
+        cw.w1 = self._expect("w1", w.get("w1"), (s.n_experts, s.m, s.l), edt)
+        cw.w2 = self._expect("w2", w.get("w2"), (s.n_experts, s.l, s.m), edt)
+        if s.has_projections:
+            cw.w_down = self._expect("w_down", w.get("w_down"), (s.l, s.d), act)
+            cw.w_up = self._expect("w_up", w.get("w_up"), (s.d, s.l), act)
+        if s.has_router_bias:
+            cw.router_bias = self._expect("router_bias", w.get("router_bias"), (s.n_experts,),
+                                          (torch.float32,))
+        if s.expert_dtype == "fp8_e4m3_rowscale":
+            cw.w1_scale = self._expect("w1_scale", w.get("w1_scale"), (s.n_experts, s.m),
+                                       (torch.float32,))
+            cw.w2_scale = self._expect("w2_scale", w.get("w2_scale"), (s.n_experts, s.l),
+                                       (torch.float32,))
+        return cw
+
+    def forward(self, x, weights, out=None, workspace=None, debug: dict | None = None,
+                timer: StageTimer | None = None, stream=None, cweights: LmoeWeights | None = None):
+        """out[T][d] = layer(x[T][d]) on the current (or given) HIP stream.
+
+        debug: optional dict of preallocated device tensors keyed like
+        lmoe_debug_out (topk_idx, topk_gate, expert_counts, expert_offsets,
+        slot_of, token_of, logits, latent).
+        """
+        torch = _torch()
+        s = self.spec
+        act = torch.float32 if s.act_dtype == "f32" else torch.bfloat16
+        T = int(x.shape[0])
+        xp = self._expect("x", x, (T, s.d), (act,))
+        if out is None:
+            out = torch.empty((T, s.d), dtype=act, device=x.device)
+        op = self._expect("out", out, (T, s.d), (act,))
+        need = self.workspace_size(T)
+        if workspace is None:
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+        if workspace.numel() < need:
+            raise ValueError("workspace has %d bytes, needs %d" % (workspace.numel(), need))
+        cw = cweights if cweights is not None else self.weights_struct(weights)
+        dbg = LmoeDebug()
+        dbg_p = None
+        if debug or timer is not None:
+            for k, v in (debug or {}).items():
+                if not hasattr(dbg, k):
+                    raise ValueError("unknown debug output %r" % k)
+                setattr(dbg, k, v.data_ptr())
+            if timer is not None:
+                dbg.timer = timer._h
+            dbg_p = ctypes.byref(dbg)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        st = ctypes.c_void_p(stream.cuda_stream)
+        _check(lib().latentmoe_forward(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
+                                       workspace.data_ptr(), workspace.numel(), st))
+        return out
+
+
+def debug_buffers(spec, T: int, device="cuda") -> dict:
+    """Device tensors for every debug output of a forward call over T tokens."""
+    torch = _torch()
+    K, N = spec.top_k, spec.n_experts
+    act = torch.float32 if spec.act_dtype == "f32" else torch.bfloat16
+    d = {"topk_idx": torch.empty((T, K), dtype=torch.int32, device=device),
+         "topk_gate": torch.empty((T, K), dtype=torch.float32, device=device),
+         "expert_counts": torch.empty((N,), dtype=torch.int32, device=device),
+         "expert_offsets": torch.empty((N + 1,), dtype=torch.int32, device=device),
+         "slot_of": torch.empty((T, K), dtype=torch.int32, device=device),
+         "token_of": torch.empty((T * K,), dtype=torch.int32, device=device),
+         "logits": torch.empty((T, N), dtype=torch.float32, device=device)}
+    if spec.has_projections:
+        d["latent"] = torch.empty((T, spec.l), dtype=act, device=device)
+    return d
+
+
+def to_device(arrays: dict, device="cuda") -> dict:
+    """numpy inputs from the synthetic generator -> device tensors of the
+    storage dtype (bf16 bit patterns become torch.bfloat16; fp8 bytes stay uint8)."""
+    torch = _torch()
+    import numpy as np
+    out = {}
+    for k, a in arrays.items():
+        if a.dtype == np.uint16:
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a)
+        out[k] = t.to(device)
+    return out

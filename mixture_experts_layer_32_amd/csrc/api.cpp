@@ -1,0 +1,410 @@
+// C ABI of the LatentMoE layer forward: validation, workspace planning and
+// the stream-ordered launch sequence (include/latentmoe.h).
+//
+// Layer (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter in
+// Mixture of Experts, §3 Eq. (1)/(2), routed term):
+//   stage 0  u = x W_down^T (bf16/f32 out); logits = r W_r^T (fp32), r = x or u
+//   stage 1  top-K per token (ties -> lower id) and gates
+//   stage 2  expert histogram / prefix sum / stable row of every token copy
+//   stage 3  H = sqrelu(u[token_of] W1_e^T)       grouped by expert
+//   stage 4  Y = H W2_e^T                         grouped by expert
+//   stage 5  v[t] = sum_j g[t][j] Y[slot_of[t][j]]
+//   stage 6  out = v W_up^T
+// Without projections (standard MoE) stage 0 computes only the logits, the
+// expert GEMMs read x, and stage 5 writes `out` directly.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/latentmoe.h"
+#include "kernels.hpp"
+
+struct lmoe_handle {
+  lmoe_config cfg;
+};
+
+struct lmoe_timer {
+  int max_calls = 0;
+  int n_calls = 0;
+  std::vector<hipEvent_t> ev;  // max_calls * (LMOE_NUM_STAGES + 1)
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lmoe_status fail(lmoe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lmoe_status fail(lmoe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+lmoe_status hip_fail(hipError_t e, const char* what) {
+  return fail(LMOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxExperts = 2048;
+constexpr int64_t kMaxTopK = 64;
+constexpr int64_t kMaxCopies = int64_t(1) << 30;  // T * K (int32 row indices)
+constexpr double kStreamMaxRowsPerExpert = 96.0;  // mean copies per expert -> streaming kernel
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+lmoe::Dt act_dt(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? lmoe::Dt::F32 : lmoe::Dt::BF16; }
+lmoe::Dt exp_dt(const lmoe_config& c) {
+  return c.expert_dtype == LMOE_F32 ? lmoe::Dt::F32
+         : c.expert_dtype == LMOE_BF16 ? lmoe::Dt::BF16 : lmoe::Dt::FP8;
+}
+size_t act_bytes(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? 4 : 2; }
+
+struct Plan {
+  int64_t T = 0, copies = 0;
+  int nblk = 0;
+  bool stream = true;   // expert GEMMs: weight-streaming kernel
+  int mb_max = 4;       // streaming kernel rows per pass / 16
+  int expert_tile = 0;  // tiled kernel tile config
+  int tile_m = 128;
+  size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, total;
+};
+
+Plan make_plan(const lmoe_config& c, int64_t T) {
+  Plan p;
+  p.T = T;
+  p.copies = T * c.top_k;
+  p.nblk = static_cast<int>((T + lmoe::kRouteBlock - 1) / lmoe::kRouteBlock);
+  const double mean = T > 0 ? double(p.copies) / double(c.n_experts) : 0.0;
+  p.stream = mean <= kStreamMaxRowsPerExpert || c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
+  p.mb_max = mean <= 40.0 ? 4 : 8;
+  p.expert_tile = 0;
+  p.tile_m = lmoe::tiled_block_m(p.expert_tile);
+  const size_t ab = act_bytes(c);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  p.u = take(c.has_projections ? size_t(T) * c.l * ab : 0);
+  p.logits = take(size_t(T) * c.n_experts * 4);
+  p.idx = take(size_t(p.copies) * 4);
+  p.gate = take(size_t(p.copies) * 4);
+  p.masks = take(size_t(p.nblk) * c.n_experts * 8);
+  p.base = take(size_t(p.nblk) * c.n_experts * 4);
+  p.counts = take(size_t(c.n_experts) * 4);
+  p.offsets = take(size_t(c.n_experts + 1) * 4);
+  p.tiles = take(size_t(c.n_experts + 1) * 4);
+  p.slot = take(size_t(p.copies) * 4);
+  p.token = take(size_t(p.copies) * 4);
+  p.H = take(size_t(p.copies) * c.m * ab);
+  p.Y = take(size_t(p.copies) * c.l * ab);
+  p.v = take(c.has_projections ? size_t(T) * c.l * ab : 0);
+  p.total = o;
+  return p;
+}
+
+// Tile config of a dense GEMM: the large tile when it still gives two
+// workgroups per compute unit, else the small one.
+int dense_tile(int64_t M, int64_t N) {
+  const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
+  return big >= 512 ? 0 : 1;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* latentmoe_status_string(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "ok";
+    case LMOE_ERR_INVALID_ARG: return "invalid argument";
+    case LMOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LMOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case LMOE_ERR_HIP: return "HIP runtime error";
+    case LMOE_ERR_ALLOC: return "host allocation failed";
+  }
+  return "unknown status";
+}
+
+const char* latentmoe_last_error(void) { return g_last_error.c_str(); }
+
+lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
+  if (!cfg || !out) return fail(LMOE_ERR_INVALID_ARG, "create: NULL argument");
+  *out = nullptr;
+  const lmoe_config& c = *cfg;
+  if (c.d <= 0 || c.l <= 0 || c.m <= 0 || c.n_experts <= 0 || c.top_k <= 0)
+    return fail(LMOE_ERR_INVALID_ARG, "create: sizes must be positive");
+  if (c.top_k > c.n_experts)
+    return fail(LMOE_ERR_INVALID_ARG, "create: top_k %lld > n_experts %lld", (long long)c.top_k,
+                (long long)c.n_experts);
+  if (c.has_projections != 0 && c.has_projections != 1)
+    return fail(LMOE_ERR_INVALID_ARG, "create: has_projections must be 0 or 1");
+  if (!c.has_projections && c.l != c.d)
+    return fail(LMOE_ERR_INVALID_ARG, "create: without projections l must equal d");
+  if (c.has_projections && c.l > c.d)
+    return fail(LMOE_ERR_INVALID_ARG, "create: latent width l > d");
+  if (c.router_input != LMOE_ROUTER_ON_X && c.router_input != LMOE_ROUTER_ON_LATENT)
+    return fail(LMOE_ERR_INVALID_ARG, "create: bad router_input");
+  if (c.gating < LMOE_GATE_SOFTMAX_ALL || c.gating > LMOE_GATE_SIGMOID_TOPK_NORM)
+    return fail(LMOE_ERR_INVALID_ARG, "create: bad gating");
+  if (c.has_router_bias != 0 && c.has_router_bias != 1)
+    return fail(LMOE_ERR_INVALID_ARG, "create: has_router_bias must be 0 or 1");
+  if (c.activation != LMOE_ACT_SQRELU)
+    return fail(LMOE_ERR_UNSUPPORTED, "create: only the squared-ReLU expert FFN is implemented");
+  if (c.act_dtype < LMOE_F32 || c.act_dtype > LMOE_FP8_E4M3_ROWSCALE ||
+      c.expert_dtype < LMOE_F32 || c.expert_dtype > LMOE_FP8_E4M3_ROWSCALE)
+    return fail(LMOE_ERR_INVALID_ARG, "create: bad dtype");
+  const bool ok_pair = (c.act_dtype == LMOE_F32 && c.expert_dtype == LMOE_F32) ||
+                       (c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16) ||
+                       (c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE);
+  if (!ok_pair)
+    return fail(LMOE_ERR_UNSUPPORTED, "create: dtype pair (act %d, experts %d) not implemented",
+                c.act_dtype, c.expert_dtype);
+  if (c.d % 16 || c.l % 16 || c.m % 16)
+    return fail(LMOE_ERR_UNSUPPORTED, "create: d, l, m must be multiples of 16");
+  if (c.n_experts > kMaxExperts || c.top_k > kMaxTopK)
+    return fail(LMOE_ERR_UNSUPPORTED, "create: n_experts <= %lld and top_k <= %lld supported",
+                (long long)kMaxExperts, (long long)kMaxTopK);
+  if (c.d > (int64_t(1) << 20) || c.m > (int64_t(1) << 20))
+    return fail(LMOE_ERR_UNSUPPORTED, "create: widths above 2^20");
+  lmoe_handle* h = new (std::nothrow) lmoe_handle;
+  if (!h) return fail(LMOE_ERR_ALLOC, "create: out of host memory");
+  h->cfg = c;
+  *out = h;
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_destroy(lmoe_handle* h) {
+  delete h;
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_workspace_size(const lmoe_handle* h, int64_t T, size_t* bytes) {
+  if (!h || !bytes) return fail(LMOE_ERR_INVALID_ARG, "workspace_size: NULL argument");
+  if (T < 0) return fail(LMOE_ERR_INVALID_ARG, "workspace_size: T < 0");
+  if (T * h->cfg.top_k > kMaxCopies) return fail(LMOE_ERR_UNSUPPORTED, "workspace_size: T*K too large");
+  *bytes = make_plan(h->cfg, T).total;
+  return LMOE_OK;
+}
+
+const char* latentmoe_expert_regime(const lmoe_handle* h, int64_t T) {
+  if (!h || T < 0) return "invalid";
+  return make_plan(h->cfg, T).stream ? "stream" : "tiled";
+}
+
+lmoe_status latentmoe_timer_create(lmoe_timer** out) {
+  if (!out) return fail(LMOE_ERR_INVALID_ARG, "timer_create: NULL argument");
+  lmoe_timer* t = new (std::nothrow) lmoe_timer;
+  if (!t) return fail(LMOE_ERR_ALLOC, "timer_create: out of host memory");
+  t->max_calls = 256;
+  t->ev.assign(size_t(t->max_calls) * (LMOE_NUM_STAGES + 1), nullptr);
+  for (auto& e : t->ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      for (auto& f : t->ev)
+        if (f) (void)hipEventDestroy(f);
+      delete t;
+      return hip_fail(r, "timer_create: hipEventCreate");
+    }
+  }
+  *out = t;
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_timer_read(lmoe_timer* t, float* stage_ms, int32_t n_stages, int32_t* n_calls) {
+  if (!t || !stage_ms || n_stages < LMOE_NUM_STAGES)
+    return fail(LMOE_ERR_INVALID_ARG, "timer_read: bad argument");
+  for (int s = 0; s < n_stages; ++s) stage_ms[s] = 0.f;
+  const int n = t->n_calls;
+  if (n > 0) {
+    hipError_t r = hipEventSynchronize(t->ev[size_t(n - 1) * (LMOE_NUM_STAGES + 1) + LMOE_NUM_STAGES]);
+    if (r != hipSuccess) return hip_fail(r, "timer_read: hipEventSynchronize");
+  }
+  for (int c = 0; c < n; ++c) {
+    const hipEvent_t* e = &t->ev[size_t(c) * (LMOE_NUM_STAGES + 1)];
+    for (int s = 0; s < LMOE_NUM_STAGES; ++s) {
+      float ms = 0.f;
+      hipError_t r = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+      if (r != hipSuccess) return hip_fail(r, "timer_read: hipEventElapsedTime");
+      stage_ms[s] += ms;
+    }
+  }
+  if (n_calls) *n_calls = n;
+  t->n_calls = 0;
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_timer_destroy(lmoe_timer* t) {
+  if (!t) return LMOE_OK;
+  for (auto& e : t->ev)
+    if (e) (void)hipEventDestroy(e);
+  delete t;
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const void* x,
+                              int64_t T, void* out, const lmoe_debug_out* dbg, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!h || !w) return fail(LMOE_ERR_INVALID_ARG, "forward: NULL handle or weights");
+  if (T < 0) return fail(LMOE_ERR_INVALID_ARG, "forward: T < 0");
+  if (T == 0) return LMOE_OK;
+  const lmoe_config& c = h->cfg;
+  if (T * c.top_k > kMaxCopies) return fail(LMOE_ERR_UNSUPPORTED, "forward: T*K too large");
+  if (!x || !out) return fail(LMOE_ERR_INVALID_ARG, "forward: NULL x or out");
+  if (!w->w_router || !w->w1 || !w->w2)
+    return fail(LMOE_ERR_INVALID_ARG, "forward: NULL router or expert weights");
+  if (c.has_projections && (!w->w_down || !w->w_up))
+    return fail(LMOE_ERR_INVALID_ARG, "forward: NULL projection weights");
+  if (c.has_router_bias && !w->router_bias)
+    return fail(LMOE_ERR_INVALID_ARG, "forward: NULL router bias");
+  if (c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE && (!w->w1_scale || !w->w2_scale))
+    return fail(LMOE_ERR_INVALID_ARG, "forward: NULL fp8 scales");
+  const void* ptrs[] = {x, out, w->w_router, w->w1, w->w2, w->w_down, w->w_up};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(LMOE_ERR_INVALID_ARG, "forward: pointers must be 16-byte aligned");
+  const Plan p = make_plan(c, T);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(LMOE_ERR_WORKSPACE, "forward: workspace %zu bytes < required %zu", workspace_bytes,
+                p.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LMOE_ERR_INVALID_ARG, "forward: workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const lmoe::Dt adt = act_dt(c), edt = exp_dt(c);
+  const int ab = static_cast<int>(act_bytes(c));
+  const int Ti = static_cast<int>(T), N = static_cast<int>(c.n_experts), K = static_cast<int>(c.top_k);
+  const int d = static_cast<int>(c.d), l = static_cast<int>(c.l), m = static_cast<int>(c.m);
+
+  void* u = c.has_projections ? ws + p.u : const_cast<void*>(x);
+  float* logits = reinterpret_cast<float*>(ws + p.logits);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + p.idx);
+  float* gate = reinterpret_cast<float*>(ws + p.gate);
+  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + p.masks);
+  int32_t* base = reinterpret_cast<int32_t*>(ws + p.base);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + p.offsets);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + p.tiles);
+  int32_t* slot_of = reinterpret_cast<int32_t*>(ws + p.slot);
+  int32_t* token_of = reinterpret_cast<int32_t*>(ws + p.token);
+  void* H = ws + p.H;
+  void* Y = ws + p.Y;
+  void* v = c.has_projections ? ws + p.v : out;
+
+  lmoe_timer* tm = dbg ? dbg->timer : nullptr;
+  hipEvent_t* ev = nullptr;
+  if (tm) {
+    if (tm->n_calls >= tm->max_calls)
+      return fail(LMOE_ERR_INVALID_ARG, "forward: timer full (%d calls); read it first", tm->max_calls);
+    ev = &tm->ev[size_t(tm->n_calls) * (LMOE_NUM_STAGES + 1)];
+    ++tm->n_calls;
+  }
+  hipError_t e;
+#define LMOE_TRY(call, what)                          \
+  do {                                                \
+    e = (call);                                       \
+    if (e != hipSuccess) return hip_fail(e, what);    \
+  } while (0)
+#define LMOE_MARK(i) \
+  if (ev) LMOE_TRY(hipEventRecord(ev[i], s), "hipEventRecord")
+
+  LMOE_MARK(0);
+  // ---- stage 0: down-projection and router logits
+  if (c.has_projections) {
+    lmoe::GemmArgs a;
+    a.A = x; a.lda = d; a.B = w->w_down; a.ldb = d; a.C = u; a.ldc = l;
+    a.M = Ti; a.N = l; a.K = d;
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, dense_tile(T, l), s), "W_down GEMM");
+  }
+  {
+    const bool lat = c.router_input == LMOE_ROUTER_ON_LATENT;
+    lmoe::GemmArgs a;
+    a.A = lat ? u : x; a.lda = lat ? l : d;
+    a.B = w->w_router; a.ldb = lat ? l : d;
+    a.C = logits; a.ldc = N;
+    a.M = Ti; a.N = N; a.K = lat ? l : d;
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, lmoe::Dt::F32, dense_tile(T, N), s), "router GEMM");
+  }
+  LMOE_MARK(1);
+  // ---- stage 1: top-k and gates
+  LMOE_TRY(lmoe::launch_topk_gate(logits, c.has_router_bias ? w->router_bias : nullptr, Ti, N, K,
+                                  c.gating, idx, gate, s), "top-k");
+  LMOE_MARK(2);
+  // ---- stage 2: dispatch indices
+  LMOE_TRY(lmoe::launch_route_masks(idx, Ti, N, K, masks, s), "route masks");
+  LMOE_TRY(lmoe::launch_route_scan(masks, p.nblk, N, p.tile_m, counts, offsets, base, tiles, s),
+           "route scan");
+  LMOE_TRY(lmoe::launch_route_assign(idx, masks, base, offsets, Ti, N, K, slot_of, token_of, s),
+           "route assign");
+  LMOE_MARK(3);
+  // ---- stage 3: FC1 + squared ReLU, token rows gathered through token_of
+  {
+    lmoe::GemmArgs a;
+    a.A = u; a.lda = l; a.a_rows = token_of;
+    a.B = w->w1; a.ldb = l; a.b_gstride = int64_t(m) * l;
+    a.b_scale = edt == lmoe::Dt::FP8 ? w->w1_scale : nullptr; a.s_gstride = m;
+    a.C = H; a.ldc = m;
+    a.N = m; a.K = l;
+    a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);
+    a.act = lmoe::kActSqRelu;
+    if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
+    else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");
+  }
+  LMOE_MARK(4);
+  // ---- stage 4: FC2
+  {
+    lmoe::GemmArgs a;
+    a.A = H; a.lda = m;
+    a.B = w->w2; a.ldb = m; a.b_gstride = int64_t(l) * m;
+    a.b_scale = edt == lmoe::Dt::FP8 ? w->w2_scale : nullptr; a.s_gstride = l;
+    a.C = Y; a.ldc = l;
+    a.N = l; a.K = m;
+    a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);
+    a.act = lmoe::kActNone;
+    if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC2 (stream)");
+    else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");
+  }
+  LMOE_MARK(5);
+  // ---- stage 5: gate-weighted combine (into out directly for the standard MoE)
+  LMOE_TRY(lmoe::launch_combine(Y, slot_of, gate, Ti, K, l, adt, v, s), "combine");
+  LMOE_MARK(6);
+  // ---- stage 6: up-projection
+  if (c.has_projections) {
+    lmoe::GemmArgs a;
+    a.A = v; a.lda = l; a.B = w->w_up; a.ldb = l; a.C = out; a.ldc = d;
+    a.M = Ti; a.N = d; a.K = l;
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, dense_tile(T, d), s), "W_up GEMM");
+  }
+  LMOE_MARK(7);
+
+  // ---- optional copies of intermediate results
+  if (dbg) {
+    auto cp = [&](void* dst, const void* src, size_t bytes, const char* what) -> lmoe_status {
+      if (!dst || bytes == 0) return LMOE_OK;
+      hipError_t r = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+      return r == hipSuccess ? LMOE_OK : hip_fail(r, what);
+    };
+    lmoe_status st;
+    if ((st = cp(dbg->topk_idx, idx, size_t(p.copies) * 4, "copy topk_idx")) != LMOE_OK) return st;
+    if ((st = cp(dbg->topk_gate, gate, size_t(p.copies) * 4, "copy topk_gate")) != LMOE_OK) return st;
+    if ((st = cp(dbg->expert_counts, counts, size_t(N) * 4, "copy counts")) != LMOE_OK) return st;
+    if ((st = cp(dbg->expert_offsets, offsets, size_t(N + 1) * 4, "copy offsets")) != LMOE_OK) return st;
+    if ((st = cp(dbg->slot_of, slot_of, size_t(p.copies) * 4, "copy slot_of")) != LMOE_OK) return st;
+    if ((st = cp(dbg->token_of, token_of, size_t(p.copies) * 4, "copy token_of")) != LMOE_OK) return st;
+    if ((st = cp(dbg->logits, logits, size_t(T) * N * 4, "copy logits")) != LMOE_OK) return st;
+    if (c.has_projections &&
+        (st = cp(dbg->latent, u, size_t(T) * l * ab, "copy latent")) != LMOE_OK) return st;
+  }
+#undef LMOE_MARK
+#undef LMOE_TRY
+  return LMOE_OK;
+}
+
+}  // extern "C"

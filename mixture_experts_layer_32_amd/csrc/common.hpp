@@ -1,0 +1,133 @@
+// Device-side building blocks shared by the LatentMoE kernels (gfx950, wave64).
+//
+// Data movement is done in 16-byte "chunks" (one dwordx4 per lane, type u32x4).  A chunk
+// holds 8 bf16, 4 fp32 or 16 fp8 values.  MFMA operands are consumed one
+// chunk per lane: for v_mfma_f32_16x16x32_bf16 the 64 lanes form 4 groups of
+// 16; lane l supplies row (l % 16) of its operand and the 8 reduction indices
+// of its group (l / 16).  Only the pairing of A and B lanes matters for the
+// reduction, so any fixed assignment of reduction indices to (group, chunk)
+// that both operands share gives the same sum; the kernels use that freedom
+// to make each lane's loads contiguous.
+//
+// Result layout of a 16x16 fp32 accumulator (4 VGPRs): lane l, element v
+// holds C[row = 4 * (l / 16) + v][col = l % 16].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace lmoe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// One 16-byte chunk.  A native vector type (not HIP's uint4 struct) so that
+// selects and copies stay in registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, WGs dispatched round-robin
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Four OCP E4M3 bytes -> four bf16 (packed in two dwords).  Every E4M3
+// value is exactly representable in bf16, so taking the upper half of the
+// fp32 produced by the hardware conversion is exact.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t q) {
+  f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(q), false);
+  f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(q), true);
+  uint2 r;
+  r.x = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+  r.y = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+  return r;
+}
+
+// 16 E4M3 bytes (one chunk) -> 16 bf16 (two chunks).
+__device__ __forceinline__ void fp8_chunk_to_bf16(u32x4 q, u32x4& lo, u32x4& hi) {
+  uint2 a = fp8x4_to_bf16x4(q.x), b = fp8x4_to_bf16x4(q.y);
+  uint2 c = fp8x4_to_bf16x4(q.z), d = fp8x4_to_bf16x4(q.w);
+  lo = u32x4{a.x, a.y, b.x, b.y};
+  hi = u32x4{c.x, c.y, d.x, d.y};
+}
+
+// ---------------------------------------------------------------- MFMA chunks
+
+// acc += A_chunk x B_chunk over the reduction indices the two chunks carry.
+struct MmaBf16 {
+  static constexpr int kElemBytes = 2;
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+};
+
+// fp32: a chunk is 4 values; element s of every group's chunk feeds one
+// v_mfma_f32_16x16x4_f32 (group g supplies reduction index g of that MFMA).
+struct MmaF32 {
+  static constexpr int kElemBytes = 4;
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------- epilogue
+
+template <int ACT>
+__device__ __forceinline__ float apply_act(float v) {
+  if constexpr (ACT == kActSqRelu) {
+    float r = v > 0.f ? v : 0.f;
+    return r * r;
+  } else {
+    return v;
+  }
+}
+
+template <typename TOut>
+__device__ __forceinline__ void store_elem(TOut* p, float v);
+template <>
+__device__ __forceinline__ void store_elem<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// ---------------------------------------------------------------- scheduling
+
+// Work item for workgroup `b` of a grid of `grid` WGs covering `total` items,
+// such that each XCD (b % 8) receives one contiguous range of items: items
+// that share operands (the N tiles of one M tile, the tiles of one expert)
+// then run on the same XCD and share its L2.  Returns -1 for idle WGs.
+// Requires grid to be a multiple of 8 and >= total rounded up to 8.
+__device__ __forceinline__ int xcd_contiguous_item(int b, int grid, int total) {
+  const int per = grid / kNumXcd;
+  const int xcd = b % kNumXcd;
+  const int local = b / kNumXcd;
+  const int per_used = (total + kNumXcd - 1) / kNumXcd;
+  if (local >= per_used) return -1;
+  const int item = xcd * per_used + local;
+  (void)per;
+  return item < total ? item : -1;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+}  // namespace lmoe

@@ -1,0 +1,60 @@
+// Host-side launch interface of the LatentMoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };
+enum ActKind : int { kActNone = 0, kActSqRelu = 1 };
+
+// C = act(scale . (A x B^T)), all operands K-contiguous ("[rows][K]").
+// Dense: one group of M rows.  Grouped: group g owns logical rows
+// [g_off[g], g_off[g+1]) and weight matrix B + g * b_gstride; g_tiles is
+// the exclusive prefix of ceil(rows_g / BM) computed on the device.
+struct GemmArgs {
+  const void* A = nullptr;
+  int64_t lda = 0;                 // elements
+  const int32_t* a_rows = nullptr; // optional gather: A row of logical row r is a_rows[r]
+  const void* B = nullptr;
+  int64_t ldb = 0;                 // elements
+  int64_t b_gstride = 0;           // elements between group weight matrices
+  const float* b_scale = nullptr;  // per output column (row of B) scale, fp8 weights
+  int64_t s_gstride = 0;
+  void* C = nullptr;
+  int64_t ldc = 0;
+  int M = 0, N = 0, K = 0;
+  const int32_t* g_off = nullptr;  // [G+1], nullptr = dense
+  const int32_t* g_tiles = nullptr;// [G+1] (tiled kernel only)
+  int G = 1;
+  int max_rows = 0;                // grouped: upper bound of the total rows (sizes the grid)
+  int act = 0;                     // ActKind
+};
+
+// LDS-tiled MFMA GEMM.  tile: 0 = 128x128 block tile, 1 = 64x64.
+hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s);
+int tiled_block_m(int tile);
+
+// Weight-streaming grouped GEMM for few rows per group (decode regime):
+// every group's weight matrix is streamed from HBM once per pass of up to
+// mrows_max rows.  mb_max: 4 or 8 (rows per pass = 16 * mb_max).
+hipError_t launch_gemm_stream(const GemmArgs& a, Dt a_dt, Dt w_dt, Dt out_dt, int mb_max,
+                              hipStream_t s);
+
+// Routing.
+hipError_t launch_topk_gate(const float* logits, const float* bias, int T, int N, int K,
+                            int gating, int32_t* idx, float* gate, hipStream_t s);
+hipError_t launch_route_masks(const int32_t* idx, int T, int N, int K, uint64_t* masks,
+                              hipStream_t s);
+hipError_t launch_route_scan(const uint64_t* masks, int nblk, int N, int tile_m, int32_t* counts,
+                             int32_t* offsets, int32_t* base, int32_t* tiles, hipStream_t s);
+hipError_t launch_route_assign(const int32_t* idx, const uint64_t* masks, const int32_t* base,
+                               const int32_t* offsets, int T, int N, int K, int32_t* slot_of,
+                               int32_t* token_of, hipStream_t s);
+hipError_t launch_combine(const void* Y, const int32_t* slot_of, const float* gate, int T, int K,
+                          int l, Dt dt, void* v, hipStream_t s);
+
+constexpr int kRouteBlock = 64;  // tokens per routing block (one 64-bit mask per expert)
+
+}  // namespace lmoe

@@ -38,6 +38,18 @@ double orc_e4m3_to_f64(uint8_t code) {
   return s ? -v : v;
 }
 
+/* fp64 -> nearest bf16 value (ties to even), finite inputs: keep 8
+ * significant bits of the binary significand. */
+static double round_bf16(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  double m = frexp(v, &e);             /* v = m 2^e, 0.5 <= |m| < 1 */
+  int bits = 8;
+  if (e - 1 < -126) bits -= -126 - (e - 1);  /* bf16 subnormals */
+  if (bits < 0) return copysign(0.0, v);
+  return ldexp(nearbyint(ldexp(m, bits)), e - bits);
+}
+
 /* element i of a tensor stored as `dtype` (fp8: times the row scale) */
 static inline double ld(const void *p, int dtype, int64_t i, const float *scale, int64_t srow) {
   switch (dtype) {
@@ -80,7 +92,14 @@ static void latent_and_logits(const orc_layer *L, const orc_weights *W, const vo
   const int64_t rw = L->router_on_latent ? l : d;
   for (int64_t e = 0; e < N; ++e) {          /* z = W_r . (x or u) [+ b] */
     double s = 0.0;
-    for (int64_t c = 0; c < rw; ++c) s += ld(W->w_router, L->act_dtype, e * rw + c, NULL, 0) * rin[c];
+    for (int64_t c = 0; c < rw; ++c) {
+      /* a router on the latent reads u as stored in the activation dtype, so
+       * the expert selection is decided on the same input values as the
+       * kernel's; everything else stays unrounded */
+      double r = rin[c];
+      if (L->router_on_latent && L->act_dtype == ORC_BF16) r = round_bf16(r);
+      s += ld(W->w_router, L->act_dtype, e * rw + c, NULL, 0) * r;
+    }
     if (L->has_router_bias) s += (double)W->router_bias[e];
     z[e] = s;
   }

@@ -21,6 +21,9 @@
  * logits; 2 = sigmoid of the selected logits normalised to sum to one.
  * Every sum runs in ascending index order, in fp64, with no intermediate
  * rounding; stored bf16 and fp8 values are upcast exactly (fp8 as q * scale).
+ * One exception: a router placed on the latent u reads u rounded to bf16
+ * when activations are bf16, so that the top-K decision is taken on the
+ * values the GPU kernel routes on.
  */
 #ifndef LATENTMOE_ORACLE_H
 #define LATENTMOE_ORACLE_H

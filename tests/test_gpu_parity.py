@@ -1,0 +1,129 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle on every token and span several tiles with
+ragged tails (T, N, d, l, m not multiples of the tile sizes), both expert
+kernels (weight-streaming and LDS-tiled), fp32 / bf16 / fp8 weights, the
+three gating rules, router bias, router on the latent, the standard MoE and
+degenerate shapes.  Full-size cases run the shapes of the benchmark
+workloads in the same launch configuration as bench.py and compare sampled
+tokens one by one, plus the routing invariants for every token.
+"""
+import numpy as np
+import pytest
+
+import synth
+from synth import LayerSpec, workload
+
+from parity_util import check_against_oracle, check_routing_structure, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(spec, T, seed=0):
+    return synth.make_weights(spec, seed), synth.make_tokens(spec, T, seed)
+
+
+SMALL = {
+    "tiny_f32": (workload("tiny").spec, 64),
+    "tiny_f32_sigmoid_latent_router": (workload("tiny").spec.replace(
+        gating="sigmoid_topk_norm", router_on_latent=True), 64),
+    "bf16_ragged_stream_mb8": (LayerSpec(d=272, l=80, m=208, n_experts=7, top_k=3,
+                                         gating="softmax_all"), 133),
+    "bf16_sigmoid_stream": (LayerSpec(d=512, l=128, m=320, n_experts=24, top_k=5,
+                                      gating="sigmoid_topk_norm"), 300),
+    "bf16_stream_mb4": (LayerSpec(d=256, l=128, m=192, n_experts=64, top_k=4,
+                                  gating="softmax_topk"), 256),
+    "bf16_tiled_experts": (LayerSpec(d=256, l=128, m=192, n_experts=8, top_k=2,
+                                     gating="softmax_topk"), 1000),
+    "bf16_zipf_bias_tiled": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=6,
+                                       gating="softmax_all", has_router_bias=True), 2048),
+    "bf16_zipf_bias_stream_multipass": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
+                                                  gating="softmax_all", has_router_bias=True),
+                                        1024),
+    "bf16_latent_router": (LayerSpec(d=256, l=96, m=128, n_experts=32, top_k=4,
+                                     gating="softmax_topk", router_on_latent=True), 200),
+    "bf16_standard_moe": (LayerSpec(d=256, l=256, m=160, n_experts=16, top_k=2,
+                                    gating="softmax_all", has_projections=False), 257),
+    "fp8_stream_mb8": (LayerSpec(d=512, l=128, m=256, n_experts=16, top_k=4,
+                                 gating="softmax_all", expert_dtype="fp8_e4m3_rowscale"), 200),
+    "fp8_stream_mb4": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
+                                 gating="sigmoid_topk_norm", expert_dtype="fp8_e4m3_rowscale"), 256),
+    "fp8_zipf_multipass": (LayerSpec(d=256, l=96, m=160, n_experts=32, top_k=3,
+                                     gating="softmax_all", expert_dtype="fp8_e4m3_rowscale",
+                                     has_router_bias=True), 700),
+    "f32_tiled_experts": (LayerSpec(d=128, l=64, m=96, n_experts=4, top_k=2,
+                                    gating="softmax_all", act_dtype="f32", expert_dtype="f32"), 600),
+    "one_token": (LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4), 1),
+    "k_equals_n": (LayerSpec(d=128, l=64, m=64, n_experts=8, top_k=8, gating="softmax_all"), 40),
+    "single_expert": (LayerSpec(d=128, l=64, m=64, n_experts=1, top_k=1), 50),
+    "k64_n128": (LayerSpec(d=128, l=64, m=64, n_experts=128, top_k=64, gating="sigmoid_topk_norm"), 30),
+    "n2048": (LayerSpec(d=128, l=64, m=64, n_experts=2048, top_k=16), 64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_case_matches_oracle(name):
+    spec, T = SMALL[name]
+    w, x = _case(spec, T, seed=1)
+    g, layer = run_gpu(spec, w, x)
+    print(name, "regime", layer.expert_regime(T), flush=True)
+    check_routing_structure(spec, g, T)
+    st = check_against_oracle(spec, w, x, g)
+    print(name, st, flush=True)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_identity_projections_equal_standard_moe_bit_exact(act):
+    base = workload("tiny_identity").spec.replace(act_dtype=act, expert_dtype=act)
+    std = base.replace(has_projections=False, identity_projections=False)
+    w, x = _case(base, 64)
+    w_std = {k: v for k, v in w.items() if k not in ("w_down", "w_up")}
+    a, _ = run_gpu(base, w, x)
+    b, _ = run_gpu(std, w_std, x)
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["latent"], x.astype(np.float64) if act == "f32" else a["latent"])
+    check_against_oracle(std, w_std, x, b)
+
+
+def test_repeated_calls_are_bit_identical():
+    spec, T = SMALL["bf16_zipf_bias_tiled"]
+    w, x = _case(spec, T)
+    a, layer = run_gpu(spec, w, x)
+    b, _ = run_gpu(spec, w, x, layer=layer)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_zero_tokens_is_a_noop():
+    import torch
+    import mixture_experts_layer_32_amd as pkg
+    spec = workload("tiny").spec
+    layer = pkg.LatentMoELayer(spec)
+    dev = pkg.to_device(synth.make_weights(spec), "cuda:0")
+    x = torch.empty((0, spec.d), dtype=torch.float32, device="cuda:0")
+    out = layer.forward(x, dev)
+    assert out.shape == (0, spec.d)
+
+
+# ---------------------------------------------------------------- full size
+
+FULL = ["std_decode", "latent_decode", "latent_prefill_zipf", "latent_fp8_sparse"]
+
+
+def _sample_tokens(T, n=48, seed=5):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s), np.int64)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_tokens(name):
+    wl = workload(name)
+    spec, T = wl.spec, wl.T
+    w, x = _case(spec, T, seed=0)
+    g, layer = run_gpu(spec, w, x)
+    print(name, "regime", layer.expert_regime(T), flush=True)
+    check_routing_structure(spec, g, T)
+    st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T))
+    print(name, st, flush=True)

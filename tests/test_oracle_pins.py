@@ -314,3 +314,21 @@ def test_bf16_generator_rounds_to_nearest_even(orc, syn):
     # exact ties go to the even code
     assert syn.f64_to_bf16(1.0 + 2.0 ** -8) == 0x3F80
     assert syn.f64_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82
+
+
+def test_latent_router_bf16_reads_rounded_latent(orc):
+    """A bf16 latent router decides on u rounded to bf16 (the stored latent)."""
+    spec = LayerSpec(d=64, l=32, m=16, n_experts=9, top_k=3, gating="softmax_all",
+                     act_dtype="bf16", expert_dtype="bf16", router_on_latent=True)
+    w, x = _inputs(spec, 12, seed=13)
+    r = orc.forward(spec, w, x, want_logits=True, want_latent=True)
+    u16 = np.array([[orc.bf16_to_f64(__import__("synth").f64_to_bf16(v)) for v in row]
+                    for row in r["latent"]])
+    Wr = _f64(orc, spec, w, "w_router")
+    np.testing.assert_allclose(r["logits"], u16 @ Wr.T, rtol=1e-12, atol=1e-13)
+    # with identity W_down the rounding is a no-op: same as routing on x
+    ident = workload("tiny_identity").spec.replace(act_dtype="bf16", expert_dtype="bf16")
+    wi, xi = _inputs(ident, 20, seed=6)
+    a = orc.forward(ident, wi, xi)
+    b = orc.forward(ident.replace(router_on_latent=True), wi, xi)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["out"], b["out"])
