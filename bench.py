@@ -53,9 +53,12 @@ def expert_kernel_work(spec, T, counts, stage):
 
 
 def cpu_baseline(spec, w_np, x_np, budget_s=15.0):
+    """The fp64 oracle on the first n tokens of the batch, n sized so that the
+    run takes about budget_s seconds on this host's cores."""
     import oracle
     T = x_np.shape[0]
-    n = 4
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n = min(T, 2 * threads)                      # probe: two tokens per thread
     t0 = time.perf_counter()
     oracle.forward(spec, w_np, x_np, tokens=list(range(n)))
     dt = time.perf_counter() - t0
@@ -64,7 +67,6 @@ def cpu_baseline(spec, w_np, x_np, budget_s=15.0):
     t0 = time.perf_counter()
     oracle.forward(spec, w_np, x_np, tokens=list(range(n2)))
     dt2 = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": n2 / dt2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "first %d of the %d tokens of the same batch, full layer in fp64 "
                       "(%.1f s)" % (n2, T, dt2)}
@@ -78,6 +80,10 @@ def main():
     ap.add_argument("--workload", default="latent_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (known HBM traffic: "
+                         "1 GiB read + 1 GiB written per launch) to scale rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
@@ -88,6 +94,17 @@ def main():
     import torch
     import mixture_experts_layer_32_amd as pkg
     import synth
+
+    if args.copy_calibration:
+        a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": 1 << 30,
+                          "bytes_written_per_launch": 1 << 30, "launches": 5}))
+        return
 
     wl = synth.workload(args.workload)
     spec, T = wl.spec, wl.T

@@ -16,7 +16,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblatentmoe.so")
+# LATENTMOE_LIB selects another build of the same library (e.g. a variant
+# compiled with different tile constants); default: the in-tree build.
+LIB_PATH = os.environ.get("LATENTMOE_LIB") or os.path.join(HERE, "liblatentmoe.so")
 
 LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE = 0, 1, 2
 ROUTER_ON_X, ROUTER_ON_LATENT = 0, 1

@@ -21,7 +21,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/latentmoe.h"
+#include "latentmoe.h"
 #include "kernels.hpp"
 
 struct lmoe_handle {
@@ -347,7 +347,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   // ---- stage 3: FC1 + squared ReLU, token rows gathered through token_of
   {
     lmoe::GemmArgs a;
-    a.A = u; a.lda = l; a.a_rows = token_of;
+    a.A = u; a.lda = l; a.a_rows = token_of; a.a_nrows = Ti;
     a.B = w->w1; a.ldb = l; a.b_gstride = int64_t(m) * l;
     a.b_scale = edt == lmoe::Dt::FP8 ? w->w1_scale : nullptr; a.s_gstride = m;
     a.C = H; a.ldc = m;

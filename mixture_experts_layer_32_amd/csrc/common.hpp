@@ -30,6 +30,39 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, WGs dispatched round-robin
 
+// A 16-byte zero chunk in global memory (one per translation unit).  Loads of
+// padding rows and of chunks past the end of K read it: selecting the ADDRESS
+// keeps the loaded value usable as is, whereas selecting between the loaded
+// value and zero would force a wait on the load right where it is issued.
+static __device__ __attribute__((aligned(16))) uint32_t g_zero_chunk[4] = {0u, 0u, 0u, 0u};
+
+__device__ __forceinline__ u32x4 load_chunk(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Raw (byte-addressed, stride 0) buffer resource: 64-bit base in SGPRs, a
+// byte range, and dword 3 = DATA_FORMAT 32-bit (value 4 in bits 15..18).
+// A buffer load whose offset lies past the range returns zeros, so loads
+// need only a 32-bit per-lane offset and padding costs no select on data.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset that always reads as zero
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes >= 0x80000000ull ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Cache policy of a buffer load: 0 = default, kCpolNonTemporal = data read
+// once (expert weights): streamed without displacing reused lines.
+constexpr int kCpolDefault = 0;
+constexpr int kCpolNonTemporal = 2;
+
+template <int CPOL = kCpolDefault>
+__device__ __forceinline__ u32x4 buffer_load_chunk(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       r, static_cast<int>(voff), static_cast<int>(soff), CPOL));
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

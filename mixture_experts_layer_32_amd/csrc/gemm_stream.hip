@@ -9,11 +9,10 @@
 //    one expert are contiguous work items, hence on one XCD, sharing the
 //    expert's token rows in that XCD's L2.
 //  - Each wave streams its own 16 * NWB weight rows straight from global
-//    memory into registers in the MFMA B-operand layout (4 lanes per weight
-//    row, 16 contiguous bytes each, so a load instruction reads 64 contiguous
-//    bytes of each of 16 rows and two consecutive ones complete 128-byte
-//    lines); the next K stage of weights is in flight while the current one
-//    is multiplied.
+//    memory into registers in the MFMA B-operand layout with raw buffer
+//    loads: 4 lanes per weight row side by side, so one load instruction
+//    reads 64 contiguous bytes of each of 16 rows.  The next K stage of
+//    weights is in flight while the current one is multiplied.
 //  - The (at most 16 * MB_MAX) token rows of the expert are staged through LDS
 //    per K stage (double-buffered), gathered through token_of for FC1: this is
 //    the dispatch of the token copies, done without materialising them.
@@ -22,125 +21,120 @@
 // Experts with more rows than one pass holds are processed in several passes
 // (the weights are then streamed once per pass).
 //
-// Reduction-index assignment within a 256-byte stage of A (bf16, fp8
-// weights): MFMA step s (32 indices) takes, for lane group q, the 8 indices
-// starting at 64 * (s / 2) + 16 * q + 8 * (s % 2), so a lane owns 16
-// consecutive indices of every 64 (one fp8 chunk, or two bf16 chunks).
+// Out-of-range buffer offsets read as zero: padding token rows and token
+// chunks past the end of K use that, so no select on loaded data delays a
+// wait.  Weight chunks past the end of K (only when K is not a multiple of
+// the stage) read neighbouring weights or zero; they meet zero token values.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace lmoe {
 namespace {
 
-template <typename TA> struct StreamTraits;
-template <> struct StreamTraits<uint16_t> {  // bf16 activations
-  static constexpr int EPC = 8;              // elements per 16-byte chunk
-  static constexpr int KSTEP = 32;           // reduction indices per MFMA
-  __device__ __forceinline__ static int elem_of(int s, int q) {
+// Reduction indices, within a K stage, that lane group q supplies to MFMA
+// step s.  Every weight load instruction then reads 64 contiguous bytes of
+// each of its 16 weight rows (the 4 groups side by side).
+template <typename TA, typename TW> struct StreamTraits;
+template <> struct StreamTraits<uint16_t, uint16_t> {  // bf16 tokens, bf16 weights
+  static constexpr int EPC = 8;                         // elements per 16-byte chunk
+  static constexpr int KSTEP = 32;                      // reduction indices per MFMA
+  __device__ __forceinline__ static int elem_of(int s, int q) { return 32 * s + 8 * q; }
+};
+template <> struct StreamTraits<uint16_t, uint8_t> {   // bf16 tokens, fp8 weights:
+  static constexpr int EPC = 8;                         // a lane owns the 16 consecutive
+  static constexpr int KSTEP = 32;                      // indices of one fp8 chunk, used
+  __device__ __forceinline__ static int elem_of(int s, int q) {  // by steps 2j and 2j+1
     return 64 * (s >> 1) + 16 * q + 8 * (s & 1);
   }
 };
-template <> struct StreamTraits<float> {     // fp32 activations and weights
+template <> struct StreamTraits<float, float> {        // fp32 tokens and weights
   static constexpr int EPC = 4;
   static constexpr int KSTEP = 16;
   __device__ __forceinline__ static int elem_of(int s, int q) { return 16 * s + 4 * q; }
 };
 
+#ifndef LMOE_W_CPOL
+#define LMOE_W_CPOL kCpolDefault
+#endif
+
 constexpr int kStageChunks = 16;  // 16-byte chunks of A per row per K stage (256 bytes)
 
-// MB_MAX m-blocks of 16 rows per pass, NWB n-blocks of 16 weight rows per wave.
-template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NWB, int ACT,
-          bool SCALE>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
-  using Tr = StreamTraits<TA>;
+// Per-workgroup context of the streaming kernel.
+template <typename TOut, int NWB>
+struct StreamCtx {
+  BufRsrc a_rsrc, w_rsrc;
+  uint32_t w_off[NWB];   // byte offset of this lane's part of its weight row, per n-block
+  TOut* C;
+  const float* sc;       // per-column scales of this group (fp8) or nullptr
+  const int32_t* a_rows; // gather index (FC1) or nullptr (rows relative to the group)
+  uint32_t a_row_bytes;  // lda * sizeof(TA)
+  int64_t ldc;
+  int K, N, gs, col0, wave, fr, fq, ac, ar0;
+};
+
+// One pass over up to 16 * NMB rows of a group: stream the group's weight
+// tile through registers once, multiply with the staged token rows.
+template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NMB, int NWB,
+          int ACT, bool SCALE>
+__device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p0, int rows,
+                                            u32x4 (*As)[MB_MAX * 16 * kStageChunks]) {
+  using Tr = StreamTraits<TA, TW>;
   constexpr int EPC = Tr::EPC;
   constexpr int KE = kStageChunks * EPC;    // reduction elements per stage
   constexpr int NS = KE / Tr::KSTEP;        // MFMA steps per stage (4)
   constexpr bool FP8 = sizeof(TW) == 1;
   constexpr int NLD = FP8 ? NS / 2 : NS;    // 16-byte weight loads per n-block per stage
-  constexpr int MROWS = MB_MAX * 16;
-  constexpr int NT = 4 * NWB * 16;          // output columns per workgroup
-  static_assert(NS % 2 == 0, "stage must hold whole fp8 chunks");
-
-  __shared__ u32x4 As[2][MROWS * kStageChunks];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int fr = lane & 15, fq = lane >> 4;
-
-  const int n_tiles = (p.N + NT - 1) / NT;
-  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x, p.G * n_tiles);
-  if (item < 0) return;
-  const int g = item / n_tiles;
-  const int col0 = (item % n_tiles) * NT;
-  const int gs = p.g_off[g];
-  const int cnt = p.g_off[g + 1] - gs;
-  if (cnt <= 0) return;
-
-  const int K = p.K;
+  constexpr uint32_t W_STAGE_BYTES = KE * sizeof(TW);
+  constexpr uint32_t A_STAGE_BYTES = KE * sizeof(TA);
+  const int K = c.K;
   const int nst = (K + KE - 1) / KE;
-  const TA* __restrict__ A = static_cast<const TA*>(p.A);
 
-  // weight rows of this lane (one per n-block), clamped into the matrix
-  const TW* wrow[NWB];
+  // byte offset of this thread's staged token rows (out of range = padding)
+  uint32_t a_row_off[NMB];
 #pragma unroll
-  for (int nb = 0; nb < NWB; ++nb) {
-    int n = col0 + wave * NWB * 16 + nb * 16 + fr;
-    n = n < p.N ? n : p.N - 1;
-    wrow[nb] = static_cast<const TW*>(p.B) + (int64_t)g * p.b_gstride + (int64_t)n * p.ldb;
-  }
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  TOut* C = static_cast<TOut*>(p.C);
-  const float* sc = SCALE ? p.b_scale + (int64_t)g * p.s_gstride : nullptr;
-
-  // A staging: thread owns chunk column ac of rows ar0 + 16 i
-  const int ac = tid & 15;
-  const int ar0 = tid >> 4;
-
-  for (int p0 = 0; p0 < cnt; p0 += MROWS) {
-    const int rows = min(MROWS, cnt - p0);
-    const int nmb = (rows + 15) >> 4;
-
-    int arow[MB_MAX];  // source row of A for each staged row, -1 = padding
-#pragma unroll
-    for (int i = 0; i < MB_MAX; ++i) {
-      const int r = ar0 + 16 * i;
-      arow[i] = r < rows ? (p.a_rows ? p.a_rows[gs + p0 + r] : gs + p0 + r) : -1;
+  for (int i = 0; i < NMB; ++i) {
+    const int r = c.ar0 + 16 * i;
+    if (r < rows) {
+      const int row = c.a_rows ? c.a_rows[c.gs + p0 + r] : p0 + r;
+      a_row_off[i] = static_cast<uint32_t>(row) * c.a_row_bytes + c.ac * 16u;
+    } else {
+      a_row_off[i] = kOutOfRange;
     }
+  }
 
-    f32x4_t acc[MB_MAX][NWB];
+  f32x4_t acc[NMB][NWB];
 #pragma unroll
-    for (int i = 0; i < MB_MAX; ++i)
+  for (int i = 0; i < NMB; ++i)
 #pragma unroll
-      for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ra[MB_MAX];
-    u32x4 b0[NWB][NLD], b1[NWB][NLD];
+  u32x4 ra0[NMB], ra1[NMB];
+  u32x4 b0[NWB][NLD], b1[NWB][NLD];
 
-#define LMOE_LOAD_A(st)                                                                      \
+  // token chunk (row i, column ac) of stage st; past the end of K -> zero
+#define LMOE_LOAD_A(st, ra)                                                                  \
   do {                                                                                       \
-    const int k_ = (st) * KE + ac * EPC;                                                     \
-    _Pragma("unroll") for (int i = 0; i < MB_MAX; ++i) {                                     \
-      const bool ok_ = arow[i] >= 0 && k_ < K;                                               \
-      const u32x4 v_ = *reinterpret_cast<const u32x4*>(                                      \
-          A + (ok_ ? (int64_t)arow[i] * p.lda + k_ : (int64_t)0));                            \
-      ra[i] = ok_ ? v_ : zero;                                                               \
+    const bool in_k_ = (st) * KE + c.ac * EPC < K;                                           \
+    const uint32_t so_ = (st) * A_STAGE_BYTES;                                               \
+    _Pragma("unroll") for (int i = 0; i < NMB; ++i)                                          \
+      ra[i] = buffer_load_chunk(c.a_rsrc, in_k_ ? a_row_off[i] : kOutOfRange, so_);         \
+  } while (0)
+#define LMOE_STORE_A(buf, ra)                                                                \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < NMB; ++i) {                                        \
+      const int r_ = c.ar0 + 16 * i;                                                         \
+      As[buf][r_ * kStageChunks + (c.ac ^ (r_ & 15))] = ra[i];                               \
     }                                                                                        \
   } while (0)
-#define LMOE_STORE_A(buf)                                                                    \
-  do {                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < MB_MAX; ++i) {                                     \
-      const int r_ = ar0 + 16 * i;                                                           \
-      As[buf][r_ * kStageChunks + (ac ^ (r_ & 15))] = ra[i];                                 \
-    }                                                                                        \
-  } while (0)
+  // weight chunk j of stage st for each n-block; the chunk's byte position
+  // inside the stage is a compile-time constant folded into the instruction
 #define LMOE_LOAD_W(st, br)                                                                  \
   do {                                                                                       \
+    const uint32_t so_ = (st) * W_STAGE_BYTES;                                               \
     _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb)                                       \
     _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                        \
-      const int k_ = (st) * KE + (FP8 ? 64 * j + 16 * fq : Tr::elem_of(j, fq));             \
-      const u32x4 v_ = *reinterpret_cast<const u32x4*>(wrow[nb] + (k_ < K ? k_ : 0));        \
-      br[nb][j] = k_ < K ? v_ : zero;                                                        \
+      const uint32_t imm_ = 64u * j;                                                          \
+      br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(c.w_rsrc, c.w_off[nb] + imm_, so_);        \
     }                                                                                        \
   } while (0)
 #define LMOE_COMPUTE(buf, br)                                                                \
@@ -156,71 +150,180 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
           bfr[nb] = br[nb][s];                                                               \
         }                                                                                    \
       }                                                                                      \
-      const int c_ = Tr::elem_of(s, fq) / EPC;                                               \
-      _Pragma("unroll") for (int mb = 0; mb < MB_MAX; ++mb) {                                \
-        if (mb < nmb) {                                                                      \
-          const int r_ = mb * 16 + fr;                                                       \
-          const u32x4 af_ = As[buf][r_ * kStageChunks + (c_ ^ (r_ & 15))];                   \
-          _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb) Mma::mma(acc[mb][nb], af_, bfr[nb]); \
-        }                                                                                    \
+      const int c_ = Tr::elem_of(s, c.fq) / EPC;                                             \
+      _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb) {                                   \
+        const int r_ = mb * 16 + c.fr;                                                       \
+        const u32x4 af_ = As[buf][r_ * kStageChunks + (c_ ^ (r_ & 15))];                     \
+        _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb) Mma::mma(acc[mb][nb], af_, bfr[nb]); \
       }                                                                                      \
     }                                                                                        \
   } while (0)
 
-    // prologue: A then W of stage 0 (A is waited on first, W stays in flight)
-    LMOE_LOAD_A(0);
-    LMOE_LOAD_W(0, b0);
-    LMOE_STORE_A(0);
-    __syncthreads();
-    for (int st = 0; st < nst; st += 2) {
-      // even stage: compute from b0 / LDS buffer 0, prefetch stage st+1 into b1
-      if (st + 1 < nst) { LMOE_LOAD_A(st + 1); LMOE_LOAD_W(st + 1, b1); }
-      LMOE_COMPUTE(0, b0);
-      if (st + 1 < nst) LMOE_STORE_A(1);
-      __syncthreads();
-      if (st + 1 >= nst) break;
-      // odd stage: compute from b1 / LDS buffer 1, prefetch stage st+2 into b0
-      if (st + 2 < nst) { LMOE_LOAD_A(st + 2); LMOE_LOAD_W(st + 2, b0); }
-      LMOE_COMPUTE(1, b1);
-      if (st + 2 < nst) LMOE_STORE_A(0);
-      __syncthreads();
-    }
+  // Stage st is multiplied from register buffer b(st%2) and LDS buffer st%2.
+  // Its weights were requested one stage earlier; its token rows two stages
+  // earlier (into register set ra(st%2)) and written to LDS one stage
+  // earlier, so the token-row latency never sets the stage rate.  Every
+  // prefetch is unconditional (past the end of K it reads zeros or is never
+  // used) and is issued before the multiplies it overlaps.
+  LMOE_LOAD_A(0, ra0);
+  LMOE_LOAD_W(0, b0);
+  LMOE_LOAD_A(1, ra1);
+  LMOE_STORE_A(0, ra0);
+  __syncthreads();
+#define LMOE_STEP(st, bcur, bnext, ra_free, ra_next)     \
+  do {                                                   \
+    LMOE_LOAD_W((st) + 1, bnext);                        \
+    LMOE_LOAD_A((st) + 2, ra_free);                      \
+    __builtin_amdgcn_sched_barrier(0);                   \
+    LMOE_COMPUTE((st) & 1, bcur);                        \
+    LMOE_STORE_A(((st) + 1) & 1, ra_next);               \
+    __syncthreads();                                     \
+  } while (0)
+  for (int st = 0; st < nst; st += 2) {
+    LMOE_STEP(st, b0, b1, ra0, ra1);
+    if (st + 1 >= nst) break;
+    LMOE_STEP(st + 1, b1, b0, ra1, ra0);
+  }
+#undef LMOE_STEP
 #undef LMOE_LOAD_A
 #undef LMOE_STORE_A
 #undef LMOE_LOAD_W
 #undef LMOE_COMPUTE
 
-    // epilogue: accumulator lane layout C[4*fq + v][fr] of each 16x16 block
+  // Epilogue.  The accumulator holds C[4*fq + v][fr] of each 16x16 block, so
+  // direct stores would be 2- or 4-byte pieces scattered over many rows.  The
+  // tile goes through LDS instead (the token-row buffers are free after the
+  // last barrier) and leaves as whole 16-byte chunks of contiguous row
+  // segments.
+  constexpr int NT = 4 * NWB * 16;            // columns of the workgroup tile
+  constexpr int CPR = NT * sizeof(TOut) / 16; // 16-byte chunks per tile row
+  static_assert(MB_MAX * 16 * NT * sizeof(TOut) <= sizeof(u32x4) * 2 * MB_MAX * 16 * kStageChunks,
+                "output tile must fit the LDS staging buffers");
+  TOut* Ct = reinterpret_cast<TOut*>(&As[0][0]);
 #pragma unroll
-    for (int nb = 0; nb < NWB; ++nb) {
-      const int col = col0 + wave * NWB * 16 + nb * 16 + fr;
-      if (col >= p.N) continue;
-      const float s = SCALE ? sc[col] : 1.f;
+  for (int nb = 0; nb < NWB; ++nb) {
+    const int colt = c.wave * NWB * 16 + nb * 16 + c.fr;
+    const int col = c.col0 + colt;
+    const float s = (SCALE && col < c.N) ? c.sc[col] : 1.f;
 #pragma unroll
-      for (int mb = 0; mb < MB_MAX; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = mb * 16 + fq * 4 + v;
-          if (r < rows) {
-            float val = acc[mb][nb][v];
-            if (SCALE) val *= s;
-            store_elem<TOut>(C + (int64_t)(gs + p0 + r) * p.ldc + col, apply_act<ACT>(val));
-          }
-        }
+      for (int v = 0; v < 4; ++v) {
+        float val = acc[mb][nb][v];
+        if (SCALE) val *= s;
+        store_elem<TOut>(Ct + (mb * 16 + c.fq * 4 + v) * NT + colt, apply_act<ACT>(val));
       }
     }
   }
+  __syncthreads();
+  const u32x4* Cv = reinterpret_cast<const u32x4*>(Ct);
+  for (int q = c.wave * 64 + c.fq * 16 + c.fr; q < rows * CPR; q += 256) {
+    const int r = q / CPR, ch = q % CPR;
+    const int col = c.col0 + ch * (16 / static_cast<int>(sizeof(TOut)));
+    if (col < c.N)  // N is a multiple of 16 elements: a chunk is all in or all out
+      *reinterpret_cast<u32x4*>(c.C + (int64_t)(c.gs + p0 + r) * c.ldc + col) = Cv[q];
+  }
 }
+
+// MB_MAX m-blocks of 16 rows per pass, NWB n-blocks of 16 weight rows per wave.
+// One workgroup per work item (group, tile of NT columns); items are ordered
+// so that each XCD receives one contiguous range of them.
+template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NWB, int ACT,
+          bool SCALE>
+__global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? 2 : 1) void gemm_stream_kernel(GemmArgs p) {
+  constexpr int MROWS = MB_MAX * 16;
+  constexpr int NT = 4 * NWB * 16;          // output columns per work item
+  __shared__ u32x4 As[2][MROWS * kStageChunks];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n_tiles = (p.N + NT - 1) / NT;
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x, p.G * n_tiles);
+  if (item < 0) return;
+  const int g = item / n_tiles;
+  const int gs = p.g_off[g];
+  const int cnt = p.g_off[g + 1] - gs;
+  if (cnt <= 0) return;
+
+  StreamCtx<TOut, NWB> c;
+  // token rows: the whole A for a gather, else the group's own rows
+  const TA* abase = static_cast<const TA*>(p.A);
+  if (!p.a_rows) abase += (int64_t)gs * p.lda;
+  const uint64_t a_bytes = (uint64_t)(p.a_rows ? p.a_nrows : cnt) * p.lda * sizeof(TA);
+  c.a_rsrc = make_rsrc(abase, a_bytes);
+  const TW* wbase = static_cast<const TW*>(p.B) + (int64_t)g * p.b_gstride;
+  c.w_rsrc = make_rsrc(wbase, (uint64_t)p.N * p.ldb * sizeof(TW));
+  c.C = static_cast<TOut*>(p.C);
+  c.sc = SCALE ? p.b_scale + (int64_t)g * p.s_gstride : nullptr;
+  c.a_rows = p.a_rows;
+  c.a_row_bytes = static_cast<uint32_t>(p.lda * sizeof(TA));
+  c.ldc = p.ldc;
+  c.K = p.K;
+  c.N = p.N;
+  c.gs = gs;
+  c.col0 = (item % n_tiles) * NT;
+  c.wave = wave;
+  c.fr = lane & 15;
+  c.fq = lane >> 4;
+  c.ac = tid & 15;   // A staging: thread owns chunk column ac of rows ar0 + 16 i
+  c.ar0 = tid >> 4;
+  // byte position of this lane's first chunk in its weight row (lane group
+  // fq supplies 16 bytes of every 64); rows past N read as zero
+#pragma unroll
+  for (int nb = 0; nb < NWB; ++nb) {
+    const int n = c.col0 + wave * NWB * 16 + nb * 16 + c.fr;
+    c.w_off[nb] = n < p.N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(p.ldb * sizeof(TW)) +
+                                16u * c.fq
+                          : kOutOfRange;
+  }
+
+  for (int p0 = 0; p0 < cnt; p0 += MROWS) {
+    const int rows = min(MROWS, cnt - p0);
+    const int nmb = (rows + 15) >> 4;
+#define LMOE_PASS(n) \
+  stream_pass<Mma, TA, TW, TOut, MB_MAX, n, NWB, ACT, SCALE>(c, p0, rows, As)
+    if constexpr (MB_MAX == 4) {
+      switch (nmb) {
+        case 1: LMOE_PASS(1); break;
+        case 2: LMOE_PASS(2); break;
+        case 3: LMOE_PASS(3); break;
+        default: LMOE_PASS(4); break;
+      }
+    } else {
+      switch (nmb) {
+        case 1: LMOE_PASS(1); break;
+        case 2: LMOE_PASS(2); break;
+        case 3: LMOE_PASS(3); break;
+        case 4: LMOE_PASS(4); break;
+        case 5: LMOE_PASS(5); break;
+        case 6: LMOE_PASS(6); break;
+        case 7: LMOE_PASS(7); break;
+        default: LMOE_PASS(8); break;
+      }
+    }
+#undef LMOE_PASS
+    __syncthreads();  // the next pass restages the LDS buffers
+  }
+}
+
+#ifndef LMOE_STREAM_NWB
+#define LMOE_STREAM_NWB 2
+#endif
 
 template <typename Mma, typename TA, typename TW, typename TOut, int MB>
 hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
-  constexpr int NWB = 2;
+  constexpr int NWB = LMOE_STREAM_NWB;
   constexpr int NT = 4 * NWB * 16;
   const int64_t n_tiles = (a.N + NT - 1) / NT;
   const int64_t total = n_tiles * a.G;
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  // 32-bit buffer offsets: token rows and one expert matrix stay below 2 GiB
+  const uint64_t a_rows = a.a_rows ? (uint64_t)a.a_nrows : (uint64_t)a.max_rows;
+  if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) ||
+      (uint64_t)a.N * a.ldb * sizeof(TW) >= (1ull << 31))
+    return hipErrorInvalidValue;
   const bool scale = a.b_scale != nullptr;
   if (a.act == kActSqRelu) {
     if (scale) gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActSqRelu, true><<<dim3(grid), dim3(256), 0, s>>>(a);

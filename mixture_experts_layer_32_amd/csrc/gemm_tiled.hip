@@ -90,15 +90,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs p) {
   }
 
   u32x4 ra[ACH], rb[BCH];
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+  const void* zp = g_zero_chunk;
   auto load_stage = [&](int kt) {
     const int kb = kt * BKE;
 #pragma unroll
     for (int i = 0; i < ACH; ++i)
-      ra[i] = (a_ok[i] && kb + a_k[i] < K) ? *reinterpret_cast<const u32x4*>(a_src[i] + kb) : zero;
+      ra[i] = load_chunk((a_ok[i] && kb + a_k[i] < K) ? static_cast<const void*>(a_src[i] + kb) : zp);
 #pragma unroll
     for (int i = 0; i < BCH; ++i)
-      rb[i] = (b_ok[i] && kb + b_k[i] < K) ? *reinterpret_cast<const u32x4*>(b_src[i] + kb) : zero;
+      rb[i] = load_chunk((b_ok[i] && kb + b_k[i] < K) ? static_cast<const void*>(b_src[i] + kb) : zp);
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs p) {
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
+    load_stage(kt + 1);  // unconditional: past the end of K it reads the zero chunk
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = ks * 4 + fq;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) Mma::mma(acc[i][j], af[i], bfr[j]);
     }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
+    store_stage(buf ^ 1);
     __syncthreads();
   }
 

@@ -17,6 +17,7 @@ struct GemmArgs {
   const void* A = nullptr;
   int64_t lda = 0;                 // elements
   const int32_t* a_rows = nullptr; // optional gather: A row of logical row r is a_rows[r]
+  int a_nrows = 0;                 // rows of A (bounds the gathered reads)
   const void* B = nullptr;
   int64_t ldb = 0;                 // elements
   int64_t b_gstride = 0;           // elements between group weight matrices
