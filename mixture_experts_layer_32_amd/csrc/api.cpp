@@ -16,6 +16,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -67,6 +68,34 @@ lmoe::Dt exp_dt(const lmoe_config& c) {
 }
 size_t act_bytes(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? 4 : 2; }
 
+// Tile config and K split of one dense GEMM (M x N x K): the large tile when
+// it still gives two workgroups per compute unit, else the small one; split K
+// when even the small tiles leave the device under-filled, keeping at least
+// 8 K stages per split.
+struct DensePlan {
+  int tile = 1;
+  int splits = 1;
+};
+
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K, size_t elem_bytes) {
+  constexpr int64_t kTargetWorkgroups = 512;  // two per compute unit of an MI355X
+  DensePlan d;
+  if (M <= 0 || N <= 0 || K <= 0) return d;
+  const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
+  if (big >= kTargetWorkgroups) {
+    d.tile = 0;
+    return d;
+  }
+  d.tile = 1;
+  const int64_t small = ((M + 63) / 64) * ((N + 63) / 64);
+  const int64_t stages = (K * int64_t(elem_bytes) + 127) / 128;
+  int64_t s = (kTargetWorkgroups + small - 1) / small;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
+  if (N % 4) s = 1;
+  d.splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
+  return d;
+}
+
 struct Plan {
   int64_t T = 0, copies = 0;
   int nblk = 0;
@@ -74,7 +103,9 @@ struct Plan {
   int mb_max = 4;       // streaming kernel rows per pass / 16
   int expert_tile = 0;  // tiled kernel tile config
   int tile_m = 128;
-  size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, total;
+  DensePlan down, router, up;
+  size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, partial,
+      total;
 };
 
 Plan make_plan(const lmoe_config& c, int64_t T) {
@@ -88,6 +119,16 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.expert_tile = 0;
   p.tile_m = lmoe::tiled_block_m(p.expert_tile);
   const size_t ab = act_bytes(c);
+  const int64_t r_in = c.router_input == LMOE_ROUTER_ON_LATENT ? c.l : c.d;
+  size_t partial = 0;
+  if (c.has_projections) {
+    p.down = plan_dense(T, c.l, c.d, ab);
+    p.up = plan_dense(T, c.d, c.l, ab);
+    partial = std::max(partial, size_t(p.down.splits > 1 ? p.down.splits : 0) * T * c.l * 4);
+    partial = std::max(partial, size_t(p.up.splits > 1 ? p.up.splits : 0) * T * c.d * 4);
+  }
+  p.router = plan_dense(T, c.n_experts, r_in, ab);
+  partial = std::max(partial, size_t(p.router.splits > 1 ? p.router.splits : 0) * T * c.n_experts * 4);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.u = take(c.has_projections ? size_t(T) * c.l * ab : 0);
@@ -104,15 +145,9 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.H = take(size_t(p.copies) * c.m * ab);
   p.Y = take(size_t(p.copies) * c.l * ab);
   p.v = take(c.has_projections ? size_t(T) * c.l * ab : 0);
+  p.partial = take(partial);
   p.total = o;
   return p;
-}
-
-// Tile config of a dense GEMM: the large tile when it still gives two
-// workgroups per compute unit, else the small one.
-int dense_tile(int64_t M, int64_t N) {
-  const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
-  return big >= 512 ? 0 : 1;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -297,6 +332,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   void* H = ws + p.H;
   void* Y = ws + p.Y;
   void* v = c.has_projections ? ws + p.v : out;
+  float* partial = reinterpret_cast<float*>(ws + p.partial);
 
   lmoe_timer* tm = dbg ? dbg->timer : nullptr;
   hipEvent_t* ev = nullptr;
@@ -321,7 +357,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     lmoe::GemmArgs a;
     a.A = x; a.lda = d; a.B = w->w_down; a.ldb = d; a.C = u; a.ldc = l;
     a.M = Ti; a.N = l; a.K = d;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, dense_tile(T, l), s), "W_down GEMM");
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial), "W_down GEMM");
   }
   {
     const bool lat = c.router_input == LMOE_ROUTER_ON_LATENT;
@@ -330,7 +366,8 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     a.B = w->w_router; a.ldb = lat ? l : d;
     a.C = logits; a.ldc = N;
     a.M = Ti; a.N = N; a.K = lat ? l : d;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, lmoe::Dt::F32, dense_tile(T, N), s), "router GEMM");
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, lmoe::Dt::F32, p.router.tile, s, p.router.splits, partial),
+             "router GEMM");
   }
   LMOE_MARK(1);
   // ---- stage 1: top-k and gates
@@ -361,7 +398,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   // ---- stage 4: FC2
   {
     lmoe::GemmArgs a;
-    a.A = H; a.lda = m;
+    a.A = H; a.lda = m; a.a_nrows = static_cast<int>(p.copies);
     a.B = w->w2; a.ldb = m; a.b_gstride = int64_t(l) * m;
     a.b_scale = edt == lmoe::Dt::FP8 ? w->w2_scale : nullptr; a.s_gstride = l;
     a.C = Y; a.ldc = l;
@@ -380,7 +417,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     lmoe::GemmArgs a;
     a.A = v; a.lda = l; a.B = w->w_up; a.ldb = l; a.C = out; a.ldc = d;
     a.M = Ti; a.N = d; a.K = l;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, dense_tile(T, d), s), "W_up GEMM");
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.up.tile, s, p.up.splits, partial), "W_up GEMM");
   }
   LMOE_MARK(7);
 

@@ -319,6 +319,9 @@ hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  // the epilogue stores whole 16-byte chunks: output width and stride are
+  // multiples of 16 elements (true of the expert widths m and l)
+  if (a.N % 16 || a.ldc % 16) return hipErrorInvalidValue;
   // 32-bit buffer offsets: token rows and one expert matrix stay below 2 GiB
   const uint64_t a_rows = a.a_rows ? (uint64_t)a.a_nrows : (uint64_t)a.max_rows;
   if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) ||

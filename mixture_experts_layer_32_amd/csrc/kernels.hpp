@@ -34,7 +34,10 @@ struct GemmArgs {
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128 block tile, 1 = 64x64.
-hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s);
+// splits > 1 (dense only): K is split and fp32 partial tiles go to `partial`
+// ([splits][M][N] floats) before a fixed-order reduction.
+hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s,
+                             int splits = 1, float* partial = nullptr);
 int tiled_block_m(int tile);
 
 // Weight-streaming grouped GEMM for few rows per group (decode regime):

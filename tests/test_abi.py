@@ -114,3 +114,10 @@ def test_status_strings():
     lib = pkg.lib()
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert lib.latentmoe_status_string(s)
+
+
+def test_workspace_size_for_zero_and_one_token():
+    for name in ("tiny", "latent_decode", "std_decode"):
+        lay = pkg.LatentMoELayer(__import__("synth").workload(name).spec)
+        assert lay.workspace_size(0) >= 0
+        assert lay.workspace_size(1) > 0

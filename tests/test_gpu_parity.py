@@ -53,6 +53,9 @@ SMALL = {
                                      has_router_bias=True), 700),
     "f32_tiled_experts": (LayerSpec(d=128, l=64, m=96, n_experts=4, top_k=2,
                                     gating="softmax_all", act_dtype="f32", expert_dtype="f32"), 600),
+    # dense GEMMs split K in two (17 stages: 9 + 8) and reduce the fp32 partials
+    "bf16_splitk_ragged": (LayerSpec(d=1040, l=64, m=128, n_experts=20, top_k=3,
+                                     gating="softmax_all"), 100),
     "one_token": (LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4), 1),
     "k_equals_n": (LayerSpec(d=128, l=64, m=64, n_experts=8, top_k=8, gating="softmax_all"), 40),
     "single_expert": (LayerSpec(d=128, l=64, m=64, n_experts=1, top_k=1), 50),
