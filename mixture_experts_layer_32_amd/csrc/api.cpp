@@ -375,11 +375,17 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
                                   c.gating, idx, gate, s), "top-k");
   LMOE_MARK(2);
   // ---- stage 2: dispatch indices
-  LMOE_TRY(lmoe::launch_route_masks(idx, Ti, N, K, masks, s), "route masks");
-  LMOE_TRY(lmoe::launch_route_scan(masks, p.nblk, N, p.tile_m, counts, offsets, base, tiles, s),
-           "route scan");
-  LMOE_TRY(lmoe::launch_route_assign(idx, masks, base, offsets, Ti, N, K, slot_of, token_of, s),
-           "route assign");
+  if (lmoe::route_small_fits(Ti, N, K)) {
+    LMOE_TRY(lmoe::launch_route_small(idx, Ti, N, K, p.tile_m, counts, offsets, tiles, slot_of,
+                                      token_of, s),
+             "route (single workgroup)");
+  } else {
+    LMOE_TRY(lmoe::launch_route_masks(idx, Ti, N, K, masks, s), "route masks");
+    LMOE_TRY(lmoe::launch_route_scan(masks, p.nblk, N, p.tile_m, counts, offsets, base, tiles, s),
+             "route scan");
+    LMOE_TRY(lmoe::launch_route_assign(idx, masks, base, offsets, Ti, N, K, slot_of, token_of, s),
+             "route assign");
+  }
   LMOE_MARK(3);
   // ---- stage 3: FC1 + squared ReLU, token rows gathered through token_of
   {

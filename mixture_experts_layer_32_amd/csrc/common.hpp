@@ -157,10 +157,58 @@ __device__ __forceinline__ int xcd_contiguous_item(int b, int grid, int total) {
   return item < total ? item : -1;
 }
 
+// ---------------------------------------------------------------- wave reductions
+//
+// DPP (data-parallel primitives) reductions over a full wave of 64 lanes:
+// quad permutations and half-row / row mirrors combine the 16 lanes of each
+// row, then the GFX9 row broadcasts carry row 0 into row 1, row 2 into row 3
+// and lane 31 into rows 2-3, so lane 63 ends with the reduction of all lanes.
+// Every lane must be active.  The result is read back from lane 63.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  // rows outside ROW_MASK keep their own value
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v),
+                                                           CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  v = max(v, dpp_u32<kDppQuadXor2>(v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = max(v, dpp_u32<kDppRowMirror>(v));
+  v = max(v, dpp_u32<kDppRowBcast15, 0xA>(v));
+  v = max(v, dpp_u32<kDppRowBcast31, 0xC>(v));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppQuadXor1>(v));
+  v = min(v, dpp_u32<kDppQuadXor2>(v));
+  v = min(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = min(v, dpp_u32<kDppRowMirror>(v));
+  v = min(v, dpp_u32<kDppRowBcast15, 0xA>(v));
+  v = min(v, dpp_u32<kDppRowBcast31, 0xC>(v));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v +=__uint_as_float(dpp_u32<kDppQuadXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppQuadXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(v)));
+  // row broadcasts add into the receiving rows only; other rows add zero
+  v += __uint_as_float(__builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(v)),
+                                                   kDppRowBcast15, 0xA, 0xF, false));
+  v += __uint_as_float(__builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(v)),
+                                                   kDppRowBcast31, 0xC, 0xF, false));
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(v)), 63)));
 }
 
 }  // namespace lmoe

@@ -59,6 +59,11 @@ template <> struct StreamTraits<float, float> {        // fp32 tokens and weight
 
 constexpr int kStageChunks = 16;  // 16-byte chunks of A per row per K stage (256 bytes)
 
+#ifndef LMOE_W_DEPTH
+#define LMOE_W_DEPTH 1
+#endif
+constexpr int kStreamWDepth = LMOE_W_DEPTH;  // K stages of weights requested ahead
+
 // Per-workgroup context of the streaming kernel.
 template <typename TOut, int NWB>
 struct StreamCtx {
@@ -75,7 +80,7 @@ struct StreamCtx {
 // One pass over up to 16 * NMB rows of a group: stream the group's weight
 // tile through registers once, multiply with the staged token rows.
 template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NMB, int NWB,
-          int ACT, bool SCALE>
+          int WD, int ACT, bool SCALE>
 __device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p0, int rows,
                                             u32x4 (*As)[MB_MAX * 16 * kStageChunks]) {
   using Tr = StreamTraits<TA, TW>;
@@ -108,8 +113,8 @@ __device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p
 #pragma unroll
     for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra0[NMB], ra1[NMB];
-  u32x4 b0[NWB][NLD], b1[NWB][NLD];
+  u32x4 ra[2][NMB];
+  u32x4 bw[WD + 1][NWB][NLD];
 
   // token chunk (row i, column ac) of stage st; past the end of K -> zero
 #define LMOE_LOAD_A(st, ra)                                                                  \
@@ -159,32 +164,33 @@ __device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p
     }                                                                                        \
   } while (0)
 
-  // Stage st is multiplied from register buffer b(st%2) and LDS buffer st%2.
-  // Its weights were requested one stage earlier; its token rows two stages
-  // earlier (into register set ra(st%2)) and written to LDS one stage
-  // earlier, so the token-row latency never sets the stage rate.  Every
+  // Stage st is multiplied from register buffer bw[st % (WD+1)] and LDS
+  // buffer st % 2.  Its weights were requested WD stages earlier; its token
+  // rows two stages earlier (into register set ra[st % 2]) and written to LDS
+  // one stage earlier, so neither latency sets the stage rate.  Every
   // prefetch is unconditional (past the end of K it reads zeros or is never
   // used) and is issued before the multiplies it overlaps.
-  LMOE_LOAD_A(0, ra0);
-  LMOE_LOAD_W(0, b0);
-  LMOE_LOAD_A(1, ra1);
-  LMOE_STORE_A(0, ra0);
+  LMOE_LOAD_A(0, ra[0]);
+#pragma unroll
+  for (int i = 0; i < WD; ++i) LMOE_LOAD_W(i, bw[i]);
+  LMOE_LOAD_A(1, ra[1]);
+  LMOE_STORE_A(0, ra[0]);
   __syncthreads();
-#define LMOE_STEP(st, bcur, bnext, ra_free, ra_next)     \
-  do {                                                   \
-    LMOE_LOAD_W((st) + 1, bnext);                        \
-    LMOE_LOAD_A((st) + 2, ra_free);                      \
-    __builtin_amdgcn_sched_barrier(0);                   \
-    LMOE_COMPUTE((st) & 1, bcur);                        \
-    LMOE_STORE_A(((st) + 1) & 1, ra_next);               \
-    __syncthreads();                                     \
-  } while (0)
-  for (int st = 0; st < nst; st += 2) {
-    LMOE_STEP(st, b0, b1, ra0, ra1);
-    if (st + 1 >= nst) break;
-    LMOE_STEP(st + 1, b1, b0, ra1, ra0);
+  // period of the register rotation: lcm(2, WD + 1) stages
+  constexpr int P = (WD + 1) % 2 == 0 ? WD + 1 : 2 * (WD + 1);
+  for (int st0 = 0; st0 < nst; st0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int st = st0 + u;
+      if (st >= nst) break;
+      LMOE_LOAD_W(st + WD, bw[(u + WD) % (WD + 1)]);
+      LMOE_LOAD_A(st + 2, ra[u % 2]);
+      __builtin_amdgcn_sched_barrier(0);
+      LMOE_COMPUTE(u % 2, bw[u % (WD + 1)]);
+      LMOE_STORE_A((u + 1) % 2, ra[(u + 1) % 2]);
+      __syncthreads();
+    }
   }
-#undef LMOE_STEP
 #undef LMOE_LOAD_A
 #undef LMOE_STORE_A
 #undef LMOE_LOAD_W
@@ -230,7 +236,10 @@ __device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p
 // so that each XCD receives one contiguous range of them.
 template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NWB, int ACT,
           bool SCALE>
-__global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? 2 : 1) void gemm_stream_kernel(GemmArgs p) {
+#ifndef LMOE_STREAM_OCC
+#define LMOE_STREAM_OCC 2
+#endif
+__global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? LMOE_STREAM_OCC : 1) void gemm_stream_kernel(GemmArgs p) {
   constexpr int MROWS = MB_MAX * 16;
   constexpr int NT = 4 * NWB * 16;          // output columns per work item
   __shared__ u32x4 As[2][MROWS * kStageChunks];
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? 2 : 1) void gemm_s
     const int rows = min(MROWS, cnt - p0);
     const int nmb = (rows + 15) >> 4;
 #define LMOE_PASS(n) \
-  stream_pass<Mma, TA, TW, TOut, MB_MAX, n, NWB, ACT, SCALE>(c, p0, rows, As)
+  stream_pass<Mma, TA, TW, TOut, MB_MAX, n, NWB, kStreamWDepth, ACT, SCALE>(c, p0, rows, As)
     if constexpr (MB_MAX == 4) {
       switch (nmb) {
         case 1: LMOE_PASS(1); break;

@@ -56,6 +56,12 @@ hipError_t launch_route_scan(const uint64_t* masks, int nblk, int N, int tile_m,
 hipError_t launch_route_assign(const int32_t* idx, const uint64_t* masks, const int32_t* base,
                                const int32_t* offsets, int T, int N, int K, int32_t* slot_of,
                                int32_t* token_of, hipStream_t s);
+// masks + scan + assign in one launch, when the per-block masks fit
+// in LDS (ceil(T/64) * N small): one launch instead of three.
+bool route_small_fits(int T, int N, int K);
+hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_m, int32_t* counts,
+                              int32_t* offsets, int32_t* tiles, int32_t* slot_of,
+                              int32_t* token_of, hipStream_t s);
 hipError_t launch_combine(const void* Y, const int32_t* slot_of, const float* gate, int T, int K,
                           int l, Dt dt, void* v, hipStream_t s);
 

@@ -6,15 +6,19 @@
 // experts and the gate-weighted aggregation sum_{i in T} p'_i E_i(u).
 //
 //  topk_gate     one wave per token: K rounds of a wave-wide arg-max over
-//                (logit desc, expert id asc), then the gate rule.
+//                (logit desc, expert id asc) with DPP reductions, then the
+//                gate rule.
 //  route_masks   per block of 64 tokens, one 64-bit mask per expert of the
 //                tokens that chose it (LDS 64-bit atomic OR; integer, exact).
 //  route_scan    one workgroup: expert counts = popcounts, exclusive prefix
-//                sum over experts (offsets), and the first row of each
-//                (block, expert) in the expert-grouped order.
-//  route_assign  one thread per copy (t, j): its row is the block base plus
-//                the number of earlier tokens of the block that chose the same
-//                expert, so rows of an expert follow increasing token index.
+//                sum over experts (offsets), and for every (block, expert)
+//                the copies of that expert in earlier blocks.
+//  route_assign  one thread per copy (t, j): its row is the expert's offset
+//                plus the copies of the expert in earlier blocks plus the
+//                earlier tokens of its own block that chose the expert, so
+//                rows of an expert follow increasing token index.
+//  route_small   the three steps above in one launch when all masks fit in
+//                LDS (decode-sized batches).
 //  combine       v[t] = sum_j gate[t][j] * Y[slot_of[t][j]] in fp32, fixed
 //                j order (deterministic), rounded once to the output dtype.
 #include "common.hpp"
@@ -23,24 +27,16 @@
 namespace lmoe {
 namespace {
 
-constexpr int kTopkMaxPerLane = 32;  // N <= 2048
+constexpr int kTopkMaxPerLane = 32;     // N <= 2048
+constexpr int kSmallRouteMasks = 4096;  // route_small: routing blocks x experts
+constexpr int kSmallRouteCopies = 16384; // route_small: token copies T x K
 
-// fp32 -> uint32 whose unsigned order is the float order (+0 == -0).
+// fp32 -> uint32 whose unsigned order is the float order (+0 == -0); zero
+// is never the key of a number, so it marks "no value".
 __device__ __forceinline__ uint32_t order_key(float z) {
   if (z == 0.f) z = 0.f;
   const uint32_t u = __float_as_uint(z);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
-    const uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
 }
 
 template <int NPL>
@@ -51,63 +47,57 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
                                                         float* __restrict__ gate) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (t >= T) return;  // whole waves leave together
   const float* zr = logits + (int64_t)t * N;
 
+  // value i of this lane is expert 64 i + lane; loads are unconditional
+  // (clamped index) so they are all in flight together
   float z[NPL];
   uint32_t key[NPL];
-  uint32_t taken = 0;  // bit i: value i of this lane already selected (or absent)
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = i * 64 + lane;
-    if (e < N) {
-      z[i] = zr[e] + (bias ? bias[e] : 0.f);
-      key[i] = order_key(z[i]);
-    } else {
-      z[i] = -INFINITY;
-      key[i] = 0;
-      taken |= 1u << i;
-    }
+    const int ec = e < N ? e : N - 1;
+    const float v = zr[ec] + (bias ? bias[ec] : 0.f);
+    z[i] = e < N ? v : -INFINITY;
+    key[i] = e < N ? order_key(v) : 0u;
   }
 
+  uint32_t taken = 0;  // bit i: value i already selected
   float my_z = 0.f;
   int my_e = 0;
   for (int j = 0; j < K; ++j) {
-    // lane-local best among untaken values; on equal keys the lower expert id
-    // (the smaller i, since e = 64 i + lane) wins because of the strict >
-    uint64_t best = 0;
-    int bi = -1;
+    // lane-local best untaken value; on equal keys the smaller i (lower id)
+    uint32_t bk = 0;
+    int bi = 0;
+    float bz = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-      const uint64_t kk = (static_cast<uint64_t>(key[i]) << 32) |
-                          (0xffffffffu - static_cast<uint32_t>(i * 64 + lane));
-      if (!((taken >> i) & 1u) && (bi < 0 || kk > best)) { best = kk; bi = i; }
+      const uint32_t kk = ((taken >> i) & 1u) ? 0u : key[i];
+      if (kk > bk) { bk = kk; bi = i; bz = z[i]; }
     }
-    const uint64_t win = wave_max_u64(bi < 0 ? 0ull : best);
-    const int we = static_cast<int>(0xffffffffu - static_cast<uint32_t>(win));
-    if ((we & 63) == lane) {
-      const int wi = we >> 6;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i)
-        if (i == wi) taken |= 1u << i;
+    const uint32_t wk = wave_max_u32(bk);
+    const uint64_t holders = __ballot(bk == wk);
+    int wl;
+    if (__popcll(holders) == 1) {
+      wl = __ffsll(static_cast<unsigned long long>(holders)) - 1;
+    } else {  // equal logits on several lanes: the lowest expert id wins
+      const uint32_t myid = bk == wk ? static_cast<uint32_t>(bi * 64 + lane) : 0xffffffffu;
+      wl = static_cast<int>(wave_min_u32(myid) & 63u);
     }
-    // winner's logit, broadcast from its lane
-    float wz = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (i == (we >> 6)) wz = z[i];
-    wz = __shfl(wz, we & 63, kWave);
+    if (lane == wl) taken |= 1u << bi;
+    const int we = __builtin_amdgcn_readlane(bi * 64 + lane, wl);
+    const float wz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bz), wl));
     if (lane == j) { my_z = wz; my_e = we; }
   }
 
   // ---- gates (rule from the layer configuration)
   const bool mine = lane < K;
-  const float zmax = __shfl(my_z, 0, kWave);  // first selected = largest logit
-  float g = 0.f;
+  const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), 0));
+  float g;
   if (gating == 2) {  // sigmoid, normalised over the selected set
     const float sgm = mine ? 1.f / (1.f + expf(-my_z)) : 0.f;
-    const float tot = wave_sum(sgm);
-    g = sgm / tot;
+    g = sgm / wave_sum(sgm);
   } else {
     const float ex = mine ? expf(my_z - zmax) : 0.f;
     float tot;
@@ -147,9 +137,46 @@ __global__ __launch_bounds__(256) void route_masks_kernel(const int32_t* __restr
   for (int e = threadIdx.x; e < N; e += blockDim.x) masks[(int64_t)blk * N + e] = sm[e];
 }
 
-// One workgroup of 1024 threads; N <= 2048 (two experts per thread).
-// base[b][e] = copies of expert e in routing blocks before b (relative to the
-// expert's first row); offsets[e] = rows of all experts before e.
+// Exclusive scans over up to 2048 experts of the counts and of their tile
+// counts, by a workgroup of 1024 threads: thread t holds the values of
+// experts t and t + 1024 in cnt[0..1].  Results in s_cnt / s_til (exclusive
+// prefix per expert) and the totals.
+__device__ void expert_scan(const int (&cnt)[2], int N, int tile_m, int* s_cnt, int* s_til,
+                            int (*s_wsum)[16], int& total_c, int& total_t) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = tid + h * 1024;
+    s_cnt[e] = e < N ? cnt[h] : 0;
+    s_til[e] = e < N ? (cnt[h] + tile_m - 1) / tile_m : 0;
+  }
+  __syncthreads();
+  // thread tid owns experts 2*tid and 2*tid+1 of the scan's linear order
+  const int a0 = s_cnt[2 * tid], a1 = s_cnt[2 * tid + 1];
+  const int t0 = s_til[2 * tid], t1 = s_til[2 * tid + 1];
+  int pc = a0 + a1, pt = t0 + t1;
+  const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {  // inclusive scan within the wave
+    const int yc = __shfl_up(pc, o, kWave), yt = __shfl_up(pt, o, kWave);
+    if (lane >= o) { pc += yc; pt += yt; }
+  }
+  if (lane == 63) { s_wsum[0][w] = pc; s_wsum[1][w] = pt; }
+  __syncthreads();
+  int wc = 0, wt = 0;
+  for (int i = 0; i < w; ++i) { wc += s_wsum[0][i]; wt += s_wsum[1][i]; }
+  const int exc = wc + pc - (a0 + a1), ext = wt + pt - (t0 + t1);
+  s_cnt[2 * tid] = exc;  // every read of s_cnt/s_til happened before the last barrier
+  s_cnt[2 * tid + 1] = exc + a0;
+  s_til[2 * tid] = ext;
+  s_til[2 * tid + 1] = ext + t0;
+  total_c = 0;
+  total_t = 0;
+  for (int i = 0; i < 16; ++i) { total_c += s_wsum[0][i]; total_t += s_wsum[1][i]; }
+  __syncthreads();
+}
+
+// One workgroup of 1024 threads; N <= 2048.
 __global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __restrict__ masks,
                                                           int nblk, int N, int tile_m,
                                                           int32_t* __restrict__ counts,
@@ -184,34 +211,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __rest
       cnt[h] = run;
     }
   }
-  // exclusive scan over experts of counts and of m-tiles; thread tid owns
-  // experts 2*tid and 2*tid+1 of the scan's linear order
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = tid + h * 1024;
-    s_cnt[e] = e < N ? cnt[h] : 0;
-    s_til[e] = e < N ? (cnt[h] + tile_m - 1) / tile_m : 0;
-  }
-  __syncthreads();
-  const int a0 = s_cnt[2 * tid], a1 = s_cnt[2 * tid + 1];
-  const int t0 = s_til[2 * tid], t1 = s_til[2 * tid + 1];
-  int pc = a0 + a1, pt = t0 + t1;
-  const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {  // inclusive scan within the wave
-    const int yc = __shfl_up(pc, o, kWave), yt = __shfl_up(pt, o, kWave);
-    if (lane >= o) { pc += yc; pt += yt; }
-  }
-  if (lane == 63) { s_wsum[0][w] = pc; s_wsum[1][w] = pt; }
-  __syncthreads();
-  int wc = 0, wt = 0;
-  for (int i = 0; i < w; ++i) { wc += s_wsum[0][i]; wt += s_wsum[1][i]; }
-  const int exc = wc + pc - (a0 + a1), ext = wt + pt - (t0 + t1);
-  s_cnt[2 * tid] = exc;  // every read of s_cnt/s_til happened before the last barrier
-  s_cnt[2 * tid + 1] = exc + a0;
-  s_til[2 * tid] = ext;
-  s_til[2 * tid + 1] = ext + t0;
-  __syncthreads();
+  int total_c, total_t;
+  expert_scan(cnt, N, tile_m, s_cnt, s_til, s_wsum, total_c, total_t);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int e = tid + h * 1024;
@@ -222,8 +223,6 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __rest
     }
   }
   if (tid == 0) {
-    int total_c = 0, total_t = 0;
-    for (int i = 0; i < 16; ++i) { total_c += s_wsum[0][i]; total_t += s_wsum[1][i]; }
     offsets[N] = total_c;
     if (tiles) tiles[N] = total_t;
   }
@@ -247,13 +246,101 @@ __global__ __launch_bounds__(256) void route_assign_kernel(const int32_t* __rest
   token_of[slot] = t;
 }
 
-// One workgroup per token; thread c handles 16 bytes of the output row.
+// masks + scan + assign for a decode-sized batch in one launch of
+// ceil(T*K / 1024) workgroups of 1024 threads; requires
+// ceil(T / 64) * N <= kSmallRouteMasks (the masks live in LDS) and
+// T * K <= kSmallRouteCopies (16 copies per thread, held in registers).
+// Every workgroup builds all masks and the expert scan itself (a few
+// microseconds of LDS work on 64 KB of indices read from L2); workgroup b
+// then assigns the copies q in [1024 b, 1024 b + 1024), so the scattered
+// token_of stores are spread over several compute units.
+__global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __restrict__ idx, int T,
+                                                           int N, int K, int tile_m,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ tiles,
+                                                           int32_t* __restrict__ slot_of,
+                                                           int32_t* __restrict__ token_of) {
+  __shared__ unsigned long long sm[kSmallRouteMasks];
+  __shared__ int s_cnt[2048];
+  __shared__ int s_til[2048];
+  __shared__ int s_wsum[2][16];
+  __shared__ uint16_t s_pre[kSmallRouteMasks];
+  const int tid = threadIdx.x;
+  const int nblk = (T + kRouteBlock - 1) / kRouteBlock;
+  const int nm = nblk * N;
+  const int ncopy = T * K;
+  // the copy this thread assigns, and every copy q = tid + 1024 i for the
+  // masks, all requested in one batch
+  const int my_q = blockIdx.x * 1024 + tid;
+  const int my_e = idx[my_q < ncopy ? my_q : 0];
+  int ids[kSmallRouteCopies / 1024];
+#pragma unroll
+  for (int i = 0; i < kSmallRouteCopies / 1024; ++i) {
+    const int q = tid + 1024 * i;
+    ids[i] = idx[q < ncopy ? q : 0];
+  }
+  for (int i = tid; i < nm; i += 1024) sm[i] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSmallRouteCopies / 1024; ++i) {
+    const int q = tid + 1024 * i;
+    if (q < ncopy) {
+      const int t = q / K;
+      atomicOr(&sm[(t / kRouteBlock) * N + ids[i]], 1ull << (t % kRouteBlock));
+    }
+  }
+  __syncthreads();
+  // per expert: its copies in earlier blocks (s_pre, < T <= 16384 so 16 bits
+  // suffice) and its total count
+  int cnt[2] = {0, 0};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = tid + h * 1024;
+    if (e < N)
+      for (int b = 0; b < nblk; ++b) {
+        s_pre[b * N + e] = static_cast<uint16_t>(cnt[h]);
+        cnt[h] += __popcll(sm[b * N + e]);
+      }
+  }
+  int total_c, total_t;
+  expert_scan(cnt, N, tile_m, s_cnt, s_til, s_wsum, total_c, total_t);
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + h * 1024;
+      if (e < N) {
+        counts[e] = cnt[h];
+        offsets[e] = s_cnt[e];
+        if (tiles) tiles[e] = s_til[e];
+      }
+    }
+    if (tid == 0) {
+      offsets[N] = total_c;
+      if (tiles) tiles[N] = total_t;
+    }
+  }
+  // s_cnt holds the exclusive offsets and is no longer written
+  if (my_q < ncopy) {
+    const int t = my_q / K;
+    const int blk = t / kRouteBlock, tl = t % kRouteBlock;
+    const int slot = s_cnt[my_e] + s_pre[blk * N + my_e] +
+                     __popcll(sm[blk * N + my_e] & ((1ull << tl) - 1ull));
+    slot_of[my_q] = slot;
+    token_of[slot] = t;
+  }
+}
+
+// One workgroup per token; thread c handles 16 bytes of the output row.  The
+// K expert rows are fetched 32 at a time (independent loads in flight)
+// and added in j order.
 template <typename T>
 __global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gate, int K, int l,
                                                       T* __restrict__ v) {
   constexpr int EPC = 16 / sizeof(T);
+  constexpr int U = 32;
   const int t = blockIdx.x;
   const int32_t* so = slot_of + (int64_t)t * K;
   const float* gt = gate + (int64_t)t * K;
@@ -261,38 +348,51 @@ __global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ Y,
     float acc[EPC];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
-    for (int j = 0; j < K; ++j) {
-      const float gj = gt[j];
-      const uint4 y = *reinterpret_cast<const uint4*>(Y + (int64_t)so[j] * l + c * EPC);
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+    for (int j0 = 0; j0 < K; j0 += U) {
+      // straight-line: rows past K re-read row K-1 and are weighted by zero
+      u32x4 y[U];
+      float gw[U];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += gj * __uint_as_float(w[i] << 16);
-          acc[2 * i + 1] += gj * __uint_as_float(w[i] & 0xffff0000u);
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u, K - 1);
+        y[u] = load_chunk(Y + (int64_t)so[j] * l + c * EPC);
+        gw[u] = j0 + u < K ? gt[j] : 0.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float gj = gw[u];
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += gj * __uint_as_float(y[u][i] << 16);
+            acc[2 * i + 1] += gj * __uint_as_float(y[u][i] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += gj * __uint_as_float(y[u][i]);
         }
-      } else {
-        acc[0] += gj * __uint_as_float(y.x);
-        acc[1] += gj * __uint_as_float(y.y);
-        acc[2] += gj * __uint_as_float(y.z);
-        acc[3] += gj * __uint_as_float(y.w);
       }
     }
-    uint4 o;
+    u32x4 o;
     if constexpr (sizeof(T) == 2) {
-      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
     } else {
-      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                     __float_as_uint(acc[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
     }
-    *reinterpret_cast<uint4*>(v + (int64_t)t * l + c * EPC) = o;
+    *reinterpret_cast<u32x4*>(v + (int64_t)t * l + c * EPC) = o;
   }
 }
 
 }  // namespace
+
+bool route_small_fits(int T, int N, int K) {
+  return N <= 2048 && (int64_t)((T + kRouteBlock - 1) / kRouteBlock) * N <= kSmallRouteMasks &&
+         (int64_t)T * K <= kSmallRouteCopies;
+}
 
 hipError_t launch_topk_gate(const float* logits, const float* bias, int T, int N, int K,
                             int gating, int32_t* idx, float* gate, hipStream_t s) {
@@ -333,6 +433,17 @@ hipError_t launch_route_assign(const int32_t* idx, const uint64_t* masks, const 
   if (n <= 0) return hipSuccess;
   route_assign_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(idx, masks, base, offsets, T, N, K,
                                                                   slot_of, token_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_m, int32_t* counts,
+                              int32_t* offsets, int32_t* tiles, int32_t* slot_of,
+                              int32_t* token_of, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!route_small_fits(T, N, K) || tile_m <= 0) return hipErrorInvalidValue;
+  const int grid = (T * K + 1023) / 1024;
+  route_small_kernel<<<dim3(grid), dim3(1024), 0, s>>>(idx, T, N, K, tile_m, counts, offsets,
+                                                       tiles, slot_of, token_of);
   return hipGetLastError();
 }
 
