@@ -52,6 +52,30 @@ def expert_kernel_work(spec, T, counts, stage):
     return float(b), 2.0 * T * K * l * m
 
 
+def layer_work(spec, T, counts):
+    """Algorithmic bytes and FLOPs of one whole layer call: weights of the
+    experts that received tokens, projections and router read once, x read
+    once, out written once (permuted copies, H, Y and logits are
+    intermediates a fused implementation keeps on chip, so they are not
+    counted); FLOPs 2*T*d*l per projection, 2*T*r_in*N for the router and
+    4*T*K*l*m for the experts."""
+    d, l, m, N, K = spec.d, spec.l, spec.m, spec.n_experts, spec.top_k
+    a, eb = spec.act_bytes, spec.expert_bytes
+    r_in = l if spec.router_on_latent else d
+    touched = int((counts > 0).sum())
+    per_expert = 2.0 * l * m * eb
+    if spec.expert_dtype == "fp8_e4m3_rowscale":
+        per_expert += 4.0 * (m + l)
+    nbytes = touched * per_expert + N * r_in * a + 2.0 * T * d * a
+    if spec.has_router_bias:
+        nbytes += 4.0 * N
+    flops = 2.0 * T * r_in * N + 4.0 * T * K * l * m
+    if spec.has_projections:
+        nbytes += 2.0 * l * d * a
+        flops += 4.0 * T * d * l
+    return nbytes, flops
+
+
 def cpu_baseline(spec, w_np, x_np, budget_s=15.0):
     """The fp64 oracle on the first n tokens of the batch, n sized so that the
     run takes about budget_s seconds on this host's cores."""
@@ -75,7 +99,7 @@ def cpu_baseline(spec, w_np, x_np, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="latent_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -149,6 +173,19 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log("bench: %.3f ms/step" % ms)
 
+    # per-step latency distribution: one event pair around every step
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    lat = np.sort(np.array([a.elapsed_time(b) for a, b in evs]))
+    pct = {"p50": float(np.percentile(lat, 50)), "p95": float(np.percentile(lat, 95)),
+           "p99": float(np.percentile(lat, 99)), "mean": float(lat.mean())}
+    log("bench: latency ms " + " ".join("%s=%.4f" % kv for kv in pct.items()))
+
     # per-stage durations from HIP events recorded by the library on the launch stream
     timer = pkg.StageTimer()
     n_done, stage_ms = 0, {k: 0.0 for k in pkg.STAGE_NAMES}
@@ -168,21 +205,35 @@ def main():
     nbytes, nflops = expert_kernel_work(spec, T, counts, dom)
     t_dom = stage_avg[dom] * 1e-3
     if wl.regime == "prefill":
-        dt_peak = "fp8" if spec.expert_dtype == "fp8_e4m3_rowscale" else spec.act_dtype
+        # the expert contraction runs on bf16 MFMA (fp8 weights are widened
+        # to bf16 in registers), f32 MFMA for fp32 layers
         achieved = nflops / t_dom / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2),
-                "peak": MFMA_PEAK_TFLOPS["bf16" if dt_peak != "f32" else "f32"],
+                "peak": MFMA_PEAK_TFLOPS["f32" if spec.act_dtype == "f32" else "bf16"],
                 "unit": "TFLOP/s"}
     else:
         achieved = nbytes / t_dom / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    # measured HBM bytes per launch of this kernel (rocprofv3 FETCH_SIZE and
+    # WRITE_SIZE, copy-calibrated), only while the kernel sources are the
+    # ones the counters were taken on
+    from mixture_experts_layer_32_amd import profiling
+    hbm = profiling.read_hbm(wl.name, dom)
+    roof["traffic"] = round(hbm) if hbm is not None else None
     roof["kernel"] = "expert GEMM %s (%s kernel)" % (dom.upper(), layer.expert_regime(T))
     roof["algorithmic_bytes_per_launch"] = nbytes
     roof["algorithmic_flops_per_launch"] = nflops
     roof["launch_ms"] = round(stage_avg[dom], 5)
+
+    # the whole step against both ceilings
+    lb, lf = layer_work(spec, T, counts)
+    mfma_peak = MFMA_PEAK_TFLOPS["f32" if spec.act_dtype == "f32" else "bf16"]
+    layer_roof = {"algorithmic_bytes": lb, "algorithmic_flops": lf,
+                  "hbm_frac": round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                  "mfma_frac": round(lf / (ms * 1e-3) / (mfma_peak * 1e12), 4),
+                  "mfma_peak_tflops": mfma_peak}
 
     res = {
         "metric": "MoE-layer tokens/s @1 GPU",
@@ -202,7 +253,9 @@ def main():
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "gating": spec.gating,
                    "expert_dtype": spec.expert_dtype, "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
+        "latency_ms": {k: round(v, 5) for k, v in pct.items()},
         "roofline": roof,
+        "layer_roofline": layer_roof,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 CPU oracle")

@@ -21,10 +21,13 @@
 // Experts with more rows than one pass holds are processed in several passes
 // (the weights are then streamed once per pass).
 //
-// Out-of-range buffer offsets read as zero: padding token rows and token
-// chunks past the end of K use that, so no select on loaded data delays a
-// wait.  Weight chunks past the end of K (only when K is not a multiple of
-// the stage) read neighbouring weights or zero; they meet zero token values.
+// Out-of-range buffer offsets read as zero without a memory request: padding
+// token rows, token chunks past the end of K and the weight prefetch past the
+// last stage use that, so no select on loaded data delays a wait.  Weight
+// chunks past the end of K inside the last stage (K not a multiple of the
+// stage) read the next weight row or zero; they meet zero token values.
+// Every weight offset is carried in the per-lane offset, which is what the
+// range check applies to.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -59,10 +62,17 @@ template <> struct StreamTraits<float, float> {        // fp32 tokens and weight
 
 constexpr int kStageChunks = 16;  // 16-byte chunks of A per row per K stage (256 bytes)
 
+// K stages of weights requested ahead.  An fp8 stage is half the bytes of a
+// bf16 one and its registers a quarter (one n-block), so fp8 looks further
+// ahead to keep as many weight bytes in flight.
 #ifndef LMOE_W_DEPTH
 #define LMOE_W_DEPTH 1
 #endif
-constexpr int kStreamWDepth = LMOE_W_DEPTH;  // K stages of weights requested ahead
+#ifndef LMOE_W_DEPTH_FP8
+#define LMOE_W_DEPTH_FP8 4
+#endif
+template <typename TW>
+constexpr int stream_w_depth() { return sizeof(TW) == 1 ? LMOE_W_DEPTH_FP8 : LMOE_W_DEPTH; }
 
 // Per-workgroup context of the streaming kernel.
 template <typename TOut, int NWB>
@@ -135,11 +145,12 @@ __device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p
   // inside the stage is a compile-time constant folded into the instruction
 #define LMOE_LOAD_W(st, br)                                                                  \
   do {                                                                                       \
+    const bool live_ = (st) < nst;                                                           \
     const uint32_t so_ = (st) * W_STAGE_BYTES;                                               \
-    _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb)                                       \
-    _Pragma("unroll") for (int j = 0; j < NLD; ++j) {                                        \
-      const uint32_t imm_ = 64u * j;                                                          \
-      br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(c.w_rsrc, c.w_off[nb] + imm_, so_);        \
+    _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb) {                                     \
+      const uint32_t vo_ = live_ ? c.w_off[nb] + so_ : kOutOfRange;                          \
+      _Pragma("unroll") for (int j = 0; j < NLD; ++j)                                        \
+        br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(c.w_rsrc, vo_ + 64u * j, 0u);            \
     }                                                                                        \
   } while (0)
 #define LMOE_COMPUTE(buf, br)                                                                \
@@ -239,7 +250,7 @@ template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int
 #ifndef LMOE_STREAM_OCC
 #define LMOE_STREAM_OCC 2
 #endif
-__global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? LMOE_STREAM_OCC : 1) void gemm_stream_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256, MB_MAX * NWB <= 8 ? LMOE_STREAM_OCC : 1) void gemm_stream_kernel(GemmArgs p) {
   constexpr int MROWS = MB_MAX * 16;
   constexpr int NT = 4 * NWB * 16;          // output columns per work item
   __shared__ u32x4 As[2][MROWS * kStageChunks];
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? LMOE_STREAM_OCC : 
     const int rows = min(MROWS, cnt - p0);
     const int nmb = (rows + 15) >> 4;
 #define LMOE_PASS(n) \
-  stream_pass<Mma, TA, TW, TOut, MB_MAX, n, NWB, kStreamWDepth, ACT, SCALE>(c, p0, rows, As)
+  stream_pass<Mma, TA, TW, TOut, MB_MAX, n, NWB, stream_w_depth<TW>(), ACT, SCALE>(c, p0, rows, As)
     if constexpr (MB_MAX == 4) {
       switch (nmb) {
         case 1: LMOE_PASS(1); break;
@@ -315,13 +326,19 @@ __global__ __launch_bounds__(256, (MB_MAX <= 4 && NWB <= 2) ? LMOE_STREAM_OCC : 
   }
 }
 
+// n-blocks of 16 weight rows per wave: two with up to 64 rows per pass, one
+// with 128 (the accumulators of the larger pass then leave room for two
+// workgroups per compute unit)
 #ifndef LMOE_STREAM_NWB
 #define LMOE_STREAM_NWB 2
+#endif
+#ifndef LMOE_STREAM_NWB_MB8
+#define LMOE_STREAM_NWB_MB8 1
 #endif
 
 template <typename Mma, typename TA, typename TW, typename TOut, int MB>
 hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
-  constexpr int NWB = LMOE_STREAM_NWB;
+  constexpr int NWB = MB >= 8 ? LMOE_STREAM_NWB_MB8 : LMOE_STREAM_NWB;
   constexpr int NT = 4 * NWB * 16;
   const int64_t n_tiles = (a.N + NT - 1) / NT;
   const int64_t total = n_tiles * a.G;

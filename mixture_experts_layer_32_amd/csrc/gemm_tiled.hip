@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs p, int splits,
   do {                                                                                  \
     const int k_ = ((kt0 + (kt)) * BKE) + sc_ * EPC;                                    \
     const bool in_ = (kt) < nk && k_ < k_end;                                           \
-    const uint32_t so_ = static_cast<uint32_t>((kt0 + (kt)) * BKE * sizeof(TA));        \
+    /* the stage offset is wave-uniform: keep it in an SGPR (buffer soffset) */         \
+    const uint32_t so_ = __builtin_amdgcn_readfirstlane(                                \
+        static_cast<uint32_t>((kt0 + (kt)) * BKE * sizeof(TA)));                        \
     _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                     \
       ra[i] = buffer_load_chunk(a_rsrc, in_ ? a_off[i] : kOutOfRange, so_);             \
     _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                     \

@@ -1,0 +1,203 @@
+"""Summaries of rocprofv3 output for the layer's kernels (text, for profiles/).
+
+    python -m mixture_experts_layer_32_amd.profiling --workload latent_decode \
+        --trace gpurun_out/prof_latent_decode --fetch gpurun_out/pmc_fetch_latent_decode \
+        --write gpurun_out/pmc_write_latent_decode --copy-fetch gpurun_out/pmc_copy_fetch \
+        --copy-write gpurun_out/pmc_copy_write --bench-json gpurun_out/prof_latent_decode_bench.json
+
+reads the CSV files of
+
+  rocprofv3 --kernel-trace --stats -o trace --output-format csv -- python3 bench.py ...
+  rocprofv3 --pmc FETCH_SIZE -o fetch --output-format csv -- python3 bench.py ...
+  rocprofv3 --pmc WRITE_SIZE -o write --output-format csv -- python3 bench.py ...
+  rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 bench.py --copy-calibration
+
+and writes profiles/<workload>_kernels_trace.md (per-kernel durations) and
+profiles/gemm_stream_<workload>_hbm.txt (HBM bytes per launch of the expert
+kernels, scaled by what the same counters read for a 1 GiB device copy).
+The HBM file records a hash of the kernel sources; bench.py reports its
+traffic only while the sources still hash the same.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+PROFILES = os.path.join(ROOT, "profiles")
+# sources that decide what the expert kernels read and write
+KERNEL_SOURCES = ("csrc/gemm_stream.hip", "csrc/gemm_tiled.hip", "csrc/common.hpp",
+                  "csrc/kernels.hpp", "csrc/api.cpp")
+COPY_BYTES = 1 << 30  # bench.py --copy-calibration: 1 GiB read + 1 GiB written per launch
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    n = name.replace("void ", "").replace("lmoe::(anonymous namespace)::", "")
+    return n.replace("lmoe::", "").replace("unsigned short", "bf16").replace("unsigned char", "u8")
+
+
+def expert_stage(name: str) -> str | None:
+    """gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, ACT, SCALE>: ACT 1 = FC1."""
+    if "gemm_stream_kernel<" not in name:
+        return None
+    args = [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")]
+    return "fc1" if args[-2] == "1" else "fc2"
+
+
+def _one(path_dir: str, suffix: str) -> str:
+    got = sorted(glob.glob(os.path.join(path_dir, "*" + suffix)))
+    if not got:
+        raise FileNotFoundError("no *%s under %s" % (suffix, path_dir))
+    return got[0]
+
+
+def kernel_stats(trace_dir: str):
+    rows = []
+    with open(_one(trace_dir, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": r["Name"], "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    return rows
+
+
+def counter_per_dispatch(pmc_dir: str, counter: str):
+    """kernel name -> (mean counter value per dispatch in KiB, dispatches)."""
+    acc = defaultdict(list)
+    with open(_one(pmc_dir, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def copy_reading(pmc_dir: str, counter: str) -> float:
+    """The counter's per-dispatch reading (KiB) for the 1 GiB copy kernel."""
+    per = counter_per_dispatch(pmc_dir, counter)
+    copies = [v for k, (v, _) in per.items() if "copyBuffer" in k]
+    if not copies:
+        raise RuntimeError("no copy kernel in %s" % pmc_dir)
+    return max(copies)
+
+
+def write_trace_md(workload: str, trace_dir: str, bench_json: str | None, out: str):
+    rows = kernel_stats(trace_dir)
+    lines = ["# Kernel durations, workload %s" % workload, "",
+             "Command (from a scratch directory, TMPDIR=/tmp):", "",
+             "    rocprofv3 --kernel-trace --stats -d <dir> -o trace --output-format csv -- "
+             "python3 bench.py --workload %s --steps 10 --warmup 3 --no-cpu-baseline" % workload,
+             "", "rocprofv3 kernel_stats (durations in microseconds, all calls of the run):", "",
+             "| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.1f |" % (
+            short_name(r["name"])[:150], r["calls"], r["avg_us"], r["min_us"], r["max_us"], r["pct"]))
+    if bench_json and os.path.exists(bench_json):
+        with open(bench_json) as f:
+            b = json.loads(f.read().strip().splitlines()[-1])
+        lines += ["", "bench.py line of the same profiled run (HIP events per stage, ms):", "",
+                  "    ms_per_step %s" % b["ms_per_step"],
+                  "    " + " ".join("%s=%s" % kv for kv in b["stage_ms"].items())]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cwrite: str,
+                  trace_dir: str | None, out: str):
+    # factor: true KiB per counted KiB, from the copy's known 1 GiB each way
+    cf, cw = copy_reading(cfetch, "FETCH_SIZE"), copy_reading(cwrite, "WRITE_SIZE")
+    ff, fw = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
+    fetch = counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = counter_per_dispatch(write_dir, "WRITE_SIZE")
+    avg = {}
+    if trace_dir:
+        avg = {r["name"]: r["avg_us"] for r in kernel_stats(trace_dir)}
+    lines = ["# HBM traffic of the expert GEMM kernels, workload %s" % workload,
+             "# commands (from a scratch directory, TMPDIR=/tmp):",
+             "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- "
+             "python3 bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline" % workload,
+             "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- "
+             "python3 bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline" % workload,
+             "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o cf --output-format csv -- "
+             "python3 bench.py --copy-calibration",
+             "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o cw --output-format csv -- "
+             "python3 bench.py --copy-calibration",
+             "# a 1 GiB device copy (1048576 KiB each way) reads FETCH_SIZE %.1f and WRITE_SIZE"
+             " %.1f KiB per dispatch: scale factors %.4f and %.4f" % (cf, cw, ff, fw),
+             "workload=%s" % workload,
+             "sources_sha256=%s" % sources_hash(),
+             "fetch_scale=%.6f" % ff,
+             "write_scale=%.6f" % fw]
+    for name, (fv, n) in sorted(fetch.items()):
+        st = expert_stage(name)
+        if not st:
+            continue
+        wv = write.get(name, (0.0, 0))[0]
+        rd, wr = fv * ff * 1024.0, wv * fw * 1024.0
+        lines.append("%s_kernel=%s" % (st, short_name(name)))
+        lines.append("%s_fetch_kib_per_dispatch=%.1f" % (st, fv))
+        lines.append("%s_write_kib_per_dispatch=%.1f" % (st, wv))
+        lines.append("%s_dispatches=%d" % (st, n))
+        lines.append("%s_hbm_read_bytes=%.0f" % (st, rd))
+        lines.append("%s_hbm_write_bytes=%.0f" % (st, wr))
+        lines.append("%s_hbm_bytes=%.0f" % (st, rd + wr))
+        if name in avg:
+            lines.append("%s_avg_us=%.2f" % (st, avg[name]))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def read_hbm(workload: str, stage: str):
+    """HBM bytes per launch of the FC1/FC2 kernel from the committed summary,
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(PROFILES, "gemm_stream_%s_hbm.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k] = v
+    if kv.get("sources_sha256") != sources_hash():
+        return None
+    v = kv.get("%s_hbm_bytes" % stage)
+    return float(v) if v is not None else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--bench-json")
+    a = ap.parse_args()
+    os.makedirs(PROFILES, exist_ok=True)
+    if a.trace:
+        out = os.path.join(PROFILES, "%s_kernels_trace.md" % a.workload)
+        write_trace_md(a.workload, a.trace, a.bench_json, out)
+        print(out)
+    if a.fetch and a.write and a.copy_fetch and a.copy_write:
+        out = os.path.join(PROFILES, "gemm_stream_%s_hbm.txt" % a.workload)
+        write_hbm_txt(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out)
+        print(out)
+
+
+if __name__ == "__main__":
+    main()
