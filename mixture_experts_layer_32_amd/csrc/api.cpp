@@ -68,33 +68,48 @@ lmoe::Dt exp_dt(const lmoe_config& c) {
 }
 size_t act_bytes(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? 4 : 2; }
 
-// Tile config and K split of one dense GEMM (M x N x K): the large tile when
-// it still gives two workgroups per compute unit, else the small one; split K
-// when even the small tiles leave the device under-filled, keeping at least
-// 8 K stages per split.
+// Tile config and K split of one dense GEMM (M x N x K).  Large problems:
+// the 256 x 256 tile (bf16 operands and output) when it still gives one
+// workgroup per compute unit, else 128 x 128 when that gives one (two fit
+// per unit).  Small problems (decode-sized M): 64 x 64 tiles, K split until
+// about two workgroups per compute unit, keeping at least 8 K stages per
+// split.
 struct DensePlan {
   int tile = 1;
   int splits = 1;
 };
 
-DensePlan plan_dense(int64_t M, int64_t N, int64_t K, size_t elem_bytes) {
-  constexpr int64_t kTargetWorkgroups = 512;  // two per compute unit of an MI355X
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K, size_t elem_bytes, bool bf16_out) {
   DensePlan d;
   if (M <= 0 || N <= 0 || K <= 0) return d;
-  const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
-  if (big >= kTargetWorkgroups) {
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (elem_bytes == 2 && bf16_out && t256 >= kComputeUnits) {
+    d.tile = 2;
+    return d;
+  }
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t128 >= kComputeUnits) {
     d.tile = 0;
     return d;
   }
   d.tile = 1;
   const int64_t small = ((M + 63) / 64) * ((N + 63) / 64);
   const int64_t stages = (K * int64_t(elem_bytes) + 127) / 128;
-  int64_t s = (kTargetWorkgroups + small - 1) / small;
+  int64_t s = (2 * kComputeUnits + small - 1) / small;
   s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
   if (N % 4) s = 1;
   d.splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
   return d;
 }
+
+// Tile of the grouped expert GEMMs when experts receive many tokens: 128 rows
+// keeps the padding of each expert's last tile small, 256 columns halve the
+// operand bytes per flop against 128 x 128.
+#ifndef LMOE_EXPERT_TILE
+#define LMOE_EXPERT_TILE 3
+#endif
 
 struct Plan {
   int64_t T = 0, copies = 0;
@@ -116,18 +131,18 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   const double mean = T > 0 ? double(p.copies) / double(c.n_experts) : 0.0;
   p.stream = mean <= kStreamMaxRowsPerExpert || c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
   p.mb_max = mean <= 40.0 ? 4 : 8;
-  p.expert_tile = 0;
+  p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 0;
   p.tile_m = lmoe::tiled_block_m(p.expert_tile);
   const size_t ab = act_bytes(c);
   const int64_t r_in = c.router_input == LMOE_ROUTER_ON_LATENT ? c.l : c.d;
   size_t partial = 0;
   if (c.has_projections) {
-    p.down = plan_dense(T, c.l, c.d, ab);
-    p.up = plan_dense(T, c.d, c.l, ab);
+    p.down = plan_dense(T, c.l, c.d, ab, ab == 2);
+    p.up = plan_dense(T, c.d, c.l, ab, ab == 2);
     partial = std::max(partial, size_t(p.down.splits > 1 ? p.down.splits : 0) * T * c.l * 4);
     partial = std::max(partial, size_t(p.up.splits > 1 ? p.up.splits : 0) * T * c.d * 4);
   }
-  p.router = plan_dense(T, c.n_experts, r_in, ab);
+  p.router = plan_dense(T, c.n_experts, r_in, ab, false);  // fp32 logits
   partial = std::max(partial, size_t(p.router.splits > 1 ? p.router.splits : 0) * T * c.n_experts * 4);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };

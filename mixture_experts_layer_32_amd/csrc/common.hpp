@@ -63,6 +63,25 @@ __device__ __forceinline__ u32x4 buffer_load_chunk(BufRsrc r, uint32_t voff, uin
                                        r, static_cast<int>(voff), static_cast<int>(soff), CPOL));
 }
 
+// One 16-byte chunk per lane straight from global memory into LDS: lane i of
+// the wave writes bytes [16 i, 16 i + 16) after `lds` (a wave-uniform
+// address); an out-of-range offset writes zeros.  The load counts in vmcnt
+// like any vector load, and nothing orders later LDS reads after it except
+// an explicit wait (wait_vmcnt_lgkm0) and, across waves, a barrier.
+__device__ __forceinline__ void buffer_load_chunk_lds(BufRsrc r, u32x4* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds), 16,
+      static_cast<int>(voff), 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt untouched).  gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -98,26 +117,79 @@ __device__ __forceinline__ void fp8_chunk_to_bf16(u32x4 q, u32x4& lo, u32x4& hi)
 }
 
 // ---------------------------------------------------------------- MFMA chunks
+//
+// Each MFMA flavour describes, for the tiled GEMM: its output block (BLK x
+// BLK), how many 16-byte chunks of K one MFMA consumes per row (CPS), which
+// fragment row and which of those chunks a lane supplies, and where
+// accumulator element v of a lane sits in the output block.
 
-// acc += A_chunk x B_chunk over the reduction indices the two chunks carry.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_16x16x32_bf16: acc += A_chunk x B_chunk over the 8 reduction
+// indices of each of the 4 lane groups (lane l: row l % 16, group l / 16).
 struct MmaBf16 {
   static constexpr int kElemBytes = 2;
+  static constexpr int BLK = 16, CPS = 4, NV = 4;
+  typedef f32x4_t Acc;
   __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4& a, const u32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   }
+  __device__ __forceinline__ static int frag_row(int lane) { return lane & 15; }
+  __device__ __forceinline__ static int frag_chunk(int lane) { return lane >> 4; }
+  __device__ __forceinline__ static int out_row(int lane, int v) { return 4 * (lane >> 4) + v; }
+  __device__ __forceinline__ static int out_col(int lane) { return lane & 15; }
+  // operands swapped (B fragment first): the block is computed transposed,
+  // so lane l holds row l % 16, columns 4 (l / 16) + 0..3
+  __device__ __forceinline__ static int t_row(int lane) { return lane & 15; }
+  __device__ __forceinline__ static int t_col(int lane, int) { return 4 * (lane >> 4); }
+};
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 and the 8 reduction
+// indices (one chunk) of half l / 32: two chunks of K per MFMA.
+// Result: lane l, element v holds C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+// A 32x32 block is twice the work per operand byte of a 16x16 one, and
+// issues back to back with only a few independent accumulators.
+struct MmaBf16x32 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int BLK = 32, CPS = 2, NV = 16;
+  typedef f32x16_t Acc;
+  __device__ __forceinline__ static void mma(f32x16_t& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static int frag_row(int lane) { return lane & 31; }
+  __device__ __forceinline__ static int frag_chunk(int lane) { return lane >> 5; }
+  __device__ __forceinline__ static int out_row(int lane, int v) {
+    return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+  }
+  __device__ __forceinline__ static int out_col(int lane) { return lane & 31; }
+  // operands swapped: lane l holds row l % 32, columns 8 g + 4 (l / 32) + 0..3
+  // in elements 4 g .. 4 g + 3
+  __device__ __forceinline__ static int t_row(int lane) { return lane & 31; }
+  __device__ __forceinline__ static int t_col(int lane, int g) { return 8 * g + 4 * (lane >> 5); }
 };
 
 // fp32: a chunk is 4 values; element s of every group's chunk feeds one
 // v_mfma_f32_16x16x4_f32 (group g supplies reduction index g of that MFMA).
 struct MmaF32 {
   static constexpr int kElemBytes = 4;
+  static constexpr int BLK = 16, CPS = 4, NV = 4;
+  typedef f32x4_t Acc;
   __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4& a, const u32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
   }
+  __device__ __forceinline__ static int frag_row(int lane) { return lane & 15; }
+  __device__ __forceinline__ static int frag_chunk(int lane) { return lane >> 4; }
+  __device__ __forceinline__ static int out_row(int lane, int v) { return 4 * (lane >> 4) + v; }
+  __device__ __forceinline__ static int out_col(int lane) { return lane & 15; }
+  // operands swapped (B fragment first): the block is computed transposed,
+  // so lane l holds row l % 16, columns 4 (l / 16) + 0..3
+  __device__ __forceinline__ static int t_row(int lane) { return lane & 15; }
+  __device__ __forceinline__ static int t_col(int lane, int) { return 4 * (lane >> 4); }
 };
 
 // ---------------------------------------------------------------- epilogue

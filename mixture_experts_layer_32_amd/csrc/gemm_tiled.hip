@@ -6,38 +6,123 @@
 // the router logits (fp32 output) and, when experts receive many tokens, the
 // grouped latent expert GEMMs (FC1 gathers token rows through token_of).
 //
-// Block tile BM x BN, 256 threads = 4 waves in a 2 x 2 arrangement, each wave
-// computing (BM/2) x (BN/2) with 16x16 MFMA blocks.  K advances in stages of
-// 128 bytes per row.  Operands are read with raw buffer loads (32-bit
-// offsets, out-of-range offsets read zero) into registers two stages ahead
-// and written to one of two LDS buffers one stage ahead, so one barrier per
-// stage separates the buffer being read from the one being filled.  LDS rows
-// are 8 chunks of 16 bytes; chunk c of row r is stored at position c ^ (r & 7)
-// so the 16 lanes reading one fragment column and the 8 lanes writing one
-// row hit distinct banks.  The output tile leaves through LDS as 16-byte row
-// chunks.
+// Block tile BM x BN computed by WGM x WGN waves, each wave a (BM / WGM) x
+// (BN / WGN) sub-tile of 16x16 or 32x32 MFMA blocks; a larger wave sub-tile
+// reuses every LDS fragment for more MFMAs, and a larger block tile needs
+// fewer operand bytes per flop (the main loop is bound by how many bytes
+// are in flight against the latency of the loads).
+// K advances in stages of BKC 16-byte chunks per row.
+//
+// Operands move from global memory straight into an LDS ring of NSTAGE
+// stage buffers with buffer loads in LDS mode (no register staging): while
+// stage kt is multiplied, stages kt+1 .. kt+NSTAGE-1 are in flight.  Every
+// thread issues the same number of loads per stage (out-of-range offsets
+// write zeros without touching memory: padding rows, K tails, stages past the
+// end), so "stage kt+1 has landed" is an exact vmcnt wait, followed by one
+// barrier per stage.  MFMA fragments are double-buffered in registers: the
+// fragment reads of the next k-step overlap the MFMAs of the current one,
+// also across the stage barrier.
+//
+// LDS rows hold BKC chunks; logical chunk c of row r sits at position
+// c ^ swz(r) (swz(r) = (r >> 1) & 7 for 8-chunk rows, (r >> 2) & 3 for 4-chunk
+// rows), so the 16 lanes reading one fragment column of 16 consecutive rows
+// touch 16 distinct 16-byte bank groups.  The output tile leaves through LDS
+// (rows padded by 16 bytes against bank conflicts) as 16-byte row chunks.
 //
 // Dense problems with too few tiles to fill the device split K: every split
 // writes an fp32 partial tile and a reduction kernel adds the partials in a
 // fixed order (deterministic), then scales, activates and converts.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace lmoe {
 namespace {
 
-template <typename Mma, typename TA, typename TOut, int BM, int BN, int ACT, bool SCALE>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs p, int splits, float* partial) {
-  constexpr int EPC = 16 / sizeof(TA);   // elements per 16-byte chunk
-  constexpr int BKE = 8 * EPC;           // elements of K per stage (128 bytes)
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int MI = WM / 16, NI = WN / 16;
-  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
-  constexpr int STAGE = (BM + BN) * 8;   // chunks per LDS stage buffer
-  __shared__ u32x4 smem[2 * STAGE];
+template <int BM_, int BN_, int WGM_, int WGN_, int BKC_, int NSTAGE_, int OCC_ = 1>
+struct TileCfg {
+  static constexpr int OCC = OCC_;               // workgroups per compute unit to fit
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WGM = WGM_, WGN = WGN_;  // waves along M and N
+  static constexpr int NW = WGM_ * WGN_;         // waves per workgroup
+  static constexpr int NT = 64 * NW;             // threads per workgroup
+  static constexpr int BKC = BKC_;               // 16-byte chunks per row per stage
+  static constexpr int NSTAGE = NSTAGE_;
+};
+// tile configurations (index = the `tile` argument of launch_gemm_tiled)
+#ifndef LMOE_T0_BKC
+#define LMOE_T0_BKC 8
+#endif
+#ifndef LMOE_T0_STAGES
+#define LMOE_T0_STAGES 2
+#endif
+#ifndef LMOE_T0_OCC
+#define LMOE_T0_OCC 2
+#endif
+#ifndef LMOE_T3_STAGES
+#define LMOE_T3_STAGES 3
+#endif
+#ifndef LMOE_T3_BKC
+#define LMOE_T3_BKC 4
+#endif
+#ifndef LMOE_T3_OCC
+#define LMOE_T3_OCC 2
+#endif
+using Tile128 = TileCfg<128, 128, 2, 2, LMOE_T0_BKC, LMOE_T0_STAGES, LMOE_T0_OCC>;  // 0: 4 waves of 64x64
+using Tile64 = TileCfg<64, 64, 2, 2, 8, 4>;                 // 1: 4 waves of 32x32
+using Tile256 = TileCfg<256, 256, 2, 4, 4, 4>;              // 2: 8 waves of 128x64 (bf16 output only)
+using Tile128x256 = TileCfg<128, 256, 2, 2, LMOE_T3_BKC, LMOE_T3_STAGES, LMOE_T3_OCC>;  // 3: 4 waves of 64x128
+
+template <int BKC>
+__device__ __forceinline__ int lds_swz(int r) {
+  return BKC == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// four consecutive output values to LDS in one store (8 or 16 bytes, aligned)
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut* p, const float (&v)[4]);
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&v)[4]) {
+  uint2 w;
+  w.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+  w.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
+  *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+}
+
+template <typename Mma, typename TA, typename TOut, typename Cfg, int ACT, bool SCALE>
+__global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs p, int splits, float* partial) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BKC = Cfg::BKC, NSTAGE = Cfg::NSTAGE;
+  constexpr int EPC = 16 / sizeof(TA);       // elements per 16-byte chunk
+  constexpr int BKE = BKC * EPC;             // elements of K per stage
+  constexpr int KS = BKC / Mma::CPS;         // MFMA k-steps per stage
+  constexpr int WM = BM / Cfg::WGM, WN = BN / Cfg::WGN;
+  constexpr int BLK = Mma::BLK, NV = Mma::NV;
+  constexpr int MI = WM / BLK, NI = WN / BLK;
+  static_assert(WM % BLK == 0 && WN % BLK == 0, "wave tile must hold whole MFMA blocks");
+  constexpr int STAGE = (BM + BN) * BKC;     // chunks per LDS stage buffer
+  constexpr int NW = Cfg::NW, NT = Cfg::NT;
+  constexpr int NDMA = STAGE / NT;           // LDS-mode loads per thread per stage
+  constexpr int OPAD = 16 / sizeof(TOut);    // output tile row padding (elements)
+  constexpr bool PARTIAL_OK = BM * BN <= 128 * 128;
+  constexpr size_t RING = size_t(NSTAGE) * STAGE * 16;
+  constexpr size_t OUT_T = size_t(BM) * (BN + OPAD) * sizeof(TOut);
+  constexpr size_t OUT_P = PARTIAL_OK ? size_t(BM) * (BN + 4) * 4 : 0;
+  static_assert(STAGE % NT == 0 && (BM * BKC) % 64 == 0, "stage must split into wave loads");
+  static_assert(BKC == 4 || BKC == 8, "stage row = 64 or 128 bytes");
+  __shared__ u32x4 smem[cmax(RING, cmax(OUT_T, OUT_P)) / 16];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index is uniform across the wave: say so, so that values
+  // derived from it (buffer resource choice, LDS bases) live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_tiles = (p.N + BN - 1) / BN;
 
   // ---- which tile (and which K split)
@@ -80,155 +165,201 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs p, int splits,
   const BufRsrc a_rsrc = make_rsrc(A, a_rows_total * p.lda * sizeof(TA));
   const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)p.N * p.ldb * sizeof(TA));
 
-  // ---- per-thread staging coordinates: chunk column sc_ of rows sr + 32 i
-  const int sc_ = tid & 7;
-  const int sr = tid >> 3;
-  uint32_t a_off[ACH], b_off[BCH];
+  // ---- LDS-mode staging.  Stage buffer position q (16-byte chunks) holds
+  // row q / BKC (A rows 0..BM-1, then B rows), logical chunk
+  // (q % BKC) ^ swz(row).  Load j of wave w fills positions
+  // (NW j + w) * 64 + lane, so each lane's row and chunk are fixed; per stage
+  // only the K offset changes.
+  uint32_t d_off[NDMA];  // byte offset in A or B of this lane's chunk at K stage 0
+  int d_k[NDMA];         // its first K element
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int r = sr + 32 * i;
-    int64_t arow = -1;
-    if (r < rows) arow = p.a_rows ? p.a_rows[row0 + r] : row0 + r;
-    a_off[i] = arow >= 0 ? static_cast<uint32_t>(arow * p.lda * sizeof(TA)) + sc_ * 16u : kOutOfRange;
+  for (int j = 0; j < NDMA; ++j) {
+    const int q = (NW * j + wave) * 64 + lane;
+    const int r = q / BKC;
+    const int c = (q % BKC) ^ lds_swz<BKC>(r);
+    d_k[j] = c * EPC;
+    if (r < BM) {
+      int64_t arow = -1;
+      if (r < rows) arow = p.a_rows ? p.a_rows[row0 + r] : row0 + r;
+      d_off[j] = arow >= 0 ? static_cast<uint32_t>(arow * p.lda * sizeof(TA)) + c * 16u : kOutOfRange;
+    } else {
+      const int n = col0 + r - BM;
+      d_off[j] = n < p.N ? static_cast<uint32_t>((int64_t)n * p.ldb * sizeof(TA)) + c * 16u
+                         : kOutOfRange;
+    }
   }
+  // stage kt -> ring buffer kt % NSTAGE, always NDMA loads per thread
+  auto issue_stage = [&](int kt) {
+    u32x4* s_ = smem + (kt % NSTAGE) * STAGE;
+    const int kb = (kt0 + kt) * BKE;
+    const uint32_t kbytes = static_cast<uint32_t>(kb) * sizeof(TA);
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int r = sr + 32 * i;
-    b_off[i] = col0 + r < p.N ? static_cast<uint32_t>((int64_t)(col0 + r) * p.ldb * sizeof(TA)) +
-                                    sc_ * 16u
-                              : kOutOfRange;
-  }
+    for (int j = 0; j < NDMA; ++j) {
+      const bool in_ = kt < nk && kb + d_k[j] < k_end && d_off[j] != kOutOfRange;
+      const bool is_a = (NW * j + wave) * 64 < BM * BKC;  // wave-uniform
+      buffer_load_chunk_lds(is_a ? a_rsrc : b_rsrc, s_ + (NW * j + wave) * 64,
+                            in_ ? d_off[j] + kbytes : kOutOfRange);
+    }
+  };
 
-  u32x4 ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
-#define LMOE_LOAD(kt, ra, rb)                                                           \
-  do {                                                                                  \
-    const int k_ = ((kt0 + (kt)) * BKE) + sc_ * EPC;                                    \
-    const bool in_ = (kt) < nk && k_ < k_end;                                           \
-    /* the stage offset is wave-uniform: keep it in an SGPR (buffer soffset) */         \
-    const uint32_t so_ = __builtin_amdgcn_readfirstlane(                                \
-        static_cast<uint32_t>((kt0 + (kt)) * BKE * sizeof(TA)));                        \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                     \
-      ra[i] = buffer_load_chunk(a_rsrc, in_ ? a_off[i] : kOutOfRange, so_);             \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                     \
-      rb[i] = buffer_load_chunk(b_rsrc, in_ ? b_off[i] : kOutOfRange, so_);             \
-  } while (0)
-#define LMOE_STORE(buf, ra, rb)                                                         \
-  do {                                                                                  \
-    u32x4* s_ = smem + (buf) * STAGE;                                                   \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i) {                                   \
-      const int r_ = sr + 32 * i;                                                       \
-      s_[r_ * 8 + (sc_ ^ (r_ & 7))] = ra[i];                                            \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                   \
-      const int r_ = BM + sr + 32 * i;                                                  \
-      s_[r_ * 8 + (sc_ ^ (r_ & 7))] = rb[i];                                            \
-    }                                                                                   \
-  } while (0)
-
-  f32x4_t acc[MI][NI];
+  typename Mma::Acc acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[i][j][v] = 0.f;
 
-  const int wm = wave >> 1, wn = wave & 1;
-  const int fr = lane & 15, fq = lane >> 4;
-#define LMOE_COMPUTE(buf)                                                               \
+  const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
+  // MFMA operand fragments of one k-step (CPS chunks of K, one MFMA per
+  // block pair): logical chunk CPS ks + frag_chunk(lane) of fragment row
+  // frag_row(lane), for this wave's m-blocks (A) and n-blocks (B)
+  const int frow = Mma::frag_row(lane);
+  const int fchk = Mma::frag_chunk(lane);
+  u32x4 fa[2][MI], fb[2][NI];
+#define LMOE_FRAGS(kt, ks, f)                                                           \
   do {                                                                                  \
-    const u32x4* s_ = smem + (buf) * STAGE;                                             \
-    _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                  \
-      const int c_ = ks * 4 + fq;                                                       \
-      u32x4 af[MI], bfr[NI];                                                            \
-      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                  \
-        const int r_ = wm * WM + i * 16 + fr;                                           \
-        af[i] = s_[r_ * 8 + (c_ ^ (r_ & 7))];                                           \
-      }                                                                                 \
-      _Pragma("unroll") for (int j = 0; j < NI; ++j) {                                  \
-        const int r_ = BM + wn * WN + j * 16 + fr;                                      \
-        bfr[j] = s_[r_ * 8 + (c_ ^ (r_ & 7))];                                          \
-      }                                                                                 \
-      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                    \
-      _Pragma("unroll") for (int j = 0; j < NI; ++j) Mma::mma(acc[i][j], af[i], bfr[j]); \
+    const u32x4* s_ = smem + ((kt) % NSTAGE) * STAGE;                                   \
+    const int c_ = (ks) * Mma::CPS + fchk;                                              \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                    \
+      const int r_ = wm * WM + i * BLK + frow;                                          \
+      fa[f][i] = s_[r_ * BKC + (c_ ^ lds_swz<BKC>(r_))];                                \
+    }                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < NI; ++j) {                                    \
+      const int r_ = BM + wn * WN + j * BLK + frow;                                     \
+      fb[f][j] = s_[r_ * BKC + (c_ ^ lds_swz<BKC>(r_))];                                \
     }                                                                                   \
   } while (0)
+#define LMOE_MMA(f)                                                                     \
+  do {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                      \
+    _Pragma("unroll") for (int j = 0; j < NI; ++j) Mma::mma(acc[i][j], fb[f][j], fa[f][i]); \
+  } while (0)
+  // after each LDS fragment read, a share of the MFMAs already possible
+#define LMOE_INTERLEAVE()                                                               \
+  do {                                                                                  \
+    _Pragma("unroll") for (int q_ = 0; q_ < MI + NI; ++q_) {                            \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x008, (MI * NI + MI + NI - 1) / (MI + NI), 0); \
+    }                                                                                   \
+  } while (0)
+  // Stage kt whose k-step 0 fragments are in register set P: issue the loads
+  // of stage kt+NSTAGE-1 (into the buffer stage kt-1 used, which every wave
+  // finished reading before the previous barrier); run the k-steps, reading
+  // the next k-step's fragments during each; wait until this thread's loads
+  // of stage kt+1 have landed and its fragment reads are done, barrier (then
+  // every thread's stage kt+1 is in LDS); read stage kt+1's k-step 0
+  // fragments during the last k-step's MFMAs.
+#define LMOE_STAGE(kt, P)                                                               \
+  do {                                                                                  \
+    issue_stage((kt) + NSTAGE - 1);                                                     \
+    _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                             \
+      LMOE_FRAGS(kt, ks + 1, ((P) + ks + 1) & 1);                                       \
+      LMOE_MMA(((P) + ks) & 1);                                                         \
+      LMOE_INTERLEAVE();                                                                \
+    }                                                                                   \
+    wait_vmcnt_lgkm0<(NSTAGE - 2) * NDMA>();                                            \
+    __builtin_amdgcn_s_barrier();                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    LMOE_FRAGS((kt) + 1, 0, ((P) + KS) & 1);                                            \
+    LMOE_MMA(((P) + KS - 1) & 1);                                                       \
+    LMOE_INTERLEAVE();                                                                  \
+  } while (0)
 
-  // stage kt: registers set kt%2 -> LDS buffer kt%2 one stage ahead; the loads
-  // of stage kt+2 are issued before the multiplies of stage kt
-  LMOE_LOAD(0, ra0, rb0);
-  LMOE_LOAD(1, ra1, rb1);
-  LMOE_STORE(0, ra0, rb0);
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) issue_stage(s);
+  wait_vmcnt_lgkm0<(NSTAGE - 2) * NDMA>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  LMOE_FRAGS(0, 0, 0);
+  // with an even number of k-steps per stage every stage starts from
+  // register set 0: one stage per iteration, so the accumulators keep their
+  // registers across iterations
+  static_assert(KS % 2 == 0, "stages must hold an even number of MFMA k-steps");
+  for (int kt = 0; kt < nk; ++kt) LMOE_STAGE(kt, 0);
+#undef LMOE_STAGE
+#undef LMOE_INTERLEAVE
+#undef LMOE_MMA
+#undef LMOE_FRAGS
+  // loads of stages past the last one still target the ring: let them land
+  // before the buffers are reused for the output tile
+  wait_vmcnt_lgkm0<0>();
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    LMOE_LOAD(kt + 2, ra0, rb0);
-    __builtin_amdgcn_sched_barrier(0);
-    LMOE_COMPUTE(0);
-    LMOE_STORE(1, ra1, rb1);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    LMOE_LOAD(kt + 3, ra1, rb1);
-    __builtin_amdgcn_sched_barrier(0);
-    LMOE_COMPUTE(1);
-    LMOE_STORE(0, ra0, rb0);
-    __syncthreads();
-  }
-#undef LMOE_LOAD
-#undef LMOE_STORE
-#undef LMOE_COMPUTE
 
   // ---- epilogue through LDS: direct output (scale, act, convert) or fp32 partial
   const float* sc = SCALE ? p.b_scale + (int64_t)g * p.s_gstride : nullptr;
   if (partial == nullptr) {
-    static_assert(BM * BN * sizeof(TOut) <= sizeof(smem), "output tile must fit LDS");
+    constexpr int LDT = BN + OPAD;  // LDS tile row stride (elements)
+    static_assert(OUT_T <= sizeof(smem), "output tile must fit LDS");
     TOut* Ct = reinterpret_cast<TOut*>(smem);
+    // blocks are held transposed (B fragment first in the MFMA): each group of
+    // 4 accumulator elements is 4 consecutive columns of one row, written to
+    // LDS as one 8-byte (bf16) or 16-byte (fp32) store
+    const int trow = Mma::t_row(lane);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int colt = wn * WN + j * 16 + fr;
-      const float s = (SCALE && col0 + colt < p.N) ? sc[col0 + colt] : 1.f;
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int g4 = 0; g4 < NV / 4; ++g4) {
+        const int colt = wn * WN + j * BLK + Mma::t_col(lane, g4);
+        float s4[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float val = acc[i][j][v];
-          if (SCALE) val *= s;
-          store_elem<TOut>(Ct + (wm * WM + i * 16 + fq * 4 + v) * BN + colt, apply_act<ACT>(val));
+        for (int e = 0; e < 4; ++e)
+          s4[e] = (SCALE && col0 + colt + e < p.N) ? sc[col0 + colt + e] : 1.f;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          float val[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            val[e] = acc[i][j][4 * g4 + e];
+            if (SCALE) val[e] *= s4[e];
+            val[e] = apply_act<ACT>(val[e]);
+          }
+          store4<TOut>(Ct + (wm * WM + i * BLK + trow) * LDT + colt, val);
         }
-    }
+      }
     __syncthreads();
-    constexpr int CPR = BN * sizeof(TOut) / 16;
     constexpr int EPO = 16 / sizeof(TOut);
+    constexpr int CPR = BN / EPO;
     TOut* C = static_cast<TOut*>(p.C);
     // whole 16-byte chunks where the row stride keeps them aligned and the
     // chunk lies inside N; element stores otherwise (e.g. N = expert count)
     const bool aligned = (p.ldc % EPO) == 0;
-    for (int q = tid; q < rows * CPR; q += 256) {
+    for (int q = tid; q < rows * CPR; q += NT) {
       const int r = q / CPR, ch = q % CPR;
       const int col = col0 + ch * EPO;
       TOut* dst = C + (int64_t)(row0 + r) * p.ldc + col;
+      const TOut* src = Ct + r * LDT + ch * EPO;
       if (aligned && col + EPO <= p.N) {
-        *reinterpret_cast<u32x4*>(dst) = reinterpret_cast<const u32x4*>(Ct)[q];
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
       } else {
-        for (int e = 0; e < EPO && col + e < p.N; ++e) dst[e] = Ct[r * BN + ch * EPO + e];
+        for (int e = 0; e < EPO && col + e < p.N; ++e) dst[e] = src[e];
       }
     }
-  } else {
-    static_assert(BM * BN * 4 <= sizeof(smem), "partial tile must fit LDS");
+  } else if constexpr (PARTIAL_OK) {
+    constexpr int LDP = BN + 4;
     float* Pt = reinterpret_cast<float*>(smem);
+    const int trow = Mma::t_row(lane);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int g4 = 0; g4 < NV / 4; ++g4)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          Pt[(wm * WM + i * 16 + fq * 4 + v) * BN + wn * WN + j * 16 + fr] = acc[i][j][v];
+        for (int i = 0; i < MI; ++i) {
+          float val[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = acc[i][j][4 * g4 + e];
+          store4<float>(Pt + (wm * WM + i * BLK + trow) * LDP + wn * WN + j * BLK +
+                            Mma::t_col(lane, g4), val);
+        }
     __syncthreads();
     constexpr int CPR = BN / 4;
     float* P = partial + (int64_t)kz * p.M * p.N;
-    for (int q = tid; q < rows * CPR; q += 256) {
+    for (int q = tid; q < rows * CPR; q += NT) {
       const int r = q / CPR, ch = q % CPR;
       const int col = col0 + ch * 4;
       if (col < p.N)
         *reinterpret_cast<u32x4*>(P + (int64_t)(row0 + r) * p.N + col) =
-            reinterpret_cast<const u32x4*>(Pt)[q];
+            *reinterpret_cast<const u32x4*>(Pt + r * LDP + ch * 4);
     }
   }
 }
@@ -254,8 +385,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <typename Mma, typename TA, typename TOut, int BM, int BN>
+template <typename Mma, typename TA, typename TOut, typename Cfg>
 hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN;
   const int n_tiles = (a.N + BN - 1) / BN;
   int64_t m_tiles;
   if (a.g_off == nullptr) m_tiles = (a.M + BM - 1) / BM;
@@ -269,12 +401,13 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s
     return hipErrorInvalidValue;
   const bool scale = a.b_scale != nullptr;
   float* part = splits > 1 ? partial : nullptr;
+  if (part && BM * BN > 128 * 128) return hipErrorInvalidValue;  // partial tile must fit LDS
   if (a.act == kActSqRelu) {
-    if (scale) gemm_tiled_kernel<Mma, TA, TOut, BM, BN, kActSqRelu, true><<<dim3(grid), dim3(256), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TOut, BM, BN, kActSqRelu, false><<<dim3(grid), dim3(256), 0, s>>>(a, splits, part);
+    if (scale) gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    else gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   } else {
-    if (scale) gemm_tiled_kernel<Mma, TA, TOut, BM, BN, kActNone, true><<<dim3(grid), dim3(256), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TOut, BM, BN, kActNone, false><<<dim3(grid), dim3(256), 0, s>>>(a, splits, part);
+    if (scale) gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActNone, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    else gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActNone, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
@@ -291,19 +424,35 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+// fp32 operands only with the small tiles; fp32 output (router logits,
+// partials) with tiles of at most 128 x 256
+template <typename Cfg>
 hipError_t launch_tile(const GemmArgs& a, Dt a_dt, Dt out_dt, int splits, float* partial,
                        hipStream_t s) {
+  // 32x32 MFMA blocks where the wave sub-tile holds at least 2 x 2 of them
+  using MmaB = std::conditional_t<(Cfg::BM / Cfg::WGM >= 64 && Cfg::BN / Cfg::WGN >= 64),
+                                  MmaBf16x32, MmaBf16>;
   if (a_dt == Dt::BF16) {
-    if (out_dt == Dt::BF16) return launch_t<MmaBf16, uint16_t, uint16_t, BM, BN>(a, splits, partial, s);
-    return launch_t<MmaBf16, uint16_t, float, BM, BN>(a, splits, partial, s);
+    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, Cfg>(a, splits, partial, s);
+    if constexpr (Cfg::BM * Cfg::BN <= 128 * 256)
+      return launch_t<MmaB, uint16_t, float, Cfg>(a, splits, partial, s);
+    return hipErrorInvalidValue;
   }
-  return launch_t<MmaF32, float, float, BM, BN>(a, splits, partial, s);
+  if constexpr (Cfg::BM * Cfg::BN <= 128 * 128)
+    return launch_t<MmaF32, float, float, Cfg>(a, splits, partial, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int tiled_block_m(int tile) { return tile == 0 ? 128 : 64; }
+int tiled_block_m(int tile) {
+  switch (tile) {
+    case 0: return Tile128::BM;
+    case 1: return Tile64::BM;
+    case 2: return Tile256::BM;
+    default: return Tile128x256::BM;
+  }
+}
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s,
                              int splits, float* partial) {
@@ -311,8 +460,13 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hi
   if (a_dt == Dt::F32 && out_dt != Dt::F32) return hipErrorInvalidValue;
   if (splits < 1 || (splits > 1 && (a.g_off != nullptr || partial == nullptr || a.N % 4)))
     return hipErrorInvalidValue;
-  if (tile == 0) return launch_tile<128, 128>(a, a_dt, out_dt, splits, partial, s);
-  return launch_tile<64, 64>(a, a_dt, out_dt, splits, partial, s);
+  switch (tile) {
+    case 0: return launch_tile<Tile128>(a, a_dt, out_dt, splits, partial, s);
+    case 1: return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, s);
+    case 2: return launch_tile<Tile256>(a, a_dt, out_dt, splits, partial, s);
+    case 3: return launch_tile<Tile128x256>(a, a_dt, out_dt, splits, partial, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lmoe

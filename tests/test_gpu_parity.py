@@ -130,3 +130,23 @@ def test_full_size_sampled_tokens(name):
     check_routing_structure(spec, g, T)
     st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T))
     print(name, st, flush=True)
+
+
+# Sizes that select the large GEMM tiles (256 x 256 dense, 128 x 256 grouped,
+# 128 x 128 dense) with ragged row and column tails, on sampled tokens.
+MID = {
+    "ragged_large_tiles": (LayerSpec(d=2064, l=1040, m=528, n_experts=64, top_k=4,
+                                     gating="softmax_topk"), 8200),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MID))
+def test_mid_size_large_tiles_sampled_tokens(name):
+    spec, T = MID[name]
+    w, x = _case(spec, T, seed=3)
+    g, layer = run_gpu(spec, w, x)
+    assert layer.expert_regime(T) == "tiled"
+    check_routing_structure(spec, g, T)
+    st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T, n=40, seed=9))
+    print(name, st, flush=True)
+
