@@ -58,6 +58,12 @@ constexpr int64_t kMaxExperts = 2048;
 constexpr int64_t kMaxTopK = 64;
 constexpr int64_t kMaxCopies = int64_t(1) << 30;  // T * K (int32 row indices)
 constexpr double kStreamMaxRowsPerExpert = 96.0;  // mean copies per expert -> streaming kernel
+// fp8 weights: the tiled kernel (one weight tile per expert and 256 columns,
+// token rows staged once per tile) from this many rows per expert on
+#ifndef LMOE_FP8_STREAM_MAX_ROWS
+#define LMOE_FP8_STREAM_MAX_ROWS 40.0
+#endif
+constexpr double kFp8StreamMaxRowsPerExpert = LMOE_FP8_STREAM_MAX_ROWS;
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -129,10 +135,11 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.copies = T * c.top_k;
   p.nblk = static_cast<int>((T + lmoe::kRouteBlock - 1) / lmoe::kRouteBlock);
   const double mean = T > 0 ? double(p.copies) / double(c.n_experts) : 0.0;
-  p.stream = mean <= kStreamMaxRowsPerExpert || c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
+  const bool fp8 = c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
+  p.stream = fp8 ? mean <= kFp8StreamMaxRowsPerExpert : mean <= kStreamMaxRowsPerExpert;
   p.mb_max = mean <= 40.0 ? 4 : 8;
   p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 0;
-  p.tile_m = lmoe::tiled_block_m(p.expert_tile);
+  p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
   const size_t ab = act_bytes(c);
   const int64_t r_in = c.router_input == LMOE_ROUTER_ON_LATENT ? c.l : c.d;
   size_t partial = 0;
@@ -413,6 +420,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);
     a.act = lmoe::kActSqRelu;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
+    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC1 (tiled, fp8)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");
   }
   LMOE_MARK(4);
@@ -427,6 +435,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);
     a.act = lmoe::kActNone;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC2 (stream)");
+    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC2 (tiled, fp8)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");
   }
   LMOE_MARK(5);

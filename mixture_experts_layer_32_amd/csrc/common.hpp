@@ -88,12 +88,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+// fp32 -> bf16, round to nearest even (NaN stays NaN): the gfx950
+// conversion instruction v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> two bf16 in one dword (lo in bits 0..15), one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Four OCP E4M3 bytes -> four bf16 (packed in two dwords).  Every E4M3

@@ -87,8 +87,8 @@ __device__ __forceinline__ void store4(TOut* p, const float (&v)[4]);
 template <>
 __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&v)[4]) {
   uint2 w;
-  w.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-  w.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<uint2*>(p) = w;
 }
 template <>
@@ -96,17 +96,26 @@ __device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
   *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
 }
 
-template <typename Mma, typename TA, typename TOut, typename Cfg, int ACT, bool SCALE>
+// TB: element type of B (TA, or uint8_t for OCP E4M3 weights with one fp32
+// scale per row of B, applied in the epilogue; fp8 fragments are widened to
+// bf16 right after their LDS read).
+template <typename Mma, typename TA, typename TB, typename TOut, typename Cfg, int ACT, bool SCALE>
 __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs p, int splits, float* partial) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BKC = Cfg::BKC, NSTAGE = Cfg::NSTAGE;
-  constexpr int EPC = 16 / sizeof(TA);       // elements per 16-byte chunk
+  constexpr int EPC = 16 / sizeof(TA);       // A elements per 16-byte chunk
   constexpr int BKE = BKC * EPC;             // elements of K per stage
+  constexpr bool FP8B = sizeof(TB) == 1 && sizeof(TA) == 2;
+  constexpr int EPCB = 16 / sizeof(TB);      // B elements per chunk
+  constexpr int BKCB = BKE / EPCB;           // B chunks per row per stage
+  static_assert(sizeof(TB) == sizeof(TA) || FP8B, "B is the A type or fp8 with bf16 A");
+  static_assert(BKCB == 4 || BKCB == 8, "B stage row = 64 or 128 bytes");
   constexpr int KS = BKC / Mma::CPS;         // MFMA k-steps per stage
   constexpr int WM = BM / Cfg::WGM, WN = BN / Cfg::WGN;
   constexpr int BLK = Mma::BLK, NV = Mma::NV;
   constexpr int MI = WM / BLK, NI = WN / BLK;
   static_assert(WM % BLK == 0 && WN % BLK == 0, "wave tile must hold whole MFMA blocks");
-  constexpr int STAGE = (BM + BN) * BKC;     // chunks per LDS stage buffer
+  constexpr int ACH = BM * BKC;              // A chunks per stage (first in the buffer)
+  constexpr int STAGE = ACH + BN * BKCB;     // chunks per LDS stage buffer
   constexpr int NW = Cfg::NW, NT = Cfg::NT;
   constexpr int NDMA = STAGE / NT;           // LDS-mode loads per thread per stage
   constexpr int OPAD = 16 / sizeof(TOut);    // output tile row padding (elements)
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   constexpr size_t RING = size_t(NSTAGE) * STAGE * 16;
   constexpr size_t OUT_T = size_t(BM) * (BN + OPAD) * sizeof(TOut);
   constexpr size_t OUT_P = PARTIAL_OK ? size_t(BM) * (BN + 4) * 4 : 0;
-  static_assert(STAGE % NT == 0 && (BM * BKC) % 64 == 0, "stage must split into wave loads");
+  static_assert(STAGE % NT == 0 && ACH % 64 == 0, "stage must split into wave loads");
   static_assert(BKC == 4 || BKC == 8, "stage row = 64 or 128 bytes");
   __shared__ u32x4 smem[cmax(RING, cmax(OUT_T, OUT_P)) / 16];
 
@@ -160,14 +169,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   const int k_end = min(p.K, (kt0 + nk) * BKE);
 
   const TA* A = static_cast<const TA*>(p.A);
-  const TA* B = static_cast<const TA*>(p.B) + (int64_t)g * p.b_gstride;
+  const TB* B = static_cast<const TB*>(p.B) + (int64_t)g * p.b_gstride;
   const uint64_t a_rows_total = p.g_off ? (uint64_t)p.a_nrows : (uint64_t)p.M;
   const BufRsrc a_rsrc = make_rsrc(A, a_rows_total * p.lda * sizeof(TA));
-  const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)p.N * p.ldb * sizeof(TA));
+  const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)p.N * p.ldb * sizeof(TB));
 
-  // ---- LDS-mode staging.  Stage buffer position q (16-byte chunks) holds
-  // row q / BKC (A rows 0..BM-1, then B rows), logical chunk
-  // (q % BKC) ^ swz(row).  Load j of wave w fills positions
+  // ---- LDS-mode staging.  Stage buffer position q (16-byte chunks): A row
+  // q / BKC for q < ACH, else B row (q - ACH) / BKCB; within a row, logical
+  // chunk c sits at position c ^ swz(row).  Load j of wave w fills positions
   // (NW j + w) * 64 + lane, so each lane's row and chunk are fixed; per stage
   // only the K offset changes.
   uint32_t d_off[NDMA];  // byte offset in A or B of this lane's chunk at K stage 0
@@ -175,16 +184,19 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
     const int q = (NW * j + wave) * 64 + lane;
-    const int r = q / BKC;
-    const int c = (q % BKC) ^ lds_swz<BKC>(r);
-    d_k[j] = c * EPC;
-    if (r < BM) {
+    if (q < ACH) {
+      const int r = q / BKC;
+      const int c = (q % BKC) ^ lds_swz<BKC>(r);
+      d_k[j] = c * EPC;
       int64_t arow = -1;
       if (r < rows) arow = p.a_rows ? p.a_rows[row0 + r] : row0 + r;
       d_off[j] = arow >= 0 ? static_cast<uint32_t>(arow * p.lda * sizeof(TA)) + c * 16u : kOutOfRange;
     } else {
-      const int n = col0 + r - BM;
-      d_off[j] = n < p.N ? static_cast<uint32_t>((int64_t)n * p.ldb * sizeof(TA)) + c * 16u
+      const int r = (q - ACH) / BKCB;
+      const int c = ((q - ACH) % BKCB) ^ lds_swz<BKCB>(r);
+      d_k[j] = c * EPCB;
+      const int n = col0 + r;
+      d_off[j] = n < p.N ? static_cast<uint32_t>((int64_t)n * p.ldb * sizeof(TB)) + c * 16u
                          : kOutOfRange;
     }
   }
@@ -192,11 +204,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   auto issue_stage = [&](int kt) {
     u32x4* s_ = smem + (kt % NSTAGE) * STAGE;
     const int kb = (kt0 + kt) * BKE;
-    const uint32_t kbytes = static_cast<uint32_t>(kb) * sizeof(TA);
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const bool in_ = kt < nk && kb + d_k[j] < k_end && d_off[j] != kOutOfRange;
-      const bool is_a = (NW * j + wave) * 64 < BM * BKC;  // wave-uniform
+      const bool is_a = (NW * j + wave) * 64 < ACH;  // wave-uniform
+      const uint32_t kbytes = static_cast<uint32_t>(kb) * (is_a ? sizeof(TA) : sizeof(TB));
       buffer_load_chunk_lds(is_a ? a_rsrc : b_rsrc, s_ + (NW * j + wave) * 64,
                             in_ ? d_off[j] + kbytes : kOutOfRange);
     }
@@ -226,8 +238,17 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
       fa[f][i] = s_[r_ * BKC + (c_ ^ lds_swz<BKC>(r_))];                                \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < NI; ++j) {                                    \
-      const int r_ = BM + wn * WN + j * BLK + frow;                                     \
-      fb[f][j] = s_[r_ * BKC + (c_ ^ lds_swz<BKC>(r_))];                                \
+      const int r_ = wn * WN + j * BLK + frow;                                          \
+      if constexpr (FP8B) {                                                             \
+        /* 8 fp8 values = K elements 8 c_ .. 8 c_ + 7: half (c_ & 1) of chunk c_ / 2 */ \
+        const int cb_ = c_ >> 1;                                                        \
+        const uint2 q8_ = reinterpret_cast<const uint2*>(                               \
+            s_ + ACH + r_ * BKCB + (cb_ ^ lds_swz<BKCB>(r_)))[c_ & 1];                  \
+        const uint2 lo_ = fp8x4_to_bf16x4(q8_.x), hi_ = fp8x4_to_bf16x4(q8_.y);         \
+        fb[f][j] = u32x4{lo_.x, lo_.y, hi_.x, hi_.y};                                   \
+      } else {                                                                          \
+        fb[f][j] = s_[ACH + r_ * BKCB + (c_ ^ lds_swz<BKCB>(r_))];                      \
+      }                                                                                 \
     }                                                                                   \
   } while (0)
 #define LMOE_MMA(f)                                                                     \
@@ -385,7 +406,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <typename Mma, typename TA, typename TOut, typename Cfg>
+template <typename Mma, typename TA, typename TB, typename TOut, typename Cfg>
 hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN;
   const int n_tiles = (a.N + BN - 1) / BN;
@@ -397,17 +418,17 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const uint64_t a_rows = a.g_off ? (uint64_t)a.a_nrows : (uint64_t)a.M;
-  if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) || (uint64_t)a.N * a.ldb * sizeof(TA) >= (1ull << 31))
+  if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) || (uint64_t)a.N * a.ldb * sizeof(TB) >= (1ull << 31))
     return hipErrorInvalidValue;
   const bool scale = a.b_scale != nullptr;
   float* part = splits > 1 ? partial : nullptr;
   if (part && BM * BN > 128 * 128) return hipErrorInvalidValue;  // partial tile must fit LDS
   if (a.act == kActSqRelu) {
-    if (scale) gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   } else {
-    if (scale) gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActNone, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActNone, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
@@ -433,17 +454,47 @@ hipError_t launch_tile(const GemmArgs& a, Dt a_dt, Dt out_dt, int splits, float*
   using MmaB = std::conditional_t<(Cfg::BM / Cfg::WGM >= 64 && Cfg::BN / Cfg::WGN >= 64),
                                   MmaBf16x32, MmaBf16>;
   if (a_dt == Dt::BF16) {
-    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, Cfg>(a, splits, partial, s);
+    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, uint16_t, Cfg>(a, splits, partial, s);
     if constexpr (Cfg::BM * Cfg::BN <= 128 * 256)
-      return launch_t<MmaB, uint16_t, float, Cfg>(a, splits, partial, s);
+      return launch_t<MmaB, uint16_t, uint16_t, float, Cfg>(a, splits, partial, s);
     return hipErrorInvalidValue;
   }
   if constexpr (Cfg::BM * Cfg::BN <= 128 * 128)
-    return launch_t<MmaF32, float, float, Cfg>(a, splits, partial, s);
+    return launch_t<MmaF32, float, float, float, Cfg>(a, splits, partial, s);
   return hipErrorInvalidValue;
 }
 
+// fp8 (OCP E4M3) B with per-row scales, bf16 A and output: grouped expert
+// GEMMs over fp8 expert weights when experts receive several dozen rows.
+// 96 rows (3 MFMA blocks of 32) cover such an expert with little padding, so
+// each weight tile is read once; 4 waves side by side along N (96 x 64 each);
+// stage rows of 64 bf16 (A) / 64 fp8 (B); two stages and two workgroups per
+// compute unit.
+#ifndef LMOE_F8_BN
+#define LMOE_F8_BN 256
+#endif
+#ifndef LMOE_F8_STAGES
+#define LMOE_F8_STAGES 2
+#endif
+#ifndef LMOE_F8_OCC
+#define LMOE_F8_OCC 2
+#endif
+#ifndef LMOE_F8_BM
+#define LMOE_F8_BM 96
+#endif
+#ifndef LMOE_F8_WGM
+#define LMOE_F8_WGM 1
+#endif
+using TileFp8 = TileCfg<LMOE_F8_BM, LMOE_F8_BN, LMOE_F8_WGM, 4 / LMOE_F8_WGM, 8, LMOE_F8_STAGES, LMOE_F8_OCC>;
+
 }  // namespace
+
+hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s) {
+  if (a.b_scale == nullptr) return hipErrorInvalidValue;
+  return launch_t<MmaBf16x32, uint16_t, uint8_t, uint16_t, TileFp8>(a, 1, nullptr, s);
+}
+
+int tiled_block_m_fp8w() { return TileFp8::BM; }
 
 int tiled_block_m(int tile) {
   switch (tile) {

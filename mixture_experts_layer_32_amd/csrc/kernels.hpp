@@ -39,6 +39,10 @@ struct GemmArgs {
 hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s,
                              int splits = 1, float* partial = nullptr);
 int tiled_block_m(int tile);
+// Grouped GEMM with OCP E4M3 weights (b_scale: one fp32 scale per weight
+// row), bf16 activations and output, LDS-tiled.
+hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s);
+int tiled_block_m_fp8w();
 
 // Weight-streaming grouped GEMM for few rows per group (decode regime):
 // every group's weight matrix is streamed from HBM once per pass of up to

@@ -378,7 +378,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ Y,
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+        o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);

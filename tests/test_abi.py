@@ -51,7 +51,9 @@ def test_regime_choice():
     lay = pkg.LatentMoELayer(workload("latent_decode").spec)
     assert lay.expert_regime(512) == "stream"
     assert lay.expert_regime(16384) == "tiled"
-    assert pkg.LatentMoELayer(workload("latent_fp8_sparse").spec).expert_regime(4096) == "stream"
+    fp8 = pkg.LatentMoELayer(workload("latent_fp8_sparse").spec)
+    assert fp8.expert_regime(4096) == "tiled"    # 73 rows per expert
+    assert fp8.expert_regime(512) == "stream"    # 9 rows per expert
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -44,8 +44,14 @@ SMALL = {
                                      gating="softmax_topk", router_on_latent=True), 200),
     "bf16_standard_moe": (LayerSpec(d=256, l=256, m=160, n_experts=16, top_k=2,
                                     gating="softmax_all", has_projections=False), 257),
-    "fp8_stream_mb8": (LayerSpec(d=512, l=128, m=256, n_experts=16, top_k=4,
-                                 gating="softmax_all", expert_dtype="fp8_e4m3_rowscale"), 200),
+    "fp8_tiled": (LayerSpec(d=512, l=128, m=256, n_experts=16, top_k=4,
+                            gating="softmax_all", expert_dtype="fp8_e4m3_rowscale"), 200),
+    "fp8_tiled_many_rows": (LayerSpec(d=256, l=160, m=288, n_experts=8, top_k=2,
+                                      gating="softmax_topk", expert_dtype="fp8_e4m3_rowscale"),
+                            1000),
+    "fp8_zipf_stream_multipass": (LayerSpec(d=256, l=96, m=160, n_experts=32, top_k=3,
+                                            gating="softmax_all", expert_dtype="fp8_e4m3_rowscale",
+                                            has_router_bias=True), 400),
     "fp8_stream_mb4": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
                                  gating="sigmoid_topk_norm", expert_dtype="fp8_e4m3_rowscale"), 256),
     "fp8_zipf_multipass": (LayerSpec(d=256, l=96, m=160, n_experts=32, top_k=3,
