@@ -138,7 +138,7 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   const bool fp8 = c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
   p.stream = fp8 ? mean <= kFp8StreamMaxRowsPerExpert : mean <= kStreamMaxRowsPerExpert;
   p.mb_max = mean <= 40.0 ? 4 : 8;
-  p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 0;
+  p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 1;  // fp32: the 64 x 64 tile
   p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
   const size_t ab = act_bytes(c);
   const int64_t r_in = c.router_input == LMOE_ROUTER_ON_LATENT ? c.l : c.d;

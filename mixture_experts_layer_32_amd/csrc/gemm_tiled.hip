@@ -459,7 +459,7 @@ hipError_t launch_tile(const GemmArgs& a, Dt a_dt, Dt out_dt, int splits, float*
       return launch_t<MmaB, uint16_t, uint16_t, float, Cfg>(a, splits, partial, s);
     return hipErrorInvalidValue;
   }
-  if constexpr (Cfg::BM * Cfg::BN <= 128 * 128)
+  if constexpr (Cfg::BM * Cfg::BN <= 64 * 64)
     return launch_t<MmaF32, float, float, float, Cfg>(a, splits, partial, s);
   return hipErrorInvalidValue;
 }
@@ -497,7 +497,7 @@ hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s) {
 int tiled_block_m_fp8w() { return TileFp8::BM; }
 
 int tiled_block_m(int tile) {
-  switch (tile) {
+  switch (tile) {  // (fp32 layers run every tile index as Tile64)
     case 0: return Tile128::BM;
     case 1: return Tile64::BM;
     case 2: return Tile256::BM;
@@ -511,6 +511,8 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hi
   if (a_dt == Dt::F32 && out_dt != Dt::F32) return hipErrorInvalidValue;
   if (splits < 1 || (splits > 1 && (a.g_off != nullptr || partial == nullptr || a.N % 4)))
     return hipErrorInvalidValue;
+  // fp32 layers (small) always take the 64 x 64 tile
+  if (a_dt == Dt::F32) return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, s);
   switch (tile) {
     case 0: return launch_tile<Tile128>(a, a_dt, out_dt, splits, partial, s);
     case 1: return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, s);
