@@ -26,6 +26,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // One 16-byte chunk.  A native vector type (not HIP's uint4 struct) so that
 // selects and copies stay in registers.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, WGs dispatched round-robin

@@ -5,29 +5,41 @@
 //
 // With a few dozen rows per expert the GEMM is bound by reading the expert
 // weights from HBM once, so the kernel is built around that stream:
-//  - One workgroup per (expert, tile of 64 * NWB output columns); the tiles of
-//    one expert are contiguous work items, hence on one XCD, sharing the
-//    expert's token rows in that XCD's L2.
+//  - A work unit is (expert, tile of 64 * NWB output columns, pass of up to
+//    16 * MB_MAX rows).  The grid is persistent: as many workgroups as stay
+//    resident, each XCD owning one contiguous range of units, so the tiles
+//    of one expert run on one XCD and share its token rows in that XCD's L2.
+//  - The weight stream of a workgroup does not stop between units.  While a
+//    unit streams, the next unit's group bounds and gather indices are read,
+//    and its first weight and token stages are requested during the unit's
+//    last stages.  Under a saturated memory queue each of those dependent
+//    reads costs microseconds, which a workgroup per unit would spend
+//    without weight bytes in flight.
+//  - Barriers order LDS only (an LDS-scoped fence around s_barrier): the
+//    epilogue's stores and the prefetches stay in flight across them.
 //  - Each wave streams its own 16 * NWB weight rows straight from global
 //    memory into registers in the MFMA B-operand layout with raw buffer
 //    loads: 4 lanes per weight row side by side, so one load instruction
-//    reads 64 contiguous bytes of each of 16 rows.  The next K stage of
-//    weights is in flight while the current one is multiplied.
-//  - The (at most 16 * MB_MAX) token rows of the expert are staged through LDS
-//    per K stage (double-buffered), gathered through token_of for FC1: this is
-//    the dispatch of the token copies, done without materialising them.
+//    reads 64 contiguous bytes of each of 16 rows.  WD stages of weights are
+//    in flight while the current one is multiplied.
+//  - The token rows of a unit are staged through LDS per K stage
+//    (double-buffered, two stages ahead), gathered through token_of for FC1:
+//    this is the dispatch of the token copies, done without materialising
+//    them.
 //  - fp8 (OCP E4M3) weights are widened to bf16 in registers (exact) and the
 //    per-row scale is applied to the fp32 accumulator in the epilogue.
-// Experts with more rows than one pass holds are processed in several passes
-// (the weights are then streamed once per pass).
+// Experts with more rows than one pass holds take several passes (units);
+// the weights are then streamed once per pass.
 //
 // Out-of-range buffer offsets read as zero without a memory request: padding
-// token rows, token chunks past the end of K and the weight prefetch past the
-// last stage use that, so no select on loaded data delays a wait.  Weight
-// chunks past the end of K inside the last stage (K not a multiple of the
-// stage) read the next weight row or zero; they meet zero token values.
-// Every weight offset is carried in the per-lane offset, which is what the
-// range check applies to.
+// token rows, token chunks past the end of K, stages past the end of K and
+// prefetches past the last unit use that, so no select on loaded data delays
+// a wait.  Weight chunks past the end of K inside the last stage (K not a
+// multiple of the stage) read the next weight row or zero; they meet zero
+// token values.  Every offset is carried in the per-lane offset, which is
+// what the range check applies to.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,267 +74,323 @@ template <> struct StreamTraits<float, float> {        // fp32 tokens and weight
 
 constexpr int kStageChunks = 16;  // 16-byte chunks of A per row per K stage (256 bytes)
 
-// K stages of weights requested ahead.  An fp8 stage is half the bytes of a
-// bf16 one and its registers a quarter (one n-block), so fp8 looks further
-// ahead to keep as many weight bytes in flight.
+// K stages of weights requested ahead of the one being multiplied.  An fp8
+// stage is half the bytes of a bf16 one and its registers a quarter (one
+// n-block), so fp8 looks further ahead.
 #ifndef LMOE_W_DEPTH
 #define LMOE_W_DEPTH 1
 #endif
 #ifndef LMOE_W_DEPTH_FP8
-#define LMOE_W_DEPTH_FP8 4
+#define LMOE_W_DEPTH_FP8 3
 #endif
-template <typename TW>
-constexpr int stream_w_depth() { return sizeof(TW) == 1 ? LMOE_W_DEPTH_FP8 : LMOE_W_DEPTH; }
 
-// Per-workgroup context of the streaming kernel.
-template <typename TOut, int NWB>
-struct StreamCtx {
-  BufRsrc a_rsrc, w_rsrc;
-  uint32_t w_off[NWB];   // byte offset of this lane's part of its weight row, per n-block
-  TOut* C;
-  const float* sc;       // per-column scales of this group (fp8) or nullptr
-  const int32_t* a_rows; // gather index (FC1) or nullptr (rows relative to the group)
-  uint32_t a_row_bytes;  // lda * sizeof(TA)
-  int64_t ldc;
-  int K, N, gs, col0, wave, fr, fq, ac, ar0;
+// Stage geometry of one (token type, weight type) pair.
+template <typename TA, typename TW>
+struct StreamShape {
+  using Tr = StreamTraits<TA, TW>;
+  static constexpr int EPC = Tr::EPC;
+  static constexpr int KE = kStageChunks * EPC;    // reduction elements per stage
+  static constexpr int NS = KE / Tr::KSTEP;        // MFMA steps per stage (4)
+  static constexpr bool FP8 = sizeof(TW) == 1;
+  static constexpr int NLD = FP8 ? NS / 2 : NS;    // 16-byte weight loads per n-block per stage
+  static constexpr uint32_t W_STAGE_BYTES = KE * sizeof(TW);
+  static constexpr uint32_t A_STAGE_BYTES = KE * sizeof(TA);
+  static constexpr int WD = FP8 ? LMOE_W_DEPTH_FP8 : LMOE_W_DEPTH;
+  // Register sets rotate: weights modulo WD + 1 stages, token rows modulo 2.
+  // Units are padded to a multiple of this period, so every unit starts at
+  // rotation phase 0 and the rotation stays in compile-time indices.
+  static constexpr int P = (WD + 1) % 2 == 0 ? WD + 1 : 2 * (WD + 1);
 };
 
-// One pass over up to 16 * NMB rows of a group: stream the group's weight
-// tile through registers once, multiply with the staged token rows.
-template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NMB, int NWB,
-          int WD, int ACT, bool SCALE>
-__device__ __forceinline__ void stream_pass(const StreamCtx<TOut, NWB>& c, int p0, int rows,
-                                            u32x4 (*As)[MB_MAX * 16 * kStageChunks]) {
-  using Tr = StreamTraits<TA, TW>;
-  constexpr int EPC = Tr::EPC;
-  constexpr int KE = kStageChunks * EPC;    // reduction elements per stage
-  constexpr int NS = KE / Tr::KSTEP;        // MFMA steps per stage (4)
-  constexpr bool FP8 = sizeof(TW) == 1;
-  constexpr int NLD = FP8 ? NS / 2 : NS;    // 16-byte weight loads per n-block per stage
-  constexpr uint32_t W_STAGE_BYTES = KE * sizeof(TW);
-  constexpr uint32_t A_STAGE_BYTES = KE * sizeof(TA);
-  const int K = c.K;
-  const int nst = (K + KE - 1) / KE;
+// One work unit.  The scalars are wave-uniform; the offsets are per lane.
+template <int MB_MAX, int NWB>
+struct Unit {
+  int local;         // position in the workgroup's item sequence
+  int g, col0;       // group (expert) and first output column
+  int gs, cnt;       // the group's first row and row count
+  int p0, rows;      // this pass's first row (within the group) and rows (0: none)
+  int valid;          // 0: past the end of the sequence (nothing to load or store)
+  BufRsrc w_rsrc;            // the group's weight matrix
+  uint32_t w_off[NWB];       // byte offset of this lane's chunk in its weight row, per n-block
+  uint32_t a_off[MB_MAX];    // byte offset of this thread's chunk column in token row ar0 + 16 i
 
-  // byte offset of this thread's staged token rows (out of range = padding)
-  uint32_t a_row_off[NMB];
+  // field by field, so that the compiler keeps every field in registers
+  __device__ __forceinline__ void assign(const Unit& o) {
+    local = o.local;
+    g = o.g;
+    col0 = o.col0;
+    gs = o.gs;
+    cnt = o.cnt;
+    p0 = o.p0;
+    rows = o.rows;
+    valid = o.valid;
+    w_rsrc = o.w_rsrc;
 #pragma unroll
-  for (int i = 0; i < NMB; ++i) {
-    const int r = c.ar0 + 16 * i;
-    if (r < rows) {
-      const int row = c.a_rows ? c.a_rows[c.gs + p0 + r] : p0 + r;
-      a_row_off[i] = static_cast<uint32_t>(row) * c.a_row_bytes + c.ac * 16u;
-    } else {
-      a_row_off[i] = kOutOfRange;
-    }
+    for (int i = 0; i < NWB; ++i) w_off[i] = o.w_off[i];
+#pragma unroll
+    for (int i = 0; i < MB_MAX; ++i) a_off[i] = o.a_off[i];
   }
+};
 
-  f32x4_t acc[NMB][NWB];
-#pragma unroll
-  for (int i = 0; i < NMB; ++i)
-#pragma unroll
-    for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[2][NMB];
-  u32x4 bw[WD + 1][NWB][NLD];
-
-  // token chunk (row i, column ac) of stage st; past the end of K -> zero
-#define LMOE_LOAD_A(st, ra)                                                                  \
-  do {                                                                                       \
-    const bool in_k_ = (st) * KE + c.ac * EPC < K;                                           \
-    const uint32_t so_ = (st) * A_STAGE_BYTES;                                               \
-    _Pragma("unroll") for (int i = 0; i < NMB; ++i)                                          \
-      ra[i] = buffer_load_chunk(c.a_rsrc, in_k_ ? a_row_off[i] : kOutOfRange, so_);         \
-  } while (0)
-#define LMOE_STORE_A(buf, ra)                                                                \
-  do {                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < NMB; ++i) {                                        \
-      const int r_ = c.ar0 + 16 * i;                                                         \
-      As[buf][r_ * kStageChunks + (c.ac ^ (r_ & 15))] = ra[i];                               \
-    }                                                                                        \
-  } while (0)
-  // weight chunk j of stage st for each n-block; the chunk's byte position
-  // inside the stage is a compile-time constant folded into the instruction
-#define LMOE_LOAD_W(st, br)                                                                  \
-  do {                                                                                       \
-    const bool live_ = (st) < nst;                                                           \
-    const uint32_t so_ = (st) * W_STAGE_BYTES;                                               \
-    _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb) {                                     \
-      const uint32_t vo_ = live_ ? c.w_off[nb] + so_ : kOutOfRange;                          \
-      _Pragma("unroll") for (int j = 0; j < NLD; ++j)                                        \
-        br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(c.w_rsrc, vo_ + 64u * j, 0u);            \
-    }                                                                                        \
-  } while (0)
-#define LMOE_COMPUTE(buf, br)                                                                \
-  do {                                                                                       \
-    _Pragma("unroll") for (int s = 0; s < NS; ++s) {                                         \
-      u32x4 bfr[NWB];                                                                        \
-      _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb) {                                   \
-        if constexpr (FP8) {                                                                 \
-          u32x4 lo_, hi_;                                                                    \
-          fp8_chunk_to_bf16(br[nb][s >> 1], lo_, hi_);                                       \
-          bfr[nb] = (s & 1) ? hi_ : lo_;                                                     \
-        } else {                                                                             \
-          bfr[nb] = br[nb][s];                                                               \
-        }                                                                                    \
-      }                                                                                      \
-      const int c_ = Tr::elem_of(s, c.fq) / EPC;                                             \
-      _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb) {                                   \
-        const int r_ = mb * 16 + c.fr;                                                       \
-        const u32x4 af_ = As[buf][r_ * kStageChunks + (c_ ^ (r_ & 15))];                     \
-        _Pragma("unroll") for (int nb = 0; nb < NWB; ++nb) Mma::mma(acc[mb][nb], af_, bfr[nb]); \
-      }                                                                                      \
-    }                                                                                        \
-  } while (0)
-
-  // Stage st is multiplied from register buffer bw[st % (WD+1)] and LDS
-  // buffer st % 2.  Its weights were requested WD stages earlier; its token
-  // rows two stages earlier (into register set ra[st % 2]) and written to LDS
-  // one stage earlier, so neither latency sets the stage rate.  Every
-  // prefetch is unconditional (past the end of K it reads zeros or is never
-  // used) and is issued before the multiplies it overlaps.
-  LMOE_LOAD_A(0, ra[0]);
-#pragma unroll
-  for (int i = 0; i < WD; ++i) LMOE_LOAD_W(i, bw[i]);
-  LMOE_LOAD_A(1, ra[1]);
-  LMOE_STORE_A(0, ra[0]);
-  __syncthreads();
-  // period of the register rotation: lcm(2, WD + 1) stages
-  constexpr int P = (WD + 1) % 2 == 0 ? WD + 1 : 2 * (WD + 1);
-  for (int st0 = 0; st0 < nst; st0 += P) {
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int st = st0 + u;
-      if (st >= nst) break;
-      LMOE_LOAD_W(st + WD, bw[(u + WD) % (WD + 1)]);
-      LMOE_LOAD_A(st + 2, ra[u % 2]);
-      __builtin_amdgcn_sched_barrier(0);
-      LMOE_COMPUTE(u % 2, bw[u % (WD + 1)]);
-      LMOE_STORE_A((u + 1) % 2, ra[(u + 1) % 2]);
-      __syncthreads();
-    }
-  }
-#undef LMOE_LOAD_A
-#undef LMOE_STORE_A
-#undef LMOE_LOAD_W
-#undef LMOE_COMPUTE
-
-  // Epilogue.  The accumulator holds C[4*fq + v][fr] of each 16x16 block, so
-  // direct stores would be 2- or 4-byte pieces scattered over many rows.  The
-  // tile goes through LDS instead (the token-row buffers are free after the
-  // last barrier) and leaves as whole 16-byte chunks of contiguous row
-  // segments.
-  constexpr int NT = 4 * NWB * 16;            // columns of the workgroup tile
-  constexpr int CPR = NT * sizeof(TOut) / 16; // 16-byte chunks per tile row
-  static_assert(MB_MAX * 16 * NT * sizeof(TOut) <= sizeof(u32x4) * 2 * MB_MAX * 16 * kStageChunks,
-                "output tile must fit the LDS staging buffers");
-  TOut* Ct = reinterpret_cast<TOut*>(&As[0][0]);
-#pragma unroll
-  for (int nb = 0; nb < NWB; ++nb) {
-    const int colt = c.wave * NWB * 16 + nb * 16 + c.fr;
-    const int col = c.col0 + colt;
-    const float s = (SCALE && col < c.N) ? c.sc[col] : 1.f;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float val = acc[mb][nb][v];
-        if (SCALE) val *= s;
-        store_elem<TOut>(Ct + (mb * 16 + c.fq * 4 + v) * NT + colt, apply_act<ACT>(val));
-      }
-    }
-  }
-  __syncthreads();
-  const u32x4* Cv = reinterpret_cast<const u32x4*>(Ct);
-  for (int q = c.wave * 64 + c.fq * 16 + c.fr; q < rows * CPR; q += 256) {
-    const int r = q / CPR, ch = q % CPR;
-    const int col = c.col0 + ch * (16 / static_cast<int>(sizeof(TOut)));
-    if (col < c.N)  // N is a multiple of 16 elements: a chunk is all in or all out
-      *reinterpret_cast<u32x4*>(c.C + (int64_t)(c.gs + p0 + r) * c.ldc + col) = Cv[q];
-  }
+// LDS-only barrier: this wave's LDS operations are complete and every wave
+// has arrived.  Global loads and stores in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// MB_MAX m-blocks of 16 rows per pass, NWB n-blocks of 16 weight rows per wave.
-// One workgroup per work item (group, tile of NT columns); items are ordered
-// so that each XCD receives one contiguous range of them.
-template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NWB, int ACT,
-          bool SCALE>
 #ifndef LMOE_STREAM_OCC
 #define LMOE_STREAM_OCC 2
 #endif
-__global__ __launch_bounds__(256, MB_MAX * NWB <= 8 ? LMOE_STREAM_OCC : 1) void gemm_stream_kernel(GemmArgs p) {
+constexpr int kStreamOcc = LMOE_STREAM_OCC;  // resident workgroups per compute unit
+
+// MB_MAX m-blocks of 16 rows per pass, NWB n-blocks of 16 weight rows per
+// wave, 4 waves.
+template <typename Mma, typename TA, typename TW, typename TOut, int MB_MAX, int NWB, int ACT,
+          bool SCALE>
+__global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p) {
+  using S = StreamShape<TA, TW>;
+  using Tr = typename S::Tr;
+  using U = Unit<MB_MAX, NWB>;
   constexpr int MROWS = MB_MAX * 16;
-  constexpr int NT = 4 * NWB * 16;          // output columns per work item
+  constexpr int NT = 4 * NWB * 16;                    // output columns per unit
+  constexpr int WD = S::WD, P = S::P, NLD = S::NLD, NS = S::NS, KE = S::KE, EPC = S::EPC;
+  constexpr int CPR = NT * static_cast<int>(sizeof(TOut)) / 16;  // 16-byte chunks per tile row
   __shared__ u32x4 As[2][MROWS * kStageChunks];
+  __shared__ u32x4 Cs[MROWS * CPR];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, fq = lane >> 4;
+  const int ac = tid & 15, ar0 = tid >> 4;  // A staging: chunk column ac of rows ar0 + 16 i
   const int n_tiles = (p.N + NT - 1) / NT;
-  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x, p.G * n_tiles);
-  if (item < 0) return;
-  const int g = item / n_tiles;
-  const int gs = p.g_off[g];
-  const int cnt = p.g_off[g + 1] - gs;
-  if (cnt <= 0) return;
+  const int total = p.G * n_tiles;
+  const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int slots = gridDim.x / kNumXcd;
+  const int item_base = (blockIdx.x % kNumXcd) * per_xcd;
+  const int K = p.K;
+  const int nst = (K + KE - 1) / KE;
+  const int nsp = (nst + P - 1) / P * P;  // stages per unit, padded to the rotation period
+  const int s_take = min(1, nsp - 2);     // stage at which the next unit's bounds are used
+  const BufRsrc a_rsrc =
+      make_rsrc(p.A, (uint64_t)(p.a_rows ? p.a_nrows : p.max_rows) * p.lda * sizeof(TA));
+  const BufRsrc goff_rsrc = make_rsrc(p.g_off, (uint64_t)(p.G + 1) * sizeof(int32_t));
+  const uint32_t a_row_bytes = static_cast<uint32_t>(p.lda * sizeof(TA));
+  const uint32_t w_row_bytes = static_cast<uint32_t>(p.ldb * sizeof(TW));
+  const TW* const wglob = static_cast<const TW*>(p.B);
+  TOut* const C = static_cast<TOut*>(p.C);
 
-  StreamCtx<TOut, NWB> c;
-  // token rows: the whole A for a gather, else the group's own rows
-  const TA* abase = static_cast<const TA*>(p.A);
-  if (!p.a_rows) abase += (int64_t)gs * p.lda;
-  const uint64_t a_bytes = (uint64_t)(p.a_rows ? p.a_nrows : cnt) * p.lda * sizeof(TA);
-  c.a_rsrc = make_rsrc(abase, a_bytes);
-  const TW* wbase = static_cast<const TW*>(p.B) + (int64_t)g * p.b_gstride;
-  c.w_rsrc = make_rsrc(wbase, (uint64_t)p.N * p.ldb * sizeof(TW));
-  c.C = static_cast<TOut*>(p.C);
-  c.sc = SCALE ? p.b_scale + (int64_t)g * p.s_gstride : nullptr;
-  c.a_rows = p.a_rows;
-  c.a_row_bytes = static_cast<uint32_t>(p.lda * sizeof(TA));
-  c.ldc = p.ldc;
-  c.K = p.K;
-  c.N = p.N;
-  c.gs = gs;
-  c.col0 = (item % n_tiles) * NT;
-  c.wave = wave;
-  c.fr = lane & 15;
-  c.fq = lane >> 4;
-  c.ac = tid & 15;   // A staging: thread owns chunk column ac of rows ar0 + 16 i
-  c.ar0 = tid >> 4;
-  // byte position of this lane's first chunk in its weight row (lane group
-  // fq supplies 16 bytes of every 64); rows past N read as zero
+  // ---- unit bookkeeping
+  // identity of the first pass of the item at sequence position `local`
+  auto set_item = [&](U& u, int local) {
+    const int item = item_base + local;
+    u.local = local;
+    u.valid = local < per_xcd && item < total;
+    const int it = u.valid ? item : 0;
+    u.g = it / n_tiles;
+    u.col0 = (it % n_tiles) * NT;
+    u.p0 = 0;
+    u.gs = 0;
+    u.cnt = 0;
+    u.rows = 0;
+    u.w_rsrc = make_rsrc(wglob + (int64_t)u.g * p.b_gstride, (uint64_t)p.N * w_row_bytes);
 #pragma unroll
-  for (int nb = 0; nb < NWB; ++nb) {
-    const int n = c.col0 + wave * NWB * 16 + nb * 16 + c.fr;
-    c.w_off[nb] = n < p.N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(p.ldb * sizeof(TW)) +
-                                16u * c.fq
-                          : kOutOfRange;
-  }
+    for (int nb = 0; nb < NWB; ++nb) {
+      const int n = u.col0 + wave * NWB * 16 + nb * 16 + fr;
+      u.w_off[nb] = (u.valid && n < p.N) ? static_cast<uint32_t>(n) * w_row_bytes + 16u * fq
+                                         : kOutOfRange;
+    }
+  };
+  // group bounds g_off[g], g_off[g + 1]: a vector load, so that waiting for
+  // it is ordered with the stream's own loads instead of the LDS counter
+  u32x2 bounds = u32x2{0u, 0u};
+  auto issue_bounds = [&](const U& u) {
+    bounds = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                   goff_rsrc, static_cast<int>(u.valid ? u.g * 4u : kOutOfRange), 0, 0));
+  };
+  auto take_bounds = [&](U& u) {
+    const int gs = __builtin_amdgcn_readfirstlane(static_cast<int>(bounds.x));
+    const int ge = __builtin_amdgcn_readfirstlane(static_cast<int>(bounds.y));
+    u.gs = gs;
+    u.cnt = u.valid ? ge - gs : 0;
+    u.rows = max(0, min(MROWS, u.cnt - u.p0));
+  };
+  // token row of each staged row (FC1 gathers it through a_rows)
+  int tok[MB_MAX];
+  auto issue_rows = [&](const U& u) {
+#pragma unroll
+    for (int i = 0; i < MB_MAX; ++i) {
+      const int r = ar0 + 16 * i;
+      const int lr = u.gs + u.p0 + r;
+      tok[i] = (p.a_rows && r < u.rows) ? p.a_rows[lr] : lr;
+    }
+  };
+  auto take_rows = [&](U& u) {
+#pragma unroll
+    for (int i = 0; i < MB_MAX; ++i) {
+      const int r = ar0 + 16 * i;
+      u.a_off[i] = r < u.rows ? static_cast<uint32_t>(tok[i]) * a_row_bytes + 16u * ac : kOutOfRange;
+    }
+  };
 
-  for (int p0 = 0; p0 < cnt; p0 += MROWS) {
-    const int rows = min(MROWS, cnt - p0);
-    const int nmb = (rows + 15) >> 4;
-#define LMOE_PASS(n) \
-  stream_pass<Mma, TA, TW, TOut, MB_MAX, n, NWB, stream_w_depth<TW>(), ACT, SCALE>(c, p0, rows, As)
-    if constexpr (MB_MAX == 4) {
-      switch (nmb) {
-        case 1: LMOE_PASS(1); break;
-        case 2: LMOE_PASS(2); break;
-        case 3: LMOE_PASS(3); break;
-        default: LMOE_PASS(4); break;
+  // ---- loads of one stage
+  // weight chunks of stage s; the chunk's position inside the stage is a
+  // compile-time constant
+  auto load_w = [&](const U& u, int s, bool live, u32x4 (&br)[NWB][NLD]) {
+    const uint32_t so = static_cast<uint32_t>(s) * S::W_STAGE_BYTES;
+#pragma unroll
+    for (int nb = 0; nb < NWB; ++nb) {
+      const uint32_t vo = live ? u.w_off[nb] + so : kOutOfRange;
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(u.w_rsrc, vo + 64u * j, 0u);
+    }
+  };
+  // token chunk (row ar0 + 16 i, column ac) of stage s; past K -> zero
+  auto load_a = [&](const U& u, int s, u32x4 (&ra)[MB_MAX]) {
+    const bool in_k = s * KE + ac * EPC < K;
+    const uint32_t so = static_cast<uint32_t>(s) * S::A_STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < MB_MAX; ++i)
+      ra[i] = buffer_load_chunk(a_rsrc, in_k ? u.a_off[i] + so : kOutOfRange, 0u);
+  };
+  auto store_a = [&](int buf, const u32x4 (&ra)[MB_MAX]) {
+#pragma unroll
+    for (int i = 0; i < MB_MAX; ++i) {
+      const int r = ar0 + 16 * i;
+      As[buf][r * kStageChunks + (ac ^ (r & 15))] = ra[i];
+    }
+  };
+
+  f32x4_t acc[MB_MAX][NWB];
+#pragma unroll
+  for (int i = 0; i < MB_MAX; ++i)
+#pragma unroll
+    for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, const u32x4 (&br)[NWB][NLD]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4 bfr[NWB];
+#pragma unroll
+      for (int nb = 0; nb < NWB; ++nb) {
+        if constexpr (S::FP8) {
+          u32x4 lo, hi;
+          fp8_chunk_to_bf16(br[nb][s >> 1], lo, hi);
+          bfr[nb] = (s & 1) ? hi : lo;
+        } else {
+          bfr[nb] = br[nb][s];
+        }
       }
-    } else {
-      switch (nmb) {
-        case 1: LMOE_PASS(1); break;
-        case 2: LMOE_PASS(2); break;
-        case 3: LMOE_PASS(3); break;
-        case 4: LMOE_PASS(4); break;
-        case 5: LMOE_PASS(5); break;
-        case 6: LMOE_PASS(6); break;
-        case 7: LMOE_PASS(7); break;
-        default: LMOE_PASS(8); break;
+      const int c = Tr::elem_of(s, fq) / EPC;
+#pragma unroll
+      for (int mb = 0; mb < MB_MAX; ++mb) {
+        const int r = mb * 16 + fr;
+        const u32x4 af = As[buf][r * kStageChunks + (c ^ (r & 15))];
+#pragma unroll
+        for (int nb = 0; nb < NWB; ++nb) Mma::mma(acc[mb][nb], af, bfr[nb]);
       }
     }
-#undef LMOE_PASS
-    __syncthreads();  // the next pass restages the LDS buffers
+  };
+
+  // ---- first unit: its weights depend on the item alone and are requested
+  // before the dependent reads of its bounds, gather indices and token rows
+  U cur, nxt;
+  set_item(cur, blockIdx.x / kNumXcd);
+  if (!cur.valid) return;
+  u32x4 bw[WD + 1][NWB][NLD];
+  u32x4 ra[2][MB_MAX];
+#pragma unroll
+  for (int i = 0; i < WD; ++i) load_w(cur, i, i < nst, bw[i]);
+  issue_bounds(cur);
+  take_bounds(cur);
+  issue_rows(cur);
+  take_rows(cur);
+  load_a(cur, 0, ra[0]);
+  load_a(cur, 1, ra[1]);
+  store_a(0, ra[0]);
+  lds_barrier();
+  nxt.assign(cur);
+
+  // Stage st of a unit is multiplied from register set bw[st % (WD+1)] and
+  // LDS buffer st % 2.  Its weights were requested WD stages earlier, its
+  // token rows two stages earlier (into ra[st % 2]) and written to LDS one
+  // stage earlier.  Requests past the unit's last stage go to the next unit.
+  for (;;) {
+    for (int st0 = 0; st0 < nsp; st0 += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const int st = st0 + u;
+        // the next unit: identity and bounds request, then bounds and gather
+        // indices, then its token-row offsets, each a stage or more apart
+        if (st == 0) {
+          if (cur.p0 + MROWS < cur.cnt) {  // another pass over the same group
+            nxt.assign(cur);
+            nxt.p0 = cur.p0 + MROWS;
+            nxt.rows = min(MROWS, cur.cnt - nxt.p0);
+          } else {
+            set_item(nxt, cur.local + slots);
+            issue_bounds(nxt);
+          }
+        }
+        if (st == s_take) {
+          if (nxt.p0 == 0) take_bounds(nxt);
+          issue_rows(nxt);
+        }
+        if (st == nsp - 2) take_rows(nxt);
+        // weights of stage st + WD, token rows of stage st + 2
+        const int sw = st + WD;
+        if (sw < nsp) load_w(cur, sw, sw < nst && cur.rows > 0, bw[(u + WD) % (WD + 1)]);
+        else load_w(nxt, sw - nsp, sw - nsp < nst && nxt.rows > 0, bw[(u + WD) % (WD + 1)]);
+        const int sa = st + 2;
+        if (sa < nsp) load_a(cur, sa, ra[u % 2]);
+        else load_a(nxt, sa - nsp, ra[u % 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(u % 2, bw[u % (WD + 1)]);
+        store_a((u + 1) % 2, ra[(u + 1) % 2]);
+        lds_barrier();
+      }
+    }
+
+    // Epilogue.  The accumulator holds C[4*fq + v][fr] of each 16x16 block,
+    // so direct stores would be 2- or 4-byte pieces scattered over many
+    // rows.  The tile goes through LDS and leaves as whole 16-byte chunks
+    // of contiguous row segments; the stores overlap the next unit.
+    if (cur.rows > 0) {
+      TOut* Ct = reinterpret_cast<TOut*>(&Cs[0]);
+#pragma unroll
+      for (int nb = 0; nb < NWB; ++nb) {
+        const int colt = wave * NWB * 16 + nb * 16 + fr;
+        const int col = cur.col0 + colt;
+        const float sc = (SCALE && col < p.N) ? p.b_scale[(int64_t)cur.g * p.s_gstride + col] : 1.f;
+#pragma unroll
+        for (int mb = 0; mb < MB_MAX; ++mb) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float val = acc[mb][nb][v];
+            if (SCALE) val *= sc;
+            store_elem<TOut>(Ct + (mb * 16 + fq * 4 + v) * NT + colt, apply_act<ACT>(val));
+          }
+        }
+      }
+      lds_barrier();
+      const int64_t row0 = (int64_t)cur.gs + cur.p0;
+      for (int q = tid; q < cur.rows * CPR; q += 256) {
+        const int r = q / CPR, ch = q % CPR;
+        const int col = cur.col0 + ch * (16 / static_cast<int>(sizeof(TOut)));
+        if (col < p.N)  // N is a multiple of 16 elements: a chunk is all in or all out
+          *reinterpret_cast<u32x4*>(C + (row0 + r) * p.ldc + col) = Cs[q];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB_MAX; ++i)
+#pragma unroll
+      for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (!nxt.valid) break;
+    cur.assign(nxt);
   }
 }
 
@@ -336,15 +404,30 @@ __global__ __launch_bounds__(256, MB_MAX * NWB <= 8 ? LMOE_STREAM_OCC : 1) void 
 #define LMOE_STREAM_NWB_MB8 1
 #endif
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <typename Mma, typename TA, typename TW, typename TOut, int MB>
 hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   constexpr int NWB = MB >= 8 ? LMOE_STREAM_NWB_MB8 : LMOE_STREAM_NWB;
   constexpr int NT = 4 * NWB * 16;
+  if (a.g_off == nullptr || a.G < 1) return hipErrorInvalidValue;
   const int64_t n_tiles = (a.N + NT - 1) / NT;
   const int64_t total = n_tiles * a.G;
-  const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (total <= 0) return hipSuccess;
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
   // the epilogue stores whole 16-byte chunks: output width and stride are
   // multiples of 16 elements (true of the expert widths m and l)
   if (a.N % 16 || a.ldc % 16) return hipErrorInvalidValue;
@@ -353,6 +436,11 @@ hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) ||
       (uint64_t)a.N * a.ldb * sizeof(TW) >= (1ull << 31))
     return hipErrorInvalidValue;
+  // persistent grid: the resident workgroups, a multiple of the XCD count,
+  // no more per XCD than it has work items
+  const int64_t per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int64_t slots = std::max<int64_t>(1, (int64_t)kStreamOcc * device_cus() / kNumXcd);
+  const int64_t grid = std::min(per_xcd, slots) * kNumXcd;
   const bool scale = a.b_scale != nullptr;
   if (a.act == kActSqRelu) {
     if (scale) gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActSqRelu, true><<<dim3(grid), dim3(256), 0, s>>>(a);
