@@ -73,6 +73,23 @@ typedef enum {
   LMOE_ACT_SQRELU = 0             /* non-gated expert FFN with (max(0, a))^2 (Table 2: Squared-ReLU) */
 } lmoe_activation;
 
+/* Expert-FFN kernels (the grouped latent expert FFN of Eq. (2)).  AUTO picks
+ * from the mean number of token copies per expert, T*K/N:
+ *   STREAM - weight-streaming grouped GEMMs, FC1 then FC2 (few rows per
+ *            expert: the decode regime, bound by reading the expert weights);
+ *   FUSED  - FC1 and FC2 in one kernel, the activated rows kept on chip
+ *            (decode regime, bf16, m <= 1536, at least one expert per compute
+ *            unit; an expert with more than 48 rows takes several passes);
+ *   TILED  - LDS-tiled MFMA grouped GEMMs (many rows per expert: prefill).
+ * Every choice computes the same function; forcing one is for tests and
+ * measurements.  FUSED needs bf16 activations and experts and m <= 1536. */
+typedef enum {
+  LMOE_EXPERTS_AUTO = 0,
+  LMOE_EXPERTS_TILED = 1,
+  LMOE_EXPERTS_STREAM = 2,
+  LMOE_EXPERTS_FUSED = 3
+} lmoe_expert_kernel;
+
 typedef struct {
   int64_t d;           /* model width */
   int64_t l;           /* latent width (== d when has_projections == 0) */
@@ -87,6 +104,7 @@ typedef struct {
                              F32 experts need F32 activations; BF16/FP8 need BF16. */
   int32_t has_projections;  /* 0: standard MoE (requires l == d) */
   int32_t has_router_bias;  /* 1: z += b before selection and gating (fp32 b[N]) */
+  int32_t expert_kernel;    /* lmoe_expert_kernel; 0 = AUTO */
 } lmoe_config;
 
 /* Device pointers; shapes use the config's d, l, m, N. */
@@ -168,8 +186,9 @@ const char *latentmoe_status_string(lmoe_status s);
 const char *latentmoe_last_error(void);
 
 /* Name of the expert-kernel regime the handle picks for T tokens:
- * "stream" (weight-streaming skinny kernel, tokens per expert small) or
- * "tiled" (LDS-tiled MFMA grouped GEMM).  For reports only. */
+ * "stream" (weight-streaming grouped GEMMs, tokens per expert few),
+ * "fused" (FC1 and FC2 in one weight-streaming kernel) or "tiled"
+ * (LDS-tiled MFMA grouped GEMMs).  For reports only. */
 const char *latentmoe_expert_regime(const lmoe_handle *h, int64_t T);
 
 #ifdef __cplusplus

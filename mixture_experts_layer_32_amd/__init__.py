@@ -24,6 +24,10 @@ LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE = 0, 1, 2
 ROUTER_ON_X, ROUTER_ON_LATENT = 0, 1
 GATE_SOFTMAX_ALL, GATE_SOFTMAX_TOPK, GATE_SIGMOID_TOPK_NORM = 0, 1, 2
 ACT_SQRELU = 0
+# expert-FFN kernel choice (lmoe_expert_kernel); every choice computes the same layer
+EXPERTS_AUTO, EXPERTS_TILED, EXPERTS_STREAM, EXPERTS_FUSED = 0, 1, 2, 3
+_EXPERT_KERNEL = {"auto": EXPERTS_AUTO, "tiled": EXPERTS_TILED, "stream": EXPERTS_STREAM,
+                  "fused": EXPERTS_FUSED}
 NUM_STAGES = 7
 STAGE_NAMES = ("down_router", "topk", "dispatch", "fc1", "fc2", "combine", "up")
 
@@ -43,7 +47,7 @@ class LmoeConfig(ctypes.Structure):
                 ("router_input", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("activation", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("expert_dtype", ctypes.c_int32), ("has_projections", ctypes.c_int32),
-                ("has_router_bias", ctypes.c_int32)]
+                ("has_router_bias", ctypes.c_int32), ("expert_kernel", ctypes.c_int32)]
 
 
 class LmoeWeights(ctypes.Structure):
@@ -111,12 +115,14 @@ def _check(status: int):
                                                  L.latentmoe_last_error().decode()))
 
 
-def make_config(spec) -> LmoeConfig:
-    """C config from a LayerSpec-like object (d, l, m, n_experts, top_k, ...)."""
+def make_config(spec, expert_kernel: str = "auto") -> LmoeConfig:
+    """C config from a LayerSpec-like object (d, l, m, n_experts, top_k, ...).
+    expert_kernel: "auto", "tiled", "stream" or "fused" (lmoe_expert_kernel)."""
     return LmoeConfig(spec.d, spec.l, spec.m, spec.n_experts, spec.top_k,
                       ROUTER_ON_LATENT if spec.router_on_latent else ROUTER_ON_X,
                       _GATE[spec.gating], ACT_SQRELU, _DT[spec.act_dtype], _DT[spec.expert_dtype],
-                      int(spec.has_projections), int(spec.has_router_bias))
+                      int(spec.has_projections), int(spec.has_router_bias),
+                      _EXPERT_KERNEL[expert_kernel])
 
 
 class StageTimer:
@@ -154,9 +160,9 @@ def _torch():
 class LatentMoELayer:
     """Handle on one layer configuration; weights are passed per call."""
 
-    def __init__(self, spec):
+    def __init__(self, spec, expert_kernel: str = "auto"):
         self.spec = spec
-        self._cfg = make_config(spec)
+        self._cfg = make_config(spec, expert_kernel)
         h = ctypes.c_void_p()
         _check(lib().latentmoe_create(ctypes.byref(self._cfg), ctypes.byref(h)))
         self._h = h

@@ -64,6 +64,9 @@ constexpr double kStreamMaxRowsPerExpert = 96.0;  // mean copies per expert -> s
 #define LMOE_FP8_STREAM_MAX_ROWS 40.0
 #endif
 constexpr double kFp8StreamMaxRowsPerExpert = LMOE_FP8_STREAM_MAX_ROWS;
+// fused expert FFN (bf16): up to this many copies per expert on average, so
+// that few experts exceed the kernel's 48-row pass
+constexpr double kFusedMaxRowsPerExpert = 36.0;
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -121,6 +124,7 @@ struct Plan {
   int64_t T = 0, copies = 0;
   int nblk = 0;
   bool stream = true;   // expert GEMMs: weight-streaming kernel
+  bool fused = false;   // FC1 + FC2 in the fused weight-streaming kernel
   int mb_max = 4;       // streaming kernel rows per pass / 16
   int expert_tile = 0;  // tiled kernel tile config
   int tile_m = 128;
@@ -136,7 +140,19 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.nblk = static_cast<int>((T + lmoe::kRouteBlock - 1) / lmoe::kRouteBlock);
   const double mean = T > 0 ? double(p.copies) / double(c.n_experts) : 0.0;
   const bool fp8 = c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
-  p.stream = fp8 ? mean <= kFp8StreamMaxRowsPerExpert : mean <= kStreamMaxRowsPerExpert;
+  const bool bf16 = c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16;
+  switch (c.expert_kernel) {
+    case LMOE_EXPERTS_TILED: p.stream = false; break;
+    case LMOE_EXPERTS_STREAM: p.stream = true; break;
+    case LMOE_EXPERTS_FUSED: p.stream = p.fused = true; break;
+    default:
+      p.stream = fp8 ? mean <= kFp8StreamMaxRowsPerExpert : mean <= kStreamMaxRowsPerExpert;
+      // one expert per resident workgroup: the fused kernel fills the chip
+      // only with at least one expert per compute unit
+      p.fused = p.stream && bf16 && mean <= kFusedMaxRowsPerExpert &&
+                lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m)) &&
+                c.n_experts >= kComputeUnits;
+  }
   p.mb_max = mean <= 40.0 ? 4 : 8;
   p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 1;  // fp32: the 64 x 64 tile
   p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
@@ -231,6 +247,12 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
                 (long long)kMaxExperts, (long long)kMaxTopK);
   if (c.d > (int64_t(1) << 20) || c.m > (int64_t(1) << 20))
     return fail(LMOE_ERR_UNSUPPORTED, "create: widths above 2^20");
+  if (c.expert_kernel < LMOE_EXPERTS_AUTO || c.expert_kernel > LMOE_EXPERTS_FUSED)
+    return fail(LMOE_ERR_INVALID_ARG, "create: bad expert_kernel");
+  if (c.expert_kernel == LMOE_EXPERTS_FUSED &&
+      !(c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16 &&
+        lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m))))
+    return fail(LMOE_ERR_UNSUPPORTED, "create: the fused expert kernel needs bf16 and m <= 1536");
   lmoe_handle* h = new (std::nothrow) lmoe_handle;
   if (!h) return fail(LMOE_ERR_ALLOC, "create: out of host memory");
   h->cfg = c;
@@ -253,7 +275,8 @@ lmoe_status latentmoe_workspace_size(const lmoe_handle* h, int64_t T, size_t* by
 
 const char* latentmoe_expert_regime(const lmoe_handle* h, int64_t T) {
   if (!h || T < 0) return "invalid";
-  return make_plan(h->cfg, T).stream ? "stream" : "tiled";
+  const Plan p = make_plan(h->cfg, T);
+  return p.fused ? "fused" : p.stream ? "stream" : "tiled";
 }
 
 lmoe_status latentmoe_timer_create(lmoe_timer** out) {
@@ -410,7 +433,16 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   }
   LMOE_MARK(3);
   // ---- stage 3: FC1 + squared ReLU, token rows gathered through token_of
-  {
+  // (fused: FC1 and FC2 of each expert in one kernel, H kept on chip)
+  if (p.fused) {
+    lmoe::FfnArgs a;
+    a.A = u; a.lda = l; a.a_rows = token_of; a.a_nrows = Ti;
+    a.W1 = w->w1; a.W2 = w->w2;
+    a.Y = Y; a.ldy = l;
+    a.g_off = offsets; a.G = N;
+    a.l = static_cast<int>(l); a.m = static_cast<int>(m);
+    LMOE_TRY(lmoe::launch_ffn_stream(a, s), "FC1 + FC2 (fused)");
+  } else {
     lmoe::GemmArgs a;
     a.A = u; a.lda = l; a.a_rows = token_of; a.a_nrows = Ti;
     a.B = w->w1; a.ldb = l; a.b_gstride = int64_t(m) * l;
@@ -425,7 +457,7 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   }
   LMOE_MARK(4);
   // ---- stage 4: FC2
-  {
+  if (!p.fused) {
     lmoe::GemmArgs a;
     a.A = H; a.lda = m; a.a_nrows = static_cast<int>(p.copies);
     a.B = w->w2; a.ldb = m; a.b_gstride = int64_t(l) * m;

@@ -50,6 +50,29 @@ int tiled_block_m_fp8w();
 hipError_t launch_gemm_stream(const GemmArgs& a, Dt a_dt, Dt w_dt, Dt out_dt, int mb_max,
                               hipStream_t s);
 
+// Fused expert FFN for few rows per expert (decode regime), bf16:
+// Y[r] = sqrelu(A[a_rows[r]] W1_g^T) W2_g^T for the rows r of each group g,
+// the hidden row kept on chip.  One resident workgroup per compute unit
+// takes whole experts; an expert with more than ffn_stream_rows() rows is
+// processed in several passes (its weights streamed once per pass).
+struct FfnArgs {
+  const void* A = nullptr;          // token rows [a_nrows][lda] (u)
+  int64_t lda = 0;
+  const int32_t* a_rows = nullptr;  // A row of grouped row r (token_of)
+  int a_nrows = 0;
+  const void* W1 = nullptr;         // [G][m][l]
+  const void* W2 = nullptr;         // [G][l][m]
+  void* Y = nullptr;                // [rows][ldy]
+  int64_t ldy = 0;
+  const int32_t* g_off = nullptr;   // [G+1] first grouped row of each group
+  int G = 0;
+  int l = 0, m = 0;
+};
+// Whether the fused kernel takes this shape (the hidden rows fit in LDS).
+bool ffn_stream_fits(int l, int m);
+int ffn_stream_rows();
+hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s);
+
 // Routing.
 hipError_t launch_topk_gate(const float* logits, const float* bias, int T, int N, int K,
                             int gating, int32_t* idx, float* gate, hipStream_t s);

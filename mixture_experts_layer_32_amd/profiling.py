@@ -13,8 +13,9 @@ reads the CSV files of
   rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 bench.py --copy-calibration
 
 and writes profiles/<workload>_kernels_trace.md (per-kernel durations) and
-profiles/gemm_stream_<workload>_hbm.txt (HBM bytes per launch of the expert
-kernels, scaled by what the same counters read for a 1 GiB device copy).
+profiles/<kernel>_<workload>_hbm.txt (HBM bytes per launch of the expert
+kernels, scaled by what the same counters read for a 1 GiB device copy;
+<kernel> is ffn_stream for the fused FC1 + FC2 kernel, else gemm_stream).
 The HBM file records a hash of the kernel sources; bench.py reports its
 traffic only while the sources still hash the same.
 """
@@ -32,8 +33,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide what the expert kernels read and write
-KERNEL_SOURCES = ("csrc/gemm_stream.hip", "csrc/gemm_tiled.hip", "csrc/common.hpp",
-                  "csrc/kernels.hpp", "csrc/api.cpp")
+KERNEL_SOURCES = ("csrc/gemm_stream.hip", "csrc/ffn_stream.hip", "csrc/gemm_tiled.hip",
+                  "csrc/common.hpp", "csrc/kernels.hpp", "csrc/api.cpp")
 COPY_BYTES = 1 << 30  # bench.py --copy-calibration: 1 GiB read + 1 GiB written per launch
 
 
@@ -51,7 +52,10 @@ def short_name(name: str) -> str:
 
 
 def expert_stage(name: str) -> str | None:
-    """gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, ACT, SCALE>: ACT 1 = FC1."""
+    """gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, ACT, SCALE>: ACT 1 = FC1;
+    ffn_stream_kernel: the fused FC1 + FC2 kernel."""
+    if "ffn_stream_kernel" in name:
+        return "ffn"
     if "gemm_stream_kernel<" not in name:
         return None
     args = [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")]
@@ -160,10 +164,16 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
         f.write("\n".join(lines) + "\n")
 
 
+def hbm_file(workload: str, stage: str) -> str:
+    kernel = "ffn_stream" if stage == "ffn" else "gemm_stream"
+    return os.path.join(PROFILES, "%s_%s_hbm.txt" % (kernel, workload))
+
+
 def read_hbm(workload: str, stage: str):
-    """HBM bytes per launch of the FC1/FC2 kernel from the committed summary,
-    or None when there is none or the kernel sources changed since."""
-    path = os.path.join(PROFILES, "gemm_stream_%s_hbm.txt" % workload)
+    """HBM bytes per launch of the FC1/FC2 (or fused, stage "ffn") kernel from
+    the committed summary, or None when there is none or the kernel sources
+    changed since."""
+    path = hbm_file(workload, stage)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -194,7 +204,8 @@ def main():
         write_trace_md(a.workload, a.trace, a.bench_json, out)
         print(out)
     if a.fetch and a.write and a.copy_fetch and a.copy_write:
-        out = os.path.join(PROFILES, "gemm_stream_%s_hbm.txt" % a.workload)
+        stages = {expert_stage(n) for n in counter_per_dispatch(a.fetch, "FETCH_SIZE")}
+        out = hbm_file(a.workload, "ffn" if "ffn" in stages else "fc1")
         write_hbm_txt(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out)
         print(out)
 

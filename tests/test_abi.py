@@ -49,11 +49,17 @@ def test_create_accepts_every_workload_and_destroys():
 
 def test_regime_choice():
     lay = pkg.LatentMoELayer(workload("latent_decode").spec)
-    assert lay.expert_regime(512) == "stream"
+    assert lay.expert_regime(512) == "fused"     # 32 rows per expert, 512 experts, m 1536
+    assert lay.expert_regime(1024) == "stream"   # 64 rows per expert
     assert lay.expert_regime(16384) == "tiled"
+    std = pkg.LatentMoELayer(workload("std_decode").spec)
+    assert std.expert_regime(512) == "stream"    # 128 experts: fewer than compute units
     fp8 = pkg.LatentMoELayer(workload("latent_fp8_sparse").spec)
     assert fp8.expert_regime(4096) == "tiled"    # 73 rows per expert
     assert fp8.expert_regime(512) == "stream"    # 9 rows per expert
+    for kind in ("tiled", "stream", "fused"):
+        forced = pkg.LatentMoELayer(workload("latent_decode").spec, expert_kernel=kind)
+        assert forced.expert_regime(512) == kind
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -66,6 +72,8 @@ def test_regime_choice():
     ("l", 264, -1),               # l > d with projections
     ("m", 120, -2),               # not a multiple of 16
     ("activation", 1, -2),        # gated experts not built
+    ("expert_kernel", 4, -1),
+    ("expert_kernel", 3, -2),     # fused kernel: bf16 only (the tiny layer is fp32)
 ])
 def test_create_rejects(field, value, status):
     cfg = pkg.make_config(workload("tiny").spec)

@@ -81,6 +81,61 @@ def test_small_case_matches_oracle(name):
     print(name, st, flush=True)
 
 
+# Each expert kernel forced on shapes the automatic choice would not give it.
+FORCED = {
+    # fused FC1 + FC2: ragged l and m (last tiles partial, stages padded),
+    # fewer experts than compute units
+    "fused_ragged": (LayerSpec(d=1056, l=1040, m=528, n_experts=24, top_k=4,
+                               gating="sigmoid_topk_norm"), 200, "fused"),
+    # experts with several 48-row passes
+    "fused_multipass": (LayerSpec(d=256, l=128, m=192, n_experts=8, top_k=4,
+                                  gating="softmax_topk"), 300, "fused"),
+    # skewed loads: empty experts and multi-pass ones in one batch
+    "fused_zipf_empty": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
+                                   gating="softmax_all", has_router_bias=True), 256, "fused"),
+    # the largest hidden width that fits on chip, more experts than compute units
+    "fused_m1536": (LayerSpec(d=512, l=256, m=1536, n_experts=300, top_k=2,
+                              gating="softmax_topk"), 600, "fused"),
+    "fused_one_token": (LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4), 1, "fused"),
+    "tiled_few_rows": (LayerSpec(d=256, l=128, m=192, n_experts=64, top_k=4,
+                                 gating="softmax_topk"), 256, "tiled"),
+    "stream_many_rows": (LayerSpec(d=256, l=128, m=192, n_experts=8, top_k=2,
+                                   gating="softmax_topk"), 1000, "stream"),
+}
+
+
+@pytest.mark.parametrize("name", list(FORCED))
+def test_forced_expert_kernel_matches_oracle(name):
+    import mixture_experts_layer_32_amd as pkg
+    spec, T, kind = FORCED[name]
+    layer = pkg.LatentMoELayer(spec, expert_kernel=kind)
+    assert layer.expert_regime(T) == kind
+    w, x = _case(spec, T, seed=2)
+    g, _ = run_gpu(spec, w, x, layer=layer)
+    check_routing_structure(spec, g, T)
+    st = check_against_oracle(spec, w, x, g)
+    print(name, kind, st, flush=True)
+
+
+def test_expert_kernels_agree():
+    """The three expert kernels on one input: same routing, outputs within
+    the bf16 tolerance of each other (each is checked against the oracle
+    above)."""
+    import mixture_experts_layer_32_amd as pkg
+    spec, T = LayerSpec(d=512, l=256, m=384, n_experts=32, top_k=4,
+                        gating="sigmoid_topk_norm"), 256
+    w, x = _case(spec, T, seed=3)
+    outs = {}
+    for kind in ("tiled", "stream", "fused"):
+        g, _ = run_gpu(spec, w, x, layer=pkg.LatentMoELayer(spec, expert_kernel=kind))
+        outs[kind] = g
+    for kind in ("stream", "fused"):
+        assert np.array_equal(outs[kind]["topk_idx"], outs["tiled"]["topk_idx"])
+        a, b = outs[kind]["out"], outs["tiled"]["out"]
+        rel = np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-30)
+        assert rel.max() < 2e-2, (kind, rel.max())
+
+
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_identity_projections_equal_standard_moe_bit_exact(act):
     base = workload("tiny_identity").spec.replace(act_dtype=act, expert_dtype=act)
