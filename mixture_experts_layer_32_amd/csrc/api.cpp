@@ -129,6 +129,10 @@ struct Plan {
   int expert_tile = 0;  // tiled kernel tile config
   int tile_m = 128;
   DensePlan down, router, up;
+  // split-K partials left for the top-k kernel to add: the router logits,
+  // and the down-projection when the router reads x (nothing needs u before)
+  bool defer_u = false, defer_z = false;
+  size_t part_z = 0;    // byte offset of the router partials in the partial region
   size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, partial,
       total;
 };
@@ -166,7 +170,15 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
     partial = std::max(partial, size_t(p.up.splits > 1 ? p.up.splits : 0) * T * c.d * 4);
   }
   p.router = plan_dense(T, c.n_experts, r_in, ab, false);  // fp32 logits
-  partial = std::max(partial, size_t(p.router.splits > 1 ? p.router.splits : 0) * T * c.n_experts * 4);
+  p.defer_u = c.has_projections && c.router_input == LMOE_ROUTER_ON_X && p.down.splits > 1;
+  p.defer_z = p.router.splits > 1;
+  const size_t router_part = size_t(p.router.splits > 1 ? p.router.splits : 0) * T * c.n_experts * 4;
+  if (p.defer_u) {  // both partial sets live until the top-k kernel
+    p.part_z = align_up(size_t(p.down.splits) * T * c.l * 4);
+    partial = std::max(partial, p.part_z + router_part);
+  } else {
+    partial = std::max(partial, router_part);
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.u = take(c.has_projections ? size_t(T) * c.l * ab : 0);
@@ -397,12 +409,15 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   if (ev) LMOE_TRY(hipEventRecord(ev[i], s), "hipEventRecord")
 
   LMOE_MARK(0);
-  // ---- stage 0: down-projection and router logits
+  // ---- stage 0: down-projection and router logits (split-K partials that
+  // the top-k kernel adds when deferred)
+  float* part_z = reinterpret_cast<float*>(ws + p.partial + p.part_z);
   if (c.has_projections) {
     lmoe::GemmArgs a;
     a.A = x; a.lda = d; a.B = w->w_down; a.ldb = d; a.C = u; a.ldc = l;
     a.M = Ti; a.N = l; a.K = d;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial), "W_down GEMM");
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial, !p.defer_u),
+             "W_down GEMM");
   }
   {
     const bool lat = c.router_input == LMOE_ROUTER_ON_LATENT;
@@ -411,13 +426,26 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     a.B = w->w_router; a.ldb = lat ? l : d;
     a.C = logits; a.ldc = N;
     a.M = Ti; a.N = N; a.K = lat ? l : d;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, lmoe::Dt::F32, p.router.tile, s, p.router.splits, partial),
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, lmoe::Dt::F32, p.router.tile, s, p.router.splits, part_z,
+                                     !p.defer_z),
              "router GEMM");
   }
   LMOE_MARK(1);
-  // ---- stage 1: top-k and gates
-  LMOE_TRY(lmoe::launch_topk_gate(logits, c.has_router_bias ? w->router_bias : nullptr, Ti, N, K,
-                                  c.gating, idx, gate, s), "top-k");
+  // ---- stage 1: top-k and gates (and the deferred split-K reductions)
+  {
+    lmoe::TopkArgs a;
+    a.logits = p.defer_z ? part_z : logits;
+    a.lsplits = p.defer_z ? p.router.splits : 1;
+    a.logits_out = p.defer_z && dbg && dbg->logits ? logits : nullptr;
+    a.bias = c.has_router_bias ? w->router_bias : nullptr;
+    a.T = Ti; a.N = N; a.K = K; a.gating = c.gating;
+    a.idx = idx; a.gate = gate;
+    if (p.defer_u) {
+      a.u_part = partial; a.usplits = p.down.splits; a.l = static_cast<int>(l);
+      a.u = u; a.u_bf16 = adt == lmoe::Dt::BF16;
+    }
+    LMOE_TRY(lmoe::launch_topk_gate(a, s), "top-k");
+  }
   LMOE_MARK(2);
   // ---- stage 2: dispatch indices
   if (lmoe::route_small_fits(Ti, N, K)) {

@@ -407,7 +407,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 template <typename Mma, typename TA, typename TB, typename TOut, typename Cfg>
-hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s) {
+hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, hipStream_t s) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN;
   const int n_tiles = (a.N + BN - 1) / BN;
   int64_t m_tiles;
@@ -431,7 +431,7 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s
     else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !part) return e;
+  if (e != hipSuccess || !part || !reduce) return e;
   const int64_t n4 = (int64_t)a.M * (a.N / 4);
   const dim3 rg((n4 + 255) / 256);
   TOut* C = static_cast<TOut*>(a.C);
@@ -449,18 +449,18 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, hipStream_t s
 // partials) with tiles of at most 128 x 256
 template <typename Cfg>
 hipError_t launch_tile(const GemmArgs& a, Dt a_dt, Dt out_dt, int splits, float* partial,
-                       hipStream_t s) {
+                       bool reduce, hipStream_t s) {
   // 32x32 MFMA blocks where the wave sub-tile holds at least 2 x 2 of them
   using MmaB = std::conditional_t<(Cfg::BM / Cfg::WGM >= 64 && Cfg::BN / Cfg::WGN >= 64),
                                   MmaBf16x32, MmaBf16>;
   if (a_dt == Dt::BF16) {
-    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, uint16_t, Cfg>(a, splits, partial, s);
+    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, uint16_t, Cfg>(a, splits, partial, reduce, s);
     if constexpr (Cfg::BM * Cfg::BN <= 128 * 256)
-      return launch_t<MmaB, uint16_t, uint16_t, float, Cfg>(a, splits, partial, s);
+      return launch_t<MmaB, uint16_t, uint16_t, float, Cfg>(a, splits, partial, reduce, s);
     return hipErrorInvalidValue;
   }
   if constexpr (Cfg::BM * Cfg::BN <= 64 * 64)
-    return launch_t<MmaF32, float, float, float, Cfg>(a, splits, partial, s);
+    return launch_t<MmaF32, float, float, float, Cfg>(a, splits, partial, reduce, s);
   return hipErrorInvalidValue;
 }
 
@@ -491,7 +491,7 @@ using TileFp8 = TileCfg<LMOE_F8_BM, LMOE_F8_BN, LMOE_F8_WGM, 4 / LMOE_F8_WGM, 8,
 
 hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s) {
   if (a.b_scale == nullptr) return hipErrorInvalidValue;
-  return launch_t<MmaBf16x32, uint16_t, uint8_t, uint16_t, TileFp8>(a, 1, nullptr, s);
+  return launch_t<MmaBf16x32, uint16_t, uint8_t, uint16_t, TileFp8>(a, 1, nullptr, false, s);
 }
 
 int tiled_block_m_fp8w() { return TileFp8::BM; }
@@ -506,18 +506,18 @@ int tiled_block_m(int tile) {
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s,
-                             int splits, float* partial) {
+                             int splits, float* partial, bool reduce) {
   if (a_dt == Dt::FP8) return hipErrorInvalidValue;  // fp8 weights go through the streaming kernel
   if (a_dt == Dt::F32 && out_dt != Dt::F32) return hipErrorInvalidValue;
   if (splits < 1 || (splits > 1 && (a.g_off != nullptr || partial == nullptr || a.N % 4)))
     return hipErrorInvalidValue;
   // fp32 layers (small) always take the 64 x 64 tile
-  if (a_dt == Dt::F32) return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, s);
+  if (a_dt == Dt::F32) return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, reduce, s);
   switch (tile) {
-    case 0: return launch_tile<Tile128>(a, a_dt, out_dt, splits, partial, s);
-    case 1: return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, s);
-    case 2: return launch_tile<Tile256>(a, a_dt, out_dt, splits, partial, s);
-    case 3: return launch_tile<Tile128x256>(a, a_dt, out_dt, splits, partial, s);
+    case 0: return launch_tile<Tile128>(a, a_dt, out_dt, splits, partial, reduce, s);
+    case 1: return launch_tile<Tile64>(a, a_dt, out_dt, splits, partial, reduce, s);
+    case 2: return launch_tile<Tile256>(a, a_dt, out_dt, splits, partial, reduce, s);
+    case 3: return launch_tile<Tile128x256>(a, a_dt, out_dt, splits, partial, reduce, s);
   }
   return hipErrorInvalidValue;
 }

@@ -33,11 +33,14 @@ struct GemmArgs {
   int act = 0;                     // ActKind
 };
 
-// LDS-tiled MFMA GEMM.  tile: 0 = 128x128 block tile, 1 = 64x64.
+// LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
+// 3 = 128x256 block tile.
 // splits > 1 (dense only): K is split and fp32 partial tiles go to `partial`
-// ([splits][M][N] floats) before a fixed-order reduction.
+// ([splits][M][N] floats) before a fixed-order reduction (split 0 + split 1
+// + ...), which a second kernel performs unless reduce is false: then the
+// consumer adds the partials itself, in the same order.
 hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s,
-                             int splits = 1, float* partial = nullptr);
+                             int splits = 1, float* partial = nullptr, bool reduce = true);
 int tiled_block_m(int tile);
 // Grouped GEMM with OCP E4M3 weights (b_scale: one fp32 scale per weight
 // row), bf16 activations and output, LDS-tiled.
@@ -74,8 +77,25 @@ int ffn_stream_rows();
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s);
 
 // Routing.
-hipError_t launch_topk_gate(const float* logits, const float* bias, int T, int N, int K,
-                            int gating, int32_t* idx, float* gate, hipStream_t s);
+// Top-k selection and gates, one wave per token.  The logits may arrive as
+// the split-K partials of the router GEMM ([lsplits][T][N]), added here in
+// split order; the kernel can also finish the down-projection (its split-K
+// partials [usplits][T][l] added the same way, written to u), which no
+// earlier stage needs when the router reads x.
+struct TopkArgs {
+  const float* logits = nullptr;  // [lsplits][T][N]
+  int lsplits = 1;
+  float* logits_out = nullptr;    // reduced logits [T][N] (before the bias), or nullptr
+  const float* bias = nullptr;    // [N] or nullptr
+  int T = 0, N = 0, K = 0, gating = 0;
+  int32_t* idx = nullptr;         // [T][K]
+  float* gate = nullptr;          // [T][K]
+  const float* u_part = nullptr;  // [usplits][T][l] or nullptr
+  int usplits = 1, l = 0;
+  void* u = nullptr;              // [T][l], bf16 (u_bf16) or fp32
+  int u_bf16 = 1;
+};
+hipError_t launch_topk_gate(const TopkArgs& a, hipStream_t s);
 hipError_t launch_route_masks(const int32_t* idx, int T, int N, int K, uint64_t* masks,
                               hipStream_t s);
 hipError_t launch_route_scan(const uint64_t* masks, int nblk, int N, int tile_m, int32_t* counts,

@@ -39,29 +39,82 @@ __device__ __forceinline__ uint32_t order_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int NPL>
-__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits,
-                                                        const float* __restrict__ bias, int T,
-                                                        int N, int K, int gating,
-                                                        int32_t* __restrict__ idx,
-                                                        float* __restrict__ gate) {
+// Blocks past tok_blocks finish the down-projection instead: one 4-column
+// piece of u per thread, its split-K partials added in split order (the
+// order of the GEMM's own reduction kernel).  SPL > 1: the logits arrive in
+// at most SPL partial sets, all loaded before they are added in order.
+template <int NPL, int SPL>
+__global__ __launch_bounds__(256) void topk_gate_kernel(TopkArgs a, int tok_blocks) {
+  const int T = a.T, N = a.N, K = a.K;
+  if (static_cast<int>(blockIdx.x) >= tok_blocks) {
+    const int l4 = a.l / 4;
+    const int64_t q = (int64_t)(blockIdx.x - tok_blocks) * 256 + threadIdx.x;
+    if (q >= (int64_t)T * l4) return;
+    const int r = static_cast<int>(q / l4), c = static_cast<int>(q % l4) * 4;
+    const int64_t tl = (int64_t)T * a.l;
+    const float* pp = a.u_part + (int64_t)r * a.l + c;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(pp);
+    for (int z = 1; z < a.usplits; ++z) v += *reinterpret_cast<const f32x4_t*>(pp + z * tl);
+    if (a.u_bf16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.u) + (int64_t)r * a.l + c) =
+          uint2{uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16),
+                uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16)};
+    } else {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.u) + (int64_t)r * a.l + c) = v;
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole waves leave together
-  const float* zr = logits + (int64_t)t * N;
 
   // value i of this lane is expert 64 i + lane; loads are unconditional
-  // (clamped index) so they are all in flight together
+  // (clamped index) so they are all in flight together.  Split-K partials
+  // of the logits are added in split order.
+  const float* zr = a.logits + (int64_t)t * N;
+  const int64_t tn = (int64_t)T * N;
+  float zs[NPL];
+  if constexpr (SPL > 1) {
+    float pz[SPL][NPL];
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int e = i * 64 + lane;
+        const int ec = e < N ? e : N - 1;
+        pz[sp][i] = zr[(sp < a.lsplits ? sp : 0) * tn + ec];
+      }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      float v = pz[0][i];
+#pragma unroll
+      for (int sp = 1; sp < SPL; ++sp)
+        if (sp < a.lsplits) v += pz[sp][i];
+      zs[i] = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = i * 64 + lane;
+      const int ec = e < N ? e : N - 1;
+      float v = zr[ec];
+      for (int sp = 1; sp < a.lsplits; ++sp) v += zr[sp * tn + ec];
+      zs[i] = v;
+    }
+  }
   float z[NPL];
   uint32_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = i * 64 + lane;
     const int ec = e < N ? e : N - 1;
-    const float v = zr[ec] + (bias ? bias[ec] : 0.f);
+    float v = zs[i];
+    if (a.logits_out && e < N) a.logits_out[(int64_t)t * N + e] = v;
+    v += a.bias ? a.bias[ec] : 0.f;
     z[i] = e < N ? v : -INFINITY;
     key[i] = e < N ? order_key(v) : 0u;
   }
+  const int gating = a.gating;
 
   uint32_t taken = 0;  // bit i: value i already selected
   float my_z = 0.f;
@@ -113,8 +166,8 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
     g = ex / tot;
   }
   if (mine) {
-    idx[(int64_t)t * K + lane] = my_e;
-    gate[(int64_t)t * K + lane] = g;
+    a.idx[(int64_t)t * K + lane] = my_e;
+    a.gate[(int64_t)t * K + lane] = g;
   }
 }
 
@@ -394,19 +447,44 @@ bool route_small_fits(int T, int N, int K) {
          (int64_t)T * K <= kSmallRouteCopies;
 }
 
-hipError_t launch_topk_gate(const float* logits, const float* bias, int T, int N, int K,
-                            int gating, int32_t* idx, float* gate, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  if (N > 64 * kTopkMaxPerLane || K > 64 || K > N) return hipErrorInvalidValue;
-  const dim3 grid((T + 3) / 4), block(256);
+template <int NPL>
+void launch_topk_npl(const TopkArgs& a, int spl, dim3 grid, int tok_blocks, hipStream_t s) {
+  const dim3 block(256);
+  if constexpr (NPL * 16 <= 128)
+    if (spl == 16) return topk_gate_kernel<NPL, 16><<<grid, block, 0, s>>>(a, tok_blocks);
+  if constexpr (NPL * 8 <= 128)
+    if (spl == 8) return topk_gate_kernel<NPL, 8><<<grid, block, 0, s>>>(a, tok_blocks);
+  if constexpr (NPL * 4 <= 128)
+    if (spl == 4) return topk_gate_kernel<NPL, 4><<<grid, block, 0, s>>>(a, tok_blocks);
+  topk_gate_kernel<NPL, 1><<<grid, block, 0, s>>>(a, tok_blocks);
+}
+
+hipError_t launch_topk_gate(const TopkArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int N = a.N, K = a.K;
+  if (N > 64 * kTopkMaxPerLane || K > 64 || K > N || a.lsplits < 1 || !a.logits)
+    return hipErrorInvalidValue;
+  if (a.u_part && (a.usplits < 1 || a.l <= 0 || a.l % 4 || !a.u)) return hipErrorInvalidValue;
+  const int tok_blocks = (a.T + 3) / 4;
+  const int64_t u_blocks = a.u_part ? ((int64_t)a.T * (a.l / 4) + 255) / 256 : 0;
+  if (tok_blocks + u_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(tok_blocks + u_blocks));
   const int npl = (N + 63) / 64;
-  if (npl <= 1) topk_gate_kernel<1><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
-  else if (npl <= 2) topk_gate_kernel<2><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
-  else if (npl <= 4) topk_gate_kernel<4><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
-  else if (npl <= 8) topk_gate_kernel<8><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
-  else if (npl <= 14) topk_gate_kernel<14><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
-  else if (npl <= 16) topk_gate_kernel<16><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
-  else topk_gate_kernel<32><<<grid, block, 0, s>>>(logits, bias, T, N, K, gating, idx, gate);
+  // partial sets loaded at once: a power of two >= lsplits, at most 128
+  // values per lane
+  int spl = a.lsplits <= 1 ? 1 : a.lsplits <= 4 ? 4 : a.lsplits <= 8 ? 8 : a.lsplits <= 16 ? 16 : 1;
+  const int npl_c = npl <= 1 ? 1 : npl <= 2 ? 2 : npl <= 4 ? 4 : npl <= 8 ? 8 : npl <= 14 ? 14
+                    : npl <= 16 ? 16 : 32;
+  if (spl * npl_c > 128) spl = 1;
+  switch (npl_c) {
+    case 1: launch_topk_npl<1>(a, spl, grid, tok_blocks, s); break;
+    case 2: launch_topk_npl<2>(a, spl, grid, tok_blocks, s); break;
+    case 4: launch_topk_npl<4>(a, spl, grid, tok_blocks, s); break;
+    case 8: launch_topk_npl<8>(a, spl, grid, tok_blocks, s); break;
+    case 14: launch_topk_npl<14>(a, spl, grid, tok_blocks, s); break;
+    case 16: launch_topk_npl<16>(a, spl, grid, tok_blocks, s); break;
+    default: launch_topk_npl<32>(a, spl, grid, tok_blocks, s); break;
+  }
   return hipGetLastError();
 }
 
