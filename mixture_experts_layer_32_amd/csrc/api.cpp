@@ -133,6 +133,10 @@ struct Plan {
   // and the down-projection when the router reads x (nothing needs u before)
   bool defer_u = false, defer_z = false;
   size_t part_z = 0;    // byte offset of the router partials in the partial region
+  // router on x with split K: W_down and W_r in one launch over x (output
+  // columns 0..l-1 from W_down, l..l+N-1 from W_r), partials only
+  bool front = false;
+  DensePlan front_plan;
   size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, partial,
       total;
 };
@@ -172,6 +176,22 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.router = plan_dense(T, c.n_experts, r_in, ab, false);  // fp32 logits
   p.defer_u = c.has_projections && c.router_input == LMOE_ROUTER_ON_X && p.down.splits > 1;
   p.defer_z = p.router.splits > 1;
+  if (p.defer_u && p.defer_z) {
+    p.front_plan = plan_dense(T, c.l + c.n_experts, c.d, ab, false);
+    const int bn = p.front_plan.tile == 1 ? 64 : 128;  // column tile of plan_dense's tiles 0 / 1
+    p.front = p.front_plan.splits > 1 && p.front_plan.tile <= 1 && c.l % bn == 0;
+    if (p.front && p.front_plan.tile == 1) {
+      // about three 64 x 64 split tiles per compute unit (measured best for
+      // the decode shapes: one launch over x for both weight matrices)
+      const int64_t small = ((T + 63) / 64) * ((c.l + c.n_experts + 63) / 64);
+      const int64_t stages = (c.d * int64_t(ab) + 127) / 128;
+      int64_t sp = (3 * kComputeUnits + small - 1) / small;
+      sp = std::min<int64_t>({sp, std::max<int64_t>(2, stages / 8), 16});
+      p.front_plan.splits = static_cast<int>(std::max<int64_t>(2, sp));
+    }
+    if (p.front)
+      partial = std::max(partial, size_t(p.front_plan.splits) * T * (c.l + c.n_experts) * 4);
+  }
   const size_t router_part = size_t(p.router.splits > 1 ? p.router.splits : 0) * T * c.n_experts * 4;
   if (p.defer_u) {  // both partial sets live until the top-k kernel
     p.part_z = align_up(size_t(p.down.splits) * T * c.l * 4);
@@ -412,14 +432,23 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   // ---- stage 0: down-projection and router logits (split-K partials that
   // the top-k kernel adds when deferred)
   float* part_z = reinterpret_cast<float*>(ws + p.partial + p.part_z);
-  if (c.has_projections) {
+  const int64_t front_ld = l + N;
+  if (p.front) {
+    lmoe::GemmArgs a;
+    a.A = x; a.lda = d; a.B = w->w_down; a.B2 = w->w_router; a.N0 = static_cast<int>(l);
+    a.ldb = d; a.ldc = front_ld;
+    a.M = Ti; a.N = static_cast<int>(front_ld); a.K = d;
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, lmoe::Dt::F32, p.front_plan.tile, s,
+                                     p.front_plan.splits, partial, false),
+             "W_down + router GEMM");
+  } else if (c.has_projections) {
     lmoe::GemmArgs a;
     a.A = x; a.lda = d; a.B = w->w_down; a.ldb = d; a.C = u; a.ldc = l;
     a.M = Ti; a.N = l; a.K = d;
     LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial, !p.defer_u),
              "W_down GEMM");
   }
-  {
+  if (!p.front) {
     const bool lat = c.router_input == LMOE_ROUTER_ON_LATENT;
     lmoe::GemmArgs a;
     a.A = lat ? u : x; a.lda = lat ? l : d;
@@ -434,14 +463,20 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   // ---- stage 1: top-k and gates (and the deferred split-K reductions)
   {
     lmoe::TopkArgs a;
-    a.logits = p.defer_z ? part_z : logits;
-    a.lsplits = p.defer_z ? p.router.splits : 1;
+    a.logits = p.front ? partial + l : p.defer_z ? part_z : logits;
+    a.logits_ld = p.front ? front_ld : N;
+    a.logits_sstride = int64_t(Ti) * a.logits_ld;
+    a.lsplits = p.front ? p.front_plan.splits : p.defer_z ? p.router.splits : 1;
     a.logits_out = p.defer_z && dbg && dbg->logits ? logits : nullptr;
     a.bias = c.has_router_bias ? w->router_bias : nullptr;
     a.T = Ti; a.N = N; a.K = K; a.gating = c.gating;
     a.idx = idx; a.gate = gate;
     if (p.defer_u) {
-      a.u_part = partial; a.usplits = p.down.splits; a.l = static_cast<int>(l);
+      a.u_part = partial;
+      a.u_ld = p.front ? front_ld : l;
+      a.u_sstride = int64_t(Ti) * a.u_ld;
+      a.usplits = p.front ? p.front_plan.splits : p.down.splits;
+      a.l = static_cast<int>(l);
       a.u = u; a.u_bf16 = adt == lmoe::Dt::BF16;
     }
     LMOE_TRY(lmoe::launch_topk_gate(a, s), "top-k");

@@ -170,9 +170,21 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
 
   const TA* A = static_cast<const TA*>(p.A);
   const TB* B = static_cast<const TB*>(p.B) + (int64_t)g * p.b_gstride;
+  // columns from the second weight matrix: this tile's rows of B are
+  // bn0 .. of B2 (the host keeps N0 a multiple of BN)
+  int bn0 = 0, bN = p.N;
+  if (p.B2) {
+    if (col0 >= p.N0) {
+      B = static_cast<const TB*>(p.B2);
+      bn0 = p.N0;
+      bN = p.N - p.N0;
+    } else {
+      bN = p.N0;
+    }
+  }
   const uint64_t a_rows_total = p.g_off ? (uint64_t)p.a_nrows : (uint64_t)p.M;
   const BufRsrc a_rsrc = make_rsrc(A, a_rows_total * p.lda * sizeof(TA));
-  const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)p.N * p.ldb * sizeof(TB));
+  const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)bN * p.ldb * sizeof(TB));
 
   // ---- LDS-mode staging.  Stage buffer position q (16-byte chunks): A row
   // q / BKC for q < ACH, else B row (q - ACH) / BKCB; within a row, logical
@@ -195,9 +207,9 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
       const int r = (q - ACH) / BKCB;
       const int c = ((q - ACH) % BKCB) ^ lds_swz<BKCB>(r);
       d_k[j] = c * EPCB;
-      const int n = col0 + r;
-      d_off[j] = n < p.N ? static_cast<uint32_t>((int64_t)n * p.ldb * sizeof(TB)) + c * 16u
-                         : kOutOfRange;
+      const int n = col0 - bn0 + r;
+      d_off[j] = n < bN ? static_cast<uint32_t>((int64_t)n * p.ldb * sizeof(TB)) + c * 16u
+                        : kOutOfRange;
     }
   }
   // stage kt -> ring buffer kt % NSTAGE, always NDMA loads per thread
@@ -423,6 +435,10 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
   const bool scale = a.b_scale != nullptr;
   float* part = splits > 1 ? partial : nullptr;
   if (part && BM * BN > 128 * 128) return hipErrorInvalidValue;  // partial tile must fit LDS
+  // two weight matrices: dense, whole column tiles each, partials only
+  if (a.B2 && (a.g_off || a.N0 <= 0 || a.N0 >= a.N || a.N0 % BN || !part || reduce ||
+               (uint64_t)a.N0 * a.ldb * sizeof(TB) >= (1ull << 31)))
+    return hipErrorInvalidValue;
   if (a.act == kActSqRelu) {
     if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
     else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);

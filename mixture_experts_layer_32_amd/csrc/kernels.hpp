@@ -31,6 +31,11 @@ struct GemmArgs {
   int G = 1;
   int max_rows = 0;                // grouped: upper bound of the total rows (sizes the grid)
   int act = 0;                     // ActKind
+  // dense only: output columns n >= N0 take row n - N0 of B2 instead of B
+  // (two weight matrices over the same A in one launch; N0 a multiple of
+  // the column tile, split-K partial output only)
+  const void* B2 = nullptr;
+  int N0 = 0;
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
@@ -83,14 +88,16 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s);
 // partials [usplits][T][l] added the same way, written to u), which no
 // earlier stage needs when the router reads x.
 struct TopkArgs {
-  const float* logits = nullptr;  // [lsplits][T][N]
+  const float* logits = nullptr;  // split z, token t, expert e at z*logits_sstride + t*logits_ld + e
+  int64_t logits_ld = 0, logits_sstride = 0;
   int lsplits = 1;
   float* logits_out = nullptr;    // reduced logits [T][N] (before the bias), or nullptr
   const float* bias = nullptr;    // [N] or nullptr
   int T = 0, N = 0, K = 0, gating = 0;
   int32_t* idx = nullptr;         // [T][K]
   float* gate = nullptr;          // [T][K]
-  const float* u_part = nullptr;  // [usplits][T][l] or nullptr
+  const float* u_part = nullptr;  // split z, token t, column c at z*u_sstride + t*u_ld + c
+  int64_t u_ld = 0, u_sstride = 0;
   int usplits = 1, l = 0;
   void* u = nullptr;              // [T][l], bf16 (u_bf16) or fp32
   int u_bf16 = 1;

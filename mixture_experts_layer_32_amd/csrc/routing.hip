@@ -51,10 +51,9 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(TopkArgs a, int tok_bloc
     const int64_t q = (int64_t)(blockIdx.x - tok_blocks) * 256 + threadIdx.x;
     if (q >= (int64_t)T * l4) return;
     const int r = static_cast<int>(q / l4), c = static_cast<int>(q % l4) * 4;
-    const int64_t tl = (int64_t)T * a.l;
-    const float* pp = a.u_part + (int64_t)r * a.l + c;
+    const float* pp = a.u_part + (int64_t)r * a.u_ld + c;
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(pp);
-    for (int z = 1; z < a.usplits; ++z) v += *reinterpret_cast<const f32x4_t*>(pp + z * tl);
+    for (int z = 1; z < a.usplits; ++z) v += *reinterpret_cast<const f32x4_t*>(pp + z * a.u_sstride);
     if (a.u_bf16) {
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.u) + (int64_t)r * a.l + c) =
           uint2{uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16),
@@ -71,8 +70,8 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(TopkArgs a, int tok_bloc
   // value i of this lane is expert 64 i + lane; loads are unconditional
   // (clamped index) so they are all in flight together.  Split-K partials
   // of the logits are added in split order.
-  const float* zr = a.logits + (int64_t)t * N;
-  const int64_t tn = (int64_t)T * N;
+  const float* zr = a.logits + (int64_t)t * a.logits_ld;
+  const int64_t tn = a.logits_sstride;
   float zs[NPL];
   if constexpr (SPL > 1) {
     float pz[SPL][NPL];
@@ -464,7 +463,10 @@ hipError_t launch_topk_gate(const TopkArgs& a, hipStream_t s) {
   const int N = a.N, K = a.K;
   if (N > 64 * kTopkMaxPerLane || K > 64 || K > N || a.lsplits < 1 || !a.logits)
     return hipErrorInvalidValue;
-  if (a.u_part && (a.usplits < 1 || a.l <= 0 || a.l % 4 || !a.u)) return hipErrorInvalidValue;
+  if (a.u_part && (a.usplits < 1 || a.l <= 0 || a.l % 4 || !a.u || a.u_ld % 4 || a.u_ld < a.l))
+    return hipErrorInvalidValue;
+  if (a.logits_ld < N || (a.lsplits > 1 && a.logits_sstride < (int64_t)a.T * a.logits_ld))
+    return hipErrorInvalidValue;
   const int tok_blocks = (a.T + 3) / 4;
   const int64_t u_blocks = a.u_part ? ((int64_t)a.T * (a.l / 4) + 255) / 256 : 0;
   if (tok_blocks + u_blocks > 0x7fffffff) return hipErrorInvalidValue;
