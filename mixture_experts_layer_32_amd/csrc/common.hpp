@@ -75,6 +75,15 @@ __device__ __forceinline__ void buffer_load_chunk_lds(BufRsrc r, u32x4* lds, uin
       static_cast<int>(voff), 0, 0, 0);
 }
 
+// LDS-only barrier: this wave's LDS operations are complete and every wave
+// of the workgroup has arrived.  Global loads and stores in flight are not
+// waited for (an LDS-scoped fence around s_barrier).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt untouched).  gfx9 encoding: vmcnt
 // bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>

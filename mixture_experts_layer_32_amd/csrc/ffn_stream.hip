@@ -84,12 +84,6 @@ struct FfnUnit {
   }
 };
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   __shared__ u32x4 Hs[kRows * kMaxM / 8];  // H, 16-byte chunk c of row r at c ^ (r & 7)
   __shared__ u32x4 As[2][kAChunks];        // FC1 token stages, chunk c of row r at c ^ ((r >> 1) & 7)
@@ -354,21 +348,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   }
 }
 
-// compute units of the current device (cached per device)
-int ffn_device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 }  // namespace
 
 bool ffn_stream_fits(int l, int m) {
@@ -385,7 +364,7 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s) {
   if ((uint64_t)a.a_nrows * a.lda * 2u >= (1ull << 31) ||
       (uint64_t)a.m * a.l * 2u >= (1ull << 31))
     return hipErrorInvalidValue;
-  const int grid = std::min(a.G, ffn_device_cus());
+  const int grid = std::min(a.G, device_compute_units());
   ffn_stream_kernel<<<dim3(grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }

@@ -132,14 +132,6 @@ struct Unit {
   }
 };
 
-// LDS-only barrier: this wave's LDS operations are complete and every wave
-// has arrived.  Global loads and stores in flight are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 #ifndef LMOE_STREAM_OCC
 #define LMOE_STREAM_OCC 2
 #endif
@@ -404,21 +396,6 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
 #define LMOE_STREAM_NWB_MB8 1
 #endif
 
-// compute units of the current device (cached per device)
-int device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 template <typename Mma, typename TA, typename TW, typename TOut, int MB>
 hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   constexpr int NWB = MB >= 8 ? LMOE_STREAM_NWB_MB8 : LMOE_STREAM_NWB;
@@ -439,7 +416,7 @@ hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   // persistent grid: the resident workgroups, a multiple of the XCD count,
   // no more per XCD than it has work items
   const int64_t per_xcd = (total + kNumXcd - 1) / kNumXcd;
-  const int64_t slots = std::max<int64_t>(1, (int64_t)kStreamOcc * device_cus() / kNumXcd);
+  const int64_t slots = std::max<int64_t>(1, (int64_t)kStreamOcc * device_compute_units() / kNumXcd);
   const int64_t grid = std::min(per_xcd, slots) * kNumXcd;
   const bool scale = a.b_scale != nullptr;
   if (a.act == kActSqRelu) {
@@ -465,6 +442,20 @@ hipError_t launch_mb(const GemmArgs& a, Dt a_dt, Dt w_dt, Dt out_dt, hipStream_t
 }
 
 }  // namespace
+
+int device_compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 hipError_t launch_gemm_stream(const GemmArgs& a, Dt a_dt, Dt w_dt, Dt out_dt, int mb_max,
                               hipStream_t s) {

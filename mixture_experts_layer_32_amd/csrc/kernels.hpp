@@ -52,6 +52,10 @@ int tiled_block_m(int tile);
 hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s);
 int tiled_block_m_fp8w();
 
+// Compute units of the current device (queried once per device; 256 on
+// MI355X), for persistent grids.
+int device_compute_units();
+
 // Weight-streaming grouped GEMM for few rows per group (decode regime):
 // every group's weight matrix is streamed from HBM once per pass of up to
 // mrows_max rows.  mb_max: 4 or 8 (rows per pass = 16 * mb_max).

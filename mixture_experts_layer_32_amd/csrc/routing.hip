@@ -21,6 +21,8 @@
 //                LDS (decode-sized batches).
 //  combine       v[t] = sum_j gate[t][j] * Y[slot_of[t][j]] in fp32, fixed
 //                j order (deterministic), rounded once to the output dtype.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -384,15 +386,14 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
 }
 
 // One workgroup per token; thread c handles 16 bytes of the output row.  The
-// K expert rows are fetched 32 at a time (independent loads in flight)
-// and added in j order.
-template <typename T>
-__global__ __launch_bounds__(128) void combine_kernel(const T* __restrict__ Y,
+// K expert rows are fetched U (8, 16 or 32, the smallest >= K) at a time
+// (independent loads in flight) and added in j order.
+template <typename T, int U>
+__global__ __launch_bounds__(512) void combine_kernel(const T* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gate, int K, int l,
                                                       T* __restrict__ v) {
   constexpr int EPC = 16 / sizeof(T);
-  constexpr int U = 32;
   const int t = blockIdx.x;
   const int32_t* so = slot_of + (int64_t)t * K;
   const float* gt = gate + (int64_t)t * K;
@@ -527,15 +528,26 @@ hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_
   return hipGetLastError();
 }
 
+template <typename T>
+void launch_combine_t(const T* Y, const int32_t* slot_of, const float* gate, int T_, int K, int l,
+                      T* v, hipStream_t s) {
+  // one thread per 16-byte chunk of the row (up to 512 threads, then a
+  // loop); as many expert rows in flight as the token has (8, 16 or 32)
+  const int chunks = l / (16 / static_cast<int>(sizeof(T)));
+  const dim3 grid(T_), block(std::min(512, (chunks + 63) / 64 * 64));
+  if (K <= 8) combine_kernel<T, 8><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, v);
+  else if (K <= 16) combine_kernel<T, 16><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, v);
+  else combine_kernel<T, 32><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, v);
+}
+
 hipError_t launch_combine(const void* Y, const int32_t* slot_of, const float* gate, int T, int K,
                           int l, Dt dt, void* v, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (dt == Dt::BF16)
-    combine_kernel<uint16_t><<<dim3(T), dim3(128), 0, s>>>(static_cast<const uint16_t*>(Y), slot_of,
-                                                          gate, K, l, static_cast<uint16_t*>(v));
+    launch_combine_t(static_cast<const uint16_t*>(Y), slot_of, gate, T, K, l,
+                     static_cast<uint16_t*>(v), s);
   else
-    combine_kernel<float><<<dim3(T), dim3(128), 0, s>>>(static_cast<const float*>(Y), slot_of, gate,
-                                                       K, l, static_cast<float*>(v));
+    launch_combine_t(static_cast<const float*>(Y), slot_of, gate, T, K, l, static_cast<float*>(v), s);
   return hipGetLastError();
 }
 
