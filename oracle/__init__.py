@@ -6,7 +6,7 @@ or calls it, and the two share no code; the seeded input generator
 (``synth``) is the only module both sides use.
 
 The layer (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter in
-Mixture of Experts, §3 Eq. (1)/(2), routed term only) is evaluated token by
+Mixture of Experts, §3 Eq. (1)/(2), routed and shared terms) is evaluated token by
 token in plain C (``latentmoe_oracle.c``), in fp64, with OpenMP over tokens.
 The closed forms of the paper's cost model are in ``cost_model.py``.
 
@@ -40,14 +40,16 @@ class _Layer(ctypes.Structure):
                 ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
                 ("router_on_latent", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("has_projections", ctypes.c_int32), ("has_router_bias", ctypes.c_int32),
-                ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
+                ("n_shared", ctypes.c_int64), ("m_shared", ctypes.c_int64)]
 
 
 class _Weights(ctypes.Structure):
     _fields_ = [("w_down", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
                 ("router_bias", ctypes.c_void_p), ("w1", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
-                ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p)]
+                ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p)]
 
 
 def build(force: bool = True) -> str:
@@ -89,13 +91,15 @@ def _p(a):
 def _layer(spec) -> _Layer:
     return _Layer(spec.d, spec.l, spec.m, spec.n_experts, spec.top_k,
                   int(spec.router_on_latent), _GATE[spec.gating], int(spec.has_projections),
-                  int(spec.has_router_bias), _DT[spec.act_dtype], _DT[spec.expert_dtype])
+                  int(spec.has_router_bias), _DT[spec.act_dtype], _DT[spec.expert_dtype],
+                  spec.n_shared, spec.m_shared)
 
 
 def _weights(w: dict):
     keep = {k: np.ascontiguousarray(v) for k, v in w.items()}
     cw = _Weights(*(_p(keep.get(k)) for k in ("w_down", "w_router", "router_bias", "w1", "w2",
-                                               "w1_scale", "w2_scale", "w_up")))
+                                               "w1_scale", "w2_scale", "w_up",
+                                               "w_shared1", "w_shared2")))
     return cw, keep
 
 

@@ -8,7 +8,8 @@
  * routing weights p' = Softmax(W'_r x) from the d-dimensional x; top-K set
  * T_{K,N'}) and Eq. (1)/(2).  The expert nonlinearity is the non-gated
  * Squared-ReLU FFN, W_FC2 . (max(0, W_FC1 . u))^2 (Table 2 lists Squared-ReLU
- * for the 4096-wide models).
+ * for the 4096-wide models).  The shared experts E_j(x; d) of Eq. (1)/(2)
+ * are the same FFN on x in the d space, added to the output ungated.
  */
 #define _GNU_SOURCE /* qsort_r */
 #include "latentmoe_oracle.h"
@@ -70,6 +71,8 @@ static int check(const orc_layer *L, const orc_weights *W, const void *x, int64_
   if (L->expert_dtype == ORC_FP8_E4M3_ROWSCALE && (!W->w1_scale || !W->w2_scale)) return -1;
   if (L->act_dtype != ORC_F32 && L->act_dtype != ORC_BF16) return -1;
   if (L->gating < 0 || L->gating > 2) return -1;
+  if (L->n_shared < 0) return -1;
+  if (L->n_shared > 0 && (L->m_shared <= 0 || !W->w_shared1 || !W->w_shared2)) return -1;
   return 0;
 }
 
@@ -139,6 +142,26 @@ static void up_project(const orc_layer *L, const orc_weights *W, const double *v
   }
 }
 
+/* out += sum_j E_j(x; d): the S shared experts, evaluated as one
+ * concatenated FFN: hs[j*ms + r] = (max(0, Ws1[j*ms + r] . x))^2, then
+ * out[r] += sum_k Ws2[r][k] hs[k] over k = 0 .. S*ms-1 in ascending order
+ * (expert j's terms are the k in [j*ms, (j+1)*ms)). */
+static void add_shared(const orc_layer *L, const orc_weights *W, const double *xt, double *hs,
+                       double *out) {
+  const int64_t d = L->d, H = L->n_shared * L->m_shared;
+  for (int64_t k = 0; k < H; ++k) {
+    double s = 0.0;
+    for (int64_t c = 0; c < d; ++c) s += ld(W->w_shared1, L->act_dtype, k * d + c, NULL, 0) * xt[c];
+    double a = s > 0.0 ? s : 0.0;
+    hs[k] = a * a;
+  }
+  for (int64_t r = 0; r < d; ++r) {
+    double s = 0.0;
+    for (int64_t k = 0; k < H; ++k) s += ld(W->w_shared2, L->act_dtype, r * H + k, NULL, 0) * hs[k];
+    out[r] += s;
+  }
+}
+
 /* order: (z desc, id asc) */
 static int cmp_desc(const void *a, const void *b, void *zv) {
   const double *z = (const double *)zv;
@@ -199,7 +222,8 @@ int orc_forward(const orc_layer *L, const orc_weights *W, const void *x, const i
     int32_t *ord = malloc(sizeof(int32_t) * (size_t)N);
     int32_t *asc = malloc(sizeof(int32_t) * (size_t)K);
     double *g = malloc(sizeof(double) * (size_t)K);
-    const int ok = xt && u && z && h && y && v && ord && asc && g;
+    double *hs = malloc(sizeof(double) * (size_t)(L->n_shared * L->m_shared + 1));
+    const int ok = xt && u && z && h && y && v && ord && asc && g && hs;
     /* every thread reaches the worksharing loop; one without buffers only flags */
 #pragma omp for schedule(dynamic, 1)
       for (int64_t i = 0; i < n; ++i) {
@@ -230,8 +254,10 @@ int orc_forward(const orc_layer *L, const orc_weights *W, const void *x, const i
           for (int64_t c = 0; c < l; ++c) v[c] += g[j] * y[c];
         }
         up_project(L, W, v, out + i * d);
+        if (L->n_shared) add_shared(L, W, xt, hs, out + i * d);
       }
     free(xt); free(u); free(z); free(h); free(y); free(v); free(ord); free(asc); free(g);
+    free(hs);
   }
   return bad ? -1 : 0;
 }
@@ -251,7 +277,9 @@ int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
     double *v = malloc(sizeof(double) * (size_t)l);
     int32_t *sel = malloc(sizeof(int32_t) * (size_t)K);
     double *g = malloc(sizeof(double) * (size_t)K);
-    const int ok = xt && u && z && h && y && v && sel && g;
+    double *hs = malloc(sizeof(double) * (size_t)(L->m_shared > 0 ? L->m_shared : 1));
+    double *ys = malloc(sizeof(double) * (size_t)d);
+    const int ok = xt && u && z && h && y && v && sel && g && hs && ys;
 #pragma omp for schedule(dynamic, 1)
       for (int64_t i = 0; i < n; ++i) {
         if (!ok) {
@@ -279,8 +307,25 @@ int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
         for (int64_t e = 0; e < N; ++e)
           for (int64_t c = 0; c < l; ++c) v[c] += G[e] * y[e * l + c];
         up_project(L, W, v, out + i * d);
+        /* each shared expert on its own: ys = E_j(x; d), then out += ys */
+        const int64_t ms = L->m_shared, H = L->n_shared * ms;
+        for (int64_t j = 0; j < L->n_shared; ++j) {
+          for (int64_t r = 0; r < ms; ++r) {
+            double s = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+              s += ld(W->w_shared1, L->act_dtype, (j * ms + r) * d + c, NULL, 0) * xt[c];
+            hs[r] = s > 0.0 ? s * s : 0.0;
+          }
+          for (int64_t r = 0; r < d; ++r) {
+            double s = 0.0;
+            for (int64_t c = 0; c < ms; ++c)
+              s += ld(W->w_shared2, L->act_dtype, r * H + j * ms + c, NULL, 0) * hs[c];
+            ys[r] = s;
+          }
+          for (int64_t r = 0; r < d; ++r) out[i * d + r] += ys[r];
+        }
       }
-    free(xt); free(u); free(z); free(h); free(y); free(v); free(sel); free(g);
+    free(xt); free(u); free(z); free(h); free(y); free(v); free(sel); free(g); free(hs); free(ys);
   }
   return bad ? -1 : 0;
 }

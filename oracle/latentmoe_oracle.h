@@ -6,8 +6,7 @@
  * it, and it shares no source with the GPU library.
  *
  * What it computes (LatentMoE: Toward Optimal Accuracy per FLOP and
- * Parameter in Mixture of Experts, §3, Eq. (1) and Eq. (2), without the
- * shared-expert term):
+ * Parameter in Mixture of Experts, §3, Eq. (1) and Eq. (2)):
  *
  *   u      = W_down . x                     (u = x for the standard MoE)
  *   z      = W_r . x  (or W_r . u)  [+ b]   router logits
@@ -15,6 +14,12 @@
  *   g_i    = gate of expert i in T           (three gating rules, below)
  *   v      = sum_{i in T, ascending i} g_i * W2_i . (max(0, W1_i . u))^2
  *   out    = W_up . v                        (out = v for the standard MoE)
+ *            + sum_{j < S} Ws2_j . (max(0, Ws1_j . x))^2   shared experts
+ *
+ * The S shared experts run on x in the d space, ungated (the second sum of
+ * Eq. (1)/(2)); their nonlinearity is the routed experts' Squared-ReLU FFN
+ * and their hidden width m_shared is a free parameter (the paper gives no
+ * separate width for them).  S = 0 drops the term.
  *
  * Gating rules: 0 = softmax over all N logits, gate = p_i of the selected
  * experts with no renormalisation (Eq. (1)); 1 = softmax over the K selected
@@ -44,17 +49,22 @@ typedef struct {
   int32_t has_router_bias;
   int32_t act_dtype;         /* ORC_F32 | ORC_BF16: x, W_down, W_router, W_up */
   int32_t expert_dtype;      /* ORC_F32 | ORC_BF16 | ORC_FP8_E4M3_ROWSCALE: W1, W2 */
+  int64_t n_shared;          /* S >= 0 shared experts */
+  int64_t m_shared;          /* their hidden width (> 0 when S > 0) */
 } orc_layer;
 
 /* Host pointers, row-major [out][in]: w_down [l][d], w_router [N][d or l],
  * router_bias [N] fp32, w1 [N][m][l], w2 [N][l][m], w1_scale [N][m],
- * w2_scale [N][l] (fp8 only), w_up [d][l]. */
+ * w2_scale [N][l] (fp8 only), w_up [d][l]; shared experts in the activation
+ * dtype: w_shared1 [S*m_shared][d] (expert j owns rows j*m_shared ..),
+ * w_shared2 [d][S*m_shared] (expert j owns columns j*m_shared ..). */
 typedef struct {
   const void *w_down, *w_router;
   const float *router_bias;
   const void *w1, *w2;
   const float *w1_scale, *w2_scale;
   const void *w_up;
+  const void *w_shared1, *w_shared2;
 } orc_weights;
 
 /* Sparse forward (the definition).  x holds all tokens ([*][d], act dtype).

@@ -7,7 +7,8 @@ both the fp64 oracle (``oracle/``) and the GPU library's tests and benchmark
 use, so that both sides see bit-identical inputs.
 
 Tensor stream ids: x = 0, W_down = 1, W_router = 2, W1 = 3, W2 = 4, W_up = 5,
-router-bias permutation = 6.  Every weight ~ N(0, 1/fan_in); x ~ N(0, 1).
+router-bias permutation = 6, shared W1 = 7, shared W2 = 8.  Every weight
+~ N(0, 1/fan_in); x ~ N(0, 1).
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lock = threading.Lock()
 _lib = None
 
-TID_X, TID_WDOWN, TID_WROUTER, TID_W1, TID_W2, TID_WUP, TID_BIAS = range(7)
+TID_X, TID_WDOWN, TID_WROUTER, TID_W1, TID_W2, TID_WUP, TID_BIAS, TID_WS1, TID_WS2 = range(9)
 
 
 def build(force: bool = True) -> str:
@@ -164,4 +165,10 @@ def make_weights(spec: LayerSpec, seed: int = 0) -> dict:
     else:
         w["w1"] = normal(seed, TID_W1, (N, m, l), l ** -0.5, spec.expert_dtype)
         w["w2"] = normal(seed, TID_W2, (N, l, m), m ** -0.5, spec.expert_dtype)
+    if spec.n_shared:
+        # shared experts, in the activation dtype: w_shared1 [S*ms][d] (expert
+        # j's rows j*ms ..), w_shared2 [d][S*ms] (expert j's columns j*ms ..)
+        S, ms = spec.n_shared, spec.m_shared
+        w["w_shared1"] = normal(seed, TID_WS1, (S * ms, d), d ** -0.5, act)
+        w["w_shared2"] = normal(seed, TID_WS2, (d, S * ms), ms ** -0.5, act)
     return w

@@ -32,6 +32,8 @@ class LayerSpec:
     has_router_bias: bool = False
     identity_projections: bool = False   # W_down = W_up = I (needs l == d)
     zipf_s: float = 1.1                  # exponent of the log-Zipf router bias
+    n_shared: int = 0                    # shared experts S (Eq. (1)/(2)), in the d space
+    m_shared: int = 0                    # their hidden width
 
     def __post_init__(self):
         assert self.gating in GATINGS, self.gating
