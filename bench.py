@@ -3,7 +3,8 @@
 
 One step = one full layer forward (all stages: W_down + router GEMMs, top-k
 and gates, dispatch indices, grouped FC1 + squared ReLU, grouped FC2,
-combine, W_up) over one batch of synthetic tokens already resident in HBM.
+combine, W_up, and the shared experts when the workload has them, by default
+on a side stream) over one batch of synthetic tokens already resident in HBM.
 Prints one JSON line: tokens/s (value), ms per step, the roofline of the
 dominant kernel (from HIP events recorded on the launch stream around each
 stage) and the fp64 CPU oracle's throughput on a bounded token sample.
@@ -62,8 +63,9 @@ def layer_work(spec, T, counts):
     experts that received tokens, projections and router read once, x read
     once, out written once (permuted copies, H, Y and logits are
     intermediates a fused implementation keeps on chip, so they are not
-    counted); FLOPs 2*T*d*l per projection, 2*T*r_in*N for the router and
-    4*T*K*l*m for the experts."""
+    counted); FLOPs 2*T*d*l per projection, 2*T*r_in*N for the router,
+    4*T*K*l*m for the routed experts and 4*T*d*S*m_s for the shared ones
+    (whose weights, 2*d*S*m_s elements, are read once)."""
     d, l, m, N, K = spec.d, spec.l, spec.m, spec.n_experts, spec.top_k
     a, eb = spec.act_bytes, spec.expert_bytes
     r_in = l if spec.router_on_latent else d
@@ -78,6 +80,9 @@ def layer_work(spec, T, counts):
     if spec.has_projections:
         nbytes += 2.0 * l * d * a
         flops += 4.0 * T * d * l
+    hs = spec.n_shared * spec.m_shared
+    nbytes += 2.0 * d * hs * a
+    flops += 4.0 * T * d * hs
     return nbytes, flops
 
 
@@ -109,6 +114,8 @@ def main():
     ap.add_argument("--workload", default="latent_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--overlap", choices=("on", "off"), default="on",
+                    help="shared experts on a side stream (on) or first on the launch stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known HBM traffic: "
                          "1 GiB read + 1 GiB written per launch) to scale rocprofv3 "
@@ -153,10 +160,11 @@ def main():
     out = torch.empty((T, spec.d), dtype=act, device=dev)
     ws = torch.empty((layer.workspace_size(T),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    overlap = pkg.Overlap(device=dev) if spec.n_shared and args.overlap == "on" else None
 
     def step(timer=None, debug=None):
         layer.forward(x, None, out=out, workspace=ws, cweights=cw, stream=stream, timer=timer,
-                      debug=debug)
+                      debug=debug, overlap=overlap)
 
     dbg = {"expert_counts": torch.empty((spec.n_experts,), dtype=torch.int32, device=dev)}
     step(debug=dbg)
@@ -263,12 +271,27 @@ def main():
         "data": "synthetic (seeded normals, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name, "T": T, "d": spec.d, "l": spec.l, "m": spec.m,
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "gating": spec.gating,
-                   "expert_dtype": spec.expert_dtype, "parallelism": "single GPU"},
+                   "expert_dtype": spec.expert_dtype, "parallelism": "single GPU",
+                   "n_shared": spec.n_shared, "m_shared": spec.m_shared,
+                   "shared_on_side_stream": overlap is not None},
         "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
         "latency_ms": {k: round(v, 5) for k, v in pct.items()},
         "roofline": roof,
         "layer_roofline": layer_roof,
     }
+    if spec.n_shared:
+        # the shared experts' two dense GEMMs (their stage's events, on the
+        # stream they ran on; beside the routed path they share the GPU)
+        hs = spec.n_shared * spec.m_shared
+        sf = 4.0 * T * spec.d * hs
+        sb = 2.0 * spec.d * hs * spec.act_bytes + T * spec.d * spec.act_bytes + \
+            2.0 * T * hs * spec.act_bytes + T * spec.d * 4.0
+        t_sh = stage_avg["shared"] * 1e-3
+        res["shared_stage"] = {"ms": round(stage_avg["shared"], 5),
+                               "algorithmic_flops": sf, "algorithmic_bytes": sb,
+                               "tflops": round(sf / t_sh / 1e12, 2) if t_sh > 0 else None,
+                               "mfma_frac": round(sf / t_sh / (mfma_peak * 1e12), 4)
+                               if t_sh > 0 else None}
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 CPU oracle")
         res["cpu_baseline"] = cpu_baseline(spec, w_np, x_np, args.cpu_budget)

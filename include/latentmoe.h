@@ -2,19 +2,22 @@
  * latentmoe.h -- C ABI of the MI355X (gfx950) LatentMoE layer forward.
  *
  * The operation (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter
- * in Mixture of Experts, §3, Eq. (1) and Eq. (2), routed-expert term):
+ * in Mixture of Experts, §3, Eq. (1) and Eq. (2)):
  *
  *   u   = W_down . x                    latent token, W_down in R^{l x d}
  *   z   = W_r . x   (or W_r . u) [+ b]  router logits over N experts, fp32
  *   T   = K experts with the largest z  ties go to the lower expert id
  *   v   = sum_{i in T} g_i E_i(u; l)    E_i(u) = W2_i . (max(0, W1_i . u))^2,
  *                                       W1_i in R^{m x l}, W2_i in R^{l x m}
- *   out = W_up . v                      W_up in R^{d x l}
+ *   out = W_up . v + sum_{j < S} E_j(x; d)       W_up in R^{d x l}
+ *
+ * The S shared experts (the second sum of Eq. (1)/(2)) run on x in the d
+ * space, ungated, with the routed experts' nonlinearity:
+ * E_j(x; d) = Ws2_j . (max(0, Ws1_j . x))^2, Ws1_j in R^{m_shared x d},
+ * Ws2_j in R^{d x m_shared}.  S = 0 leaves them out.
  *
  * With has_projections == 0 the layer is the standard MoE (l == d, u = x,
- * out = v): the same code path with the two projections skipped.  The
- * paper's shared experts (the second sum of Eq. (1)) are not part of this
- * call.
+ * out = v + shared): the same code path with the two projections skipped.
  *
  * Conventions
  *  - Every tensor is row-major "[out][in]" (y = W . x), dense, with the
@@ -28,6 +31,8 @@
  *    kernels on `stream` (a hipStream_t passed as void*, NULL = the null
  *    stream) and returns; it never synchronises the host, never allocates
  *    device memory and never copies data to the host.
+ *    latentmoe_forward_overlap may also use a second stream for the shared
+ *    experts; the call's outputs are still ordered on `stream`.
  *  - Errors are returned as lmoe_status, never thrown; on a non-OK status
  *    nothing has been enqueued except for LMOE_ERR_HIP (a launch failed
  *    part-way; the stream's outputs are then undefined).
@@ -105,6 +110,8 @@ typedef struct {
   int32_t has_projections;  /* 0: standard MoE (requires l == d) */
   int32_t has_router_bias;  /* 1: z += b before selection and gating (fp32 b[N]) */
   int32_t expert_kernel;    /* lmoe_expert_kernel; 0 = AUTO */
+  int64_t n_shared;         /* S shared experts, 0 .. 64 (Eq. (1)/(2), second sum) */
+  int64_t m_shared;         /* their FFN width, a multiple of 16 (read when n_shared > 0) */
 } lmoe_config;
 
 /* Device pointers; shapes use the config's d, l, m, N. */
@@ -117,12 +124,17 @@ typedef struct {
   const float *w1_scale;    /* [N][m] fp32; FP8 experts only */
   const float *w2_scale;    /* [N][l] fp32; FP8 experts only */
   const void *w_up;         /* [d][l] act dtype; NULL without projections */
+  const void *w_shared1;    /* [S*m_shared][d] act dtype: Ws1_j is rows j*m_shared ..; n_shared > 0 */
+  const void *w_shared2;    /* [d][S*m_shared] act dtype: Ws2_j is columns j*m_shared ..; n_shared > 0 */
 } lmoe_weights;
 
 /* Per-stage GPU timing: an opaque object holding HIP events.  Attach one to
  * a forward call through lmoe_debug_out.timer; the call then records an
- * event before its first kernel and after each stage.  Reading synchronises
- * on the last event and ADDS the stage durations to the accumulators. */
+ * event at the beginning and at the end of each stage (the shared-expert
+ * stage on the stream it runs on).  Reading synchronises on those events and
+ * ADDS the stage durations to the accumulators.  With the shared experts on
+ * a side stream, the stage that adds their sum (UP, or COMBINE for the
+ * standard MoE) includes any wait for them. */
 typedef struct lmoe_timer lmoe_timer;
 
 enum {
@@ -132,8 +144,9 @@ enum {
   LMOE_STAGE_FC1 = 3,         /* grouped latent FC1 + squared ReLU (gathers u rows) */
   LMOE_STAGE_FC2 = 4,         /* grouped latent FC2 */
   LMOE_STAGE_COMBINE = 5,     /* gate-weighted sum of the K expert outputs per token */
-  LMOE_STAGE_UP = 6,          /* W_up GEMM */
-  LMOE_NUM_STAGES = 7
+  LMOE_STAGE_UP = 6,          /* W_up GEMM (+ the shared experts' sum) */
+  LMOE_STAGE_SHARED = 7,      /* shared experts: x Ws1^T + squared ReLU, then . Ws2^T (fp32) */
+  LMOE_NUM_STAGES = 8
 };
 
 /* Optional device outputs of a forward call (any may be NULL). */
@@ -170,6 +183,25 @@ lmoe_status latentmoe_workspace_size(const lmoe_handle *h, int64_t T, size_t *by
 lmoe_status latentmoe_forward(const lmoe_handle *h, const lmoe_weights *w, const void *x,
                               int64_t T, void *out, const lmoe_debug_out *dbg,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* A second stream for the shared experts (LatentMoE §4.3 names separate
+ * streams for routed and shared experts as a way to cut latency when the
+ * routed path leaves the GPU partly idle).  The object holds the side
+ * stream (a hipStream_t as void*, owned by the caller, on the device of the
+ * forward calls, not NULL, default priority) and two events of its own.
+ * One forward call at a time may use an lmoe_overlap. */
+typedef struct lmoe_overlap lmoe_overlap;
+lmoe_status latentmoe_overlap_create(void *side_stream, lmoe_overlap **out);
+lmoe_status latentmoe_overlap_destroy(lmoe_overlap *o);
+
+/* latentmoe_forward with the shared experts on ov's side stream: forked
+ * from `stream` at the start of the call (they read only x) and joined back
+ * before the stage that adds their sum.  ov == NULL (or n_shared == 0) is
+ * latentmoe_forward.  The side stream must differ from `stream`. */
+lmoe_status latentmoe_forward_overlap(const lmoe_handle *h, const lmoe_weights *w, const void *x,
+                                      int64_t T, void *out, const lmoe_debug_out *dbg,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      lmoe_overlap *ov);
 
 lmoe_status latentmoe_destroy(lmoe_handle *h);
 

@@ -1,7 +1,7 @@
 """MI355X (gfx950) LatentMoE layer forward -- Python binding of liblatentmoe.so.
 
 The layer (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter in
-Mixture of Experts, §3 Eq. (1)/(2), routed-expert term) runs entirely in the
+Mixture of Experts, §3 Eq. (1)/(2), routed and shared experts) runs entirely in the
 HIP kernels behind the C ABI declared in ``include/latentmoe.h``.  This module
 only marshals arguments: it checks shapes/dtypes of torch tensors, passes
 their device pointers, the current HIP stream and a workspace tensor, and
@@ -28,8 +28,8 @@ ACT_SQRELU = 0
 EXPERTS_AUTO, EXPERTS_TILED, EXPERTS_STREAM, EXPERTS_FUSED = 0, 1, 2, 3
 _EXPERT_KERNEL = {"auto": EXPERTS_AUTO, "tiled": EXPERTS_TILED, "stream": EXPERTS_STREAM,
                   "fused": EXPERTS_FUSED}
-NUM_STAGES = 7
-STAGE_NAMES = ("down_router", "topk", "dispatch", "fc1", "fc2", "combine", "up")
+NUM_STAGES = 8
+STAGE_NAMES = ("down_router", "topk", "dispatch", "fc1", "fc2", "combine", "up", "shared")
 
 _DT = {"f32": LMOE_F32, "bf16": LMOE_BF16, "fp8_e4m3_rowscale": LMOE_FP8_E4M3_ROWSCALE}
 _GATE = {"softmax_all": GATE_SOFTMAX_ALL, "softmax_topk": GATE_SOFTMAX_TOPK,
@@ -38,7 +38,8 @@ _GATE = {"softmax_all": GATE_SOFTMAX_ALL, "softmax_topk": GATE_SOFTMAX_TOPK,
 EXPORTED = ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
             "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
             "latentmoe_timer_destroy", "latentmoe_status_string", "latentmoe_last_error",
-            "latentmoe_expert_regime")
+            "latentmoe_expert_regime", "latentmoe_overlap_create", "latentmoe_overlap_destroy",
+            "latentmoe_forward_overlap")
 
 
 class LmoeConfig(ctypes.Structure):
@@ -47,14 +48,16 @@ class LmoeConfig(ctypes.Structure):
                 ("router_input", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("activation", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("expert_dtype", ctypes.c_int32), ("has_projections", ctypes.c_int32),
-                ("has_router_bias", ctypes.c_int32), ("expert_kernel", ctypes.c_int32)]
+                ("has_router_bias", ctypes.c_int32), ("expert_kernel", ctypes.c_int32),
+                ("n_shared", ctypes.c_int64), ("m_shared", ctypes.c_int64)]
 
 
 class LmoeWeights(ctypes.Structure):
     _fields_ = [("w_down", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
                 ("router_bias", ctypes.c_void_p), ("w1", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
-                ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p)]
+                ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p)]
 
 
 class LmoeDebug(ctypes.Structure):
@@ -89,6 +92,11 @@ def lib():
             L.latentmoe_workspace_size.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_size_t)]
             L.latentmoe_forward.argtypes = [vp, ctypes.POINTER(LmoeWeights), vp, i64, vp,
                                             ctypes.POINTER(LmoeDebug), vp, ctypes.c_size_t, vp]
+            L.latentmoe_forward_overlap.argtypes = [vp, ctypes.POINTER(LmoeWeights), vp, i64, vp,
+                                                    ctypes.POINTER(LmoeDebug), vp,
+                                                    ctypes.c_size_t, vp, vp]
+            L.latentmoe_overlap_create.argtypes = [vp, ctypes.POINTER(vp)]
+            L.latentmoe_overlap_destroy.argtypes = [vp]
             L.latentmoe_destroy.argtypes = [vp]
             L.latentmoe_timer_create.argtypes = [ctypes.POINTER(vp)]
             L.latentmoe_timer_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
@@ -102,7 +110,8 @@ def lib():
             L.latentmoe_expert_regime.restype = ctypes.c_char_p
             for f in ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
                       "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
-                      "latentmoe_timer_destroy"):
+                      "latentmoe_timer_destroy", "latentmoe_forward_overlap",
+                      "latentmoe_overlap_create", "latentmoe_overlap_destroy"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -122,7 +131,8 @@ def make_config(spec, expert_kernel: str = "auto") -> LmoeConfig:
                       ROUTER_ON_LATENT if spec.router_on_latent else ROUTER_ON_X,
                       _GATE[spec.gating], ACT_SQRELU, _DT[spec.act_dtype], _DT[spec.expert_dtype],
                       int(spec.has_projections), int(spec.has_router_bias),
-                      _EXPERT_KERNEL[expert_kernel])
+                      _EXPERT_KERNEL[expert_kernel], getattr(spec, "n_shared", 0),
+                      getattr(spec, "m_shared", 0))
 
 
 class StageTimer:
@@ -143,6 +153,31 @@ class StageTimer:
     def close(self):
         if self._h:
             lib().latentmoe_timer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Overlap:
+    """A side HIP stream for the shared experts (lmoe_overlap).  The stream
+    is a torch.cuda.Stream at the default priority, created here unless one
+    is given; one forward call at a time may use the object."""
+
+    def __init__(self, stream=None, device=None):
+        torch = _torch()
+        self.stream = stream if stream is not None else torch.cuda.Stream(device=device)
+        h = ctypes.c_void_p()
+        _check(lib().latentmoe_overlap_create(ctypes.c_void_p(self.stream.cuda_stream),
+                                              ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().latentmoe_overlap_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -227,15 +262,22 @@ class LatentMoELayer:
                                        (torch.float32,))
             cw.w2_scale = self._expect("w2_scale", w.get("w2_scale"), (s.n_experts, s.l),
                                        (torch.float32,))
+        S = getattr(s, "n_shared", 0)
+        if S:
+            hs = S * s.m_shared
+            cw.w_shared1 = self._expect("w_shared1", w.get("w_shared1"), (hs, s.d), act)
+            cw.w_shared2 = self._expect("w_shared2", w.get("w_shared2"), (s.d, hs), act)
         return cw
 
     def forward(self, x, weights, out=None, workspace=None, debug: dict | None = None,
-                timer: StageTimer | None = None, stream=None, cweights: LmoeWeights | None = None):
+                timer: StageTimer | None = None, stream=None, cweights: LmoeWeights | None = None,
+                overlap: Overlap | None = None):
         """out[T][d] = layer(x[T][d]) on the current (or given) HIP stream.
 
         debug: optional dict of preallocated device tensors keyed like
         lmoe_debug_out (topk_idx, topk_gate, expert_counts, expert_offsets,
-        slot_of, token_of, logits, latent).
+        slot_of, token_of, logits, latent).  overlap: run the shared experts
+        on that object's side stream (latentmoe_forward_overlap).
         """
         torch = _torch()
         s = self.spec
@@ -264,8 +306,13 @@ class LatentMoELayer:
         if stream is None:
             stream = torch.cuda.current_stream(x.device)
         st = ctypes.c_void_p(stream.cuda_stream)
-        _check(lib().latentmoe_forward(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
-                                       workspace.data_ptr(), workspace.numel(), st))
+        if overlap is not None:
+            _check(lib().latentmoe_forward_overlap(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
+                                                   workspace.data_ptr(), workspace.numel(), st,
+                                                   overlap._h))
+        else:
+            _check(lib().latentmoe_forward(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
+                                           workspace.data_ptr(), workspace.numel(), st))
         return out
 
 

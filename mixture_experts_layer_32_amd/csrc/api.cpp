@@ -2,16 +2,20 @@
 // the stream-ordered launch sequence (include/latentmoe.h).
 //
 // Layer (LatentMoE: Toward Optimal Accuracy per FLOP and Parameter in
-// Mixture of Experts, §3 Eq. (1)/(2), routed term):
+// Mixture of Experts, §3 Eq. (1)/(2)):
+//   shared   Hs = sqrelu(x Ws1^T); R = Hs Ws2^T (fp32)   the S shared experts
 //   stage 0  u = x W_down^T (bf16/f32 out); logits = r W_r^T (fp32), r = x or u
 //   stage 1  top-K per token (ties -> lower id) and gates
 //   stage 2  expert histogram / prefix sum / stable row of every token copy
 //   stage 3  H = sqrelu(u[token_of] W1_e^T)       grouped by expert
 //   stage 4  Y = H W2_e^T                         grouped by expert
 //   stage 5  v[t] = sum_j g[t][j] Y[slot_of[t][j]]
-//   stage 6  out = v W_up^T
+//   stage 6  out = v W_up^T + R
 // Without projections (standard MoE) stage 0 computes only the logits, the
-// expert GEMMs read x, and stage 5 writes `out` directly.
+// expert GEMMs read x, and stage 5 writes `out` directly (adding R there).
+// The shared experts read only x: with a side stream (lmoe_overlap) they run
+// there, forked at the start of the call and joined before the stage that
+// adds R; otherwise they run first on the call's stream.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -32,7 +36,12 @@ struct lmoe_handle {
 struct lmoe_timer {
   int max_calls = 0;
   int n_calls = 0;
-  std::vector<hipEvent_t> ev;  // max_calls * (LMOE_NUM_STAGES + 1)
+  std::vector<hipEvent_t> ev;  // max_calls * 2 * LMOE_NUM_STAGES: begin and end of each stage
+};
+
+struct lmoe_overlap {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -56,6 +65,7 @@ lmoe_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxExperts = 2048;
 constexpr int64_t kMaxTopK = 64;
+constexpr int64_t kMaxShared = 64;
 constexpr int64_t kMaxCopies = int64_t(1) << 30;  // T * K (int32 row indices)
 constexpr double kStreamMaxRowsPerExpert = 96.0;  // mean copies per expert -> streaming kernel
 // fp8 weights: the tiled kernel (one weight tile per expert and 256 columns,
@@ -113,6 +123,28 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, size_t elem_bytes, bool bf
   return d;
 }
 
+// Dense GEMM on 128 x 128 tiles with K split until about `per_cu` workgroups
+// per compute unit (at least 8 K stages per split, at most 16 splits).  Fewer
+// operand bytes per flop than the 64 x 64 tile for decode-sized M.
+DensePlan plan_dense_128(int64_t M, int64_t N, int64_t K, size_t elem_bytes, int per_cu) {
+  DensePlan d;
+  d.tile = 0;
+  if (M <= 0 || N <= 0 || K <= 0) return d;
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t stages = (K * int64_t(elem_bytes) + 127) / 128;
+  int64_t s = (per_cu * kComputeUnits + t128 - 1) / t128;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
+  if (N % 4) s = 1;
+  d.splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
+  return d;
+}
+
+// Shared-expert GEMMs: 0 = plan_dense, 1 / 2 = 128 x 128 tiles split to 1 / 2
+// workgroups per compute unit
+#ifndef LMOE_SHARED_PLAN
+#define LMOE_SHARED_PLAN 1
+#endif
+
 // Tile of the grouped expert GEMMs when experts receive many tokens: 128 rows
 // keeps the padding of each expert's last tile small, 256 columns halve the
 // operand bytes per flop against 128 x 128.
@@ -137,8 +169,9 @@ struct Plan {
   // columns 0..l-1 from W_down, l..l+N-1 from W_r), partials only
   bool front = false;
   DensePlan front_plan;
+  DensePlan sh1, sh2;   // shared experts: x Ws1^T (+ sqrelu), Hs Ws2^T (fp32 out)
   size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, partial,
-      total;
+      Hs, R, partial_sh, total;
 };
 
 Plan make_plan(const lmoe_config& c, int64_t T) {
@@ -199,6 +232,22 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   } else {
     partial = std::max(partial, router_part);
   }
+  // shared experts: their own partial region (they may run beside the routed path)
+  const int64_t hs = c.n_shared * c.m_shared;
+  size_t partial_sh = 0;
+  if (hs > 0) {
+    if (LMOE_SHARED_PLAN == 0 || ab != 2) {
+      p.sh1 = plan_dense(T, hs, c.d, ab, ab == 2);
+      p.sh2 = plan_dense(T, c.d, hs, ab, false);
+    } else {
+      p.sh1 = plan_dense_128(T, hs, c.d, ab, LMOE_SHARED_PLAN);
+      p.sh2 = plan_dense_128(T, c.d, hs, ab, LMOE_SHARED_PLAN);
+      const int64_t t256 = ((T + 255) / 256) * ((hs + 255) / 256);
+      if (t256 >= kComputeUnits) p.sh1 = plan_dense(T, hs, c.d, ab, true);
+    }
+    partial_sh = std::max(size_t(p.sh1.splits > 1 ? p.sh1.splits : 0) * T * hs * 4,
+                          size_t(p.sh2.splits > 1 ? p.sh2.splits : 0) * T * c.d * 4);
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.u = take(c.has_projections ? size_t(T) * c.l * ab : 0);
@@ -216,6 +265,9 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.Y = take(size_t(p.copies) * c.l * ab);
   p.v = take(c.has_projections ? size_t(T) * c.l * ab : 0);
   p.partial = take(partial);
+  p.Hs = take(size_t(T) * hs * ab);
+  p.R = take(hs > 0 ? size_t(T) * c.d * 4 : 0);
+  p.partial_sh = take(partial_sh);
   p.total = o;
   return p;
 }
@@ -281,6 +333,11 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
     return fail(LMOE_ERR_UNSUPPORTED, "create: widths above 2^20");
   if (c.expert_kernel < LMOE_EXPERTS_AUTO || c.expert_kernel > LMOE_EXPERTS_FUSED)
     return fail(LMOE_ERR_INVALID_ARG, "create: bad expert_kernel");
+  if (c.n_shared < 0 || (c.n_shared > 0 && c.m_shared <= 0))
+    return fail(LMOE_ERR_INVALID_ARG, "create: n_shared < 0, or shared experts without a width");
+  if (c.n_shared > kMaxShared || (c.n_shared > 0 && (c.m_shared % 16 || c.m_shared > (int64_t(1) << 20))))
+    return fail(LMOE_ERR_UNSUPPORTED, "create: n_shared <= %lld and m_shared a multiple of 16 "
+                "up to 2^20 supported", (long long)kMaxShared);
   if (c.expert_kernel == LMOE_EXPERTS_FUSED &&
       !(c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16 &&
         lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m))))
@@ -316,7 +373,7 @@ lmoe_status latentmoe_timer_create(lmoe_timer** out) {
   lmoe_timer* t = new (std::nothrow) lmoe_timer;
   if (!t) return fail(LMOE_ERR_ALLOC, "timer_create: out of host memory");
   t->max_calls = 256;
-  t->ev.assign(size_t(t->max_calls) * (LMOE_NUM_STAGES + 1), nullptr);
+  t->ev.assign(size_t(t->max_calls) * 2 * LMOE_NUM_STAGES, nullptr);
   for (auto& e : t->ev) {
     hipError_t r = hipEventCreate(&e);
     if (r != hipSuccess) {
@@ -335,15 +392,15 @@ lmoe_status latentmoe_timer_read(lmoe_timer* t, float* stage_ms, int32_t n_stage
     return fail(LMOE_ERR_INVALID_ARG, "timer_read: bad argument");
   for (int s = 0; s < n_stages; ++s) stage_ms[s] = 0.f;
   const int n = t->n_calls;
-  if (n > 0) {
-    hipError_t r = hipEventSynchronize(t->ev[size_t(n - 1) * (LMOE_NUM_STAGES + 1) + LMOE_NUM_STAGES]);
-    if (r != hipSuccess) return hip_fail(r, "timer_read: hipEventSynchronize");
-  }
   for (int c = 0; c < n; ++c) {
-    const hipEvent_t* e = &t->ev[size_t(c) * (LMOE_NUM_STAGES + 1)];
+    // stage s of call c: events 2s (begin) and 2s + 1 (end), possibly on
+    // the side stream (shared experts)
+    const hipEvent_t* e = &t->ev[size_t(c) * 2 * LMOE_NUM_STAGES];
     for (int s = 0; s < LMOE_NUM_STAGES; ++s) {
+      hipError_t r = hipEventSynchronize(e[2 * s + 1]);
+      if (r != hipSuccess) return hip_fail(r, "timer_read: hipEventSynchronize");
       float ms = 0.f;
-      hipError_t r = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+      r = hipEventElapsedTime(&ms, e[2 * s], e[2 * s + 1]);
       if (r != hipSuccess) return hip_fail(r, "timer_read: hipEventElapsedTime");
       stage_ms[s] += ms;
     }
@@ -361,9 +418,42 @@ lmoe_status latentmoe_timer_destroy(lmoe_timer* t) {
   return LMOE_OK;
 }
 
+lmoe_status latentmoe_overlap_create(void* side_stream, lmoe_overlap** out) {
+  if (!out) return fail(LMOE_ERR_INVALID_ARG, "overlap_create: NULL argument");
+  *out = nullptr;
+  if (!side_stream) return fail(LMOE_ERR_INVALID_ARG, "overlap_create: the side stream must not be NULL");
+  lmoe_overlap* o = new (std::nothrow) lmoe_overlap;
+  if (!o) return fail(LMOE_ERR_ALLOC, "overlap_create: out of host memory");
+  o->side = static_cast<hipStream_t>(side_stream);
+  hipError_t r = hipEventCreateWithFlags(&o->fork, hipEventDisableTiming);
+  if (r == hipSuccess) r = hipEventCreateWithFlags(&o->join, hipEventDisableTiming);
+  if (r != hipSuccess) {
+    if (o->fork) (void)hipEventDestroy(o->fork);
+    delete o;
+    return hip_fail(r, "overlap_create: hipEventCreateWithFlags");
+  }
+  *out = o;
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_overlap_destroy(lmoe_overlap* o) {
+  if (!o) return LMOE_OK;
+  (void)hipEventDestroy(o->fork);
+  (void)hipEventDestroy(o->join);
+  delete o;
+  return LMOE_OK;
+}
+
 lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const void* x,
                               int64_t T, void* out, const lmoe_debug_out* dbg, void* workspace,
                               size_t workspace_bytes, void* stream) {
+  return latentmoe_forward_overlap(h, w, x, T, out, dbg, workspace, workspace_bytes, stream, nullptr);
+}
+
+lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* w, const void* x,
+                                      int64_t T, void* out, const lmoe_debug_out* dbg,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      lmoe_overlap* ov) {
   if (!h || !w) return fail(LMOE_ERR_INVALID_ARG, "forward: NULL handle or weights");
   if (T < 0) return fail(LMOE_ERR_INVALID_ARG, "forward: T < 0");
   if (T == 0) return LMOE_OK;
@@ -378,7 +468,13 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     return fail(LMOE_ERR_INVALID_ARG, "forward: NULL router bias");
   if (c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE && (!w->w1_scale || !w->w2_scale))
     return fail(LMOE_ERR_INVALID_ARG, "forward: NULL fp8 scales");
-  const void* ptrs[] = {x, out, w->w_router, w->w1, w->w2, w->w_down, w->w_up};
+  const bool shared = c.n_shared > 0;
+  if (shared && (!w->w_shared1 || !w->w_shared2))
+    return fail(LMOE_ERR_INVALID_ARG, "forward: NULL shared-expert weights");
+  if (ov && static_cast<hipStream_t>(stream) == ov->side)
+    return fail(LMOE_ERR_INVALID_ARG, "forward: the side stream must differ from the call's stream");
+  const void* ptrs[] = {x, out, w->w_router, w->w1, w->w2, w->w_down, w->w_up,
+                        shared ? w->w_shared1 : nullptr, shared ? w->w_shared2 : nullptr};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(LMOE_ERR_INVALID_ARG, "forward: pointers must be 16-byte aligned");
   const Plan p = make_plan(c, T);
@@ -410,13 +506,16 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
   void* Y = ws + p.Y;
   void* v = c.has_projections ? ws + p.v : out;
   float* partial = reinterpret_cast<float*>(ws + p.partial);
+  void* Hs = ws + p.Hs;
+  float* R = shared ? reinterpret_cast<float*>(ws + p.R) : nullptr;
+  float* partial_sh = reinterpret_cast<float*>(ws + p.partial_sh);
 
   lmoe_timer* tm = dbg ? dbg->timer : nullptr;
   hipEvent_t* ev = nullptr;
   if (tm) {
     if (tm->n_calls >= tm->max_calls)
       return fail(LMOE_ERR_INVALID_ARG, "forward: timer full (%d calls); read it first", tm->max_calls);
-    ev = &tm->ev[size_t(tm->n_calls) * (LMOE_NUM_STAGES + 1)];
+    ev = &tm->ev[size_t(tm->n_calls) * 2 * LMOE_NUM_STAGES];
     ++tm->n_calls;
   }
   hipError_t e;
@@ -425,8 +524,44 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     e = (call);                                       \
     if (e != hipSuccess) return hip_fail(e, what);    \
   } while (0)
+  // stage i: begin / end events (stages 0..6 follow each other on `s`)
+#define LMOE_BEGIN(i, st) \
+  if (ev) LMOE_TRY(hipEventRecord(ev[2 * (i)], st), "hipEventRecord")
+#define LMOE_END(i, st) \
+  if (ev) LMOE_TRY(hipEventRecord(ev[2 * (i) + 1], st), "hipEventRecord")
 #define LMOE_MARK(i) \
-  if (ev) LMOE_TRY(hipEventRecord(ev[i], s), "hipEventRecord")
+  if (ev) {                                                                  \
+    if ((i) > 0) LMOE_TRY(hipEventRecord(ev[2 * (i) - 1], s), "hipEventRecord"); \
+    if ((i) < LMOE_STAGE_SHARED) LMOE_TRY(hipEventRecord(ev[2 * (i)], s), "hipEventRecord"); \
+  }
+
+  // ---- shared experts (second sum of Eq. (1)/(2)), on x only: on the side
+  // stream after a fork from `s`, or first on `s`
+  hipStream_t ss = ov && shared ? ov->side : s;
+  if (ss != s) {
+    LMOE_TRY(hipEventRecord(ov->fork, s), "hipEventRecord (fork)");
+    LMOE_TRY(hipStreamWaitEvent(ss, ov->fork, 0), "hipStreamWaitEvent (fork)");
+  }
+  LMOE_BEGIN(LMOE_STAGE_SHARED, ss);
+  if (shared) {
+    const int hs = static_cast<int>(c.n_shared * c.m_shared);
+    lmoe::GemmArgs a;
+    a.A = x; a.lda = d; a.B = w->w_shared1; a.ldb = d; a.C = Hs; a.ldc = hs;
+    a.M = Ti; a.N = hs; a.K = d; a.act = lmoe::kActSqRelu;
+    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.sh1.tile, ss, p.sh1.splits, partial_sh),
+             "shared FC1 GEMM");
+    lmoe::GemmArgs b;
+    b.A = Hs; b.lda = hs; b.B = w->w_shared2; b.ldb = hs; b.C = R; b.ldc = d;
+    b.M = Ti; b.N = d; b.K = hs;
+    LMOE_TRY(lmoe::launch_gemm_tiled(b, adt, lmoe::Dt::F32, p.sh2.tile, ss, p.sh2.splits, partial_sh),
+             "shared FC2 GEMM");
+  }
+  LMOE_END(LMOE_STAGE_SHARED, ss);
+  if (ss != s) LMOE_TRY(hipEventRecord(ov->join, ss), "hipEventRecord (join)");
+  // the stage that adds R waits for the side stream
+  auto join = [&]() -> hipError_t {
+    return ss != s ? hipStreamWaitEvent(s, ov->join, 0) : hipSuccess;
+  };
 
   LMOE_MARK(0);
   // ---- stage 0: down-projection and router logits (split-K partials that
@@ -534,14 +669,20 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");
   }
   LMOE_MARK(5);
-  // ---- stage 5: gate-weighted combine (into out directly for the standard MoE)
-  LMOE_TRY(lmoe::launch_combine(Y, slot_of, gate, Ti, K, l, adt, v, s), "combine");
+  // ---- stage 5: gate-weighted combine (into out directly for the standard
+  // MoE, adding the shared experts' R there)
+  if (!c.has_projections) LMOE_TRY(join(), "hipStreamWaitEvent (join)");
+  LMOE_TRY(lmoe::launch_combine(Y, slot_of, gate, Ti, K, l, adt, c.has_projections ? nullptr : R,
+                                v, s),
+           "combine");
   LMOE_MARK(6);
-  // ---- stage 6: up-projection
+  // ---- stage 6: up-projection, + R in its epilogue
   if (c.has_projections) {
+    LMOE_TRY(join(), "hipStreamWaitEvent (join)");
     lmoe::GemmArgs a;
     a.A = v; a.lda = l; a.B = w->w_up; a.ldb = l; a.C = out; a.ldc = d;
     a.M = Ti; a.N = d; a.K = l;
+    a.R = R; a.ldr = d;
     LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.up.tile, s, p.up.splits, partial), "W_up GEMM");
   }
   LMOE_MARK(7);
@@ -565,6 +706,8 @@ lmoe_status latentmoe_forward(const lmoe_handle* h, const lmoe_weights* w, const
         (st = cp(dbg->latent, u, size_t(T) * l * ab, "copy latent")) != LMOE_OK) return st;
   }
 #undef LMOE_MARK
+#undef LMOE_BEGIN
+#undef LMOE_END
 #undef LMOE_TRY
   return LMOE_OK;
 }

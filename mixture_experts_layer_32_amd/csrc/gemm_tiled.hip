@@ -1,6 +1,6 @@
 // LDS-tiled MFMA GEMM, dense or grouped by expert, for gfx950.
 //
-// C[r][n] = act(scale[n] * sum_k A[arow(r)][k] * B[g][n][k])
+// C[r][n] = act(scale[n] * sum_k A[arow(r)][k] * B[g][n][k])  (+ R[r][n], dense)
 //
 // Used for the two projections (W_down: u = x W_down^T, W_up: out = v W_up^T),
 // the router logits (fp32 output) and, when experts receive many tokens, the
@@ -28,6 +28,8 @@
 // rows), so the 16 lanes reading one fragment column of 16 consecutive rows
 // touch 16 distinct 16-byte bank groups.  The output tile leaves through LDS
 // (rows padded by 16 bytes against bank conflicts) as 16-byte row chunks.
+// An optional fp32 residual R (the shared experts' sum, added to W_up's
+// output) joins the accumulators before the one rounding to the output type.
 //
 // Dense problems with too few tiles to fill the device split K: every split
 // writes an fp32 partial tile and a reduction kernel adds the partials in a
@@ -347,6 +349,14 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
             if (SCALE) val[e] *= s4[e];
             val[e] = apply_act<ACT>(val[e]);
           }
+          // residual (dense, N % 4 == 0: the 4 columns are in or out together)
+          const int lr = wm * WM + i * BLK + trow;
+          if (p.R != nullptr && lr < rows && col0 + colt < p.N) {
+            const f32x4_t r4 =
+                *reinterpret_cast<const f32x4_t*>(p.R + (int64_t)(row0 + lr) * p.ldr + col0 + colt);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] += r4[e];
+          }
           store4<TOut>(Ct + (wm * WM + i * BLK + trow) * LDT + colt, val);
         }
       }
@@ -397,10 +407,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   }
 }
 
-// C[r][c] = act(scale[c] * sum_s P[s][r][c]), splits added in order.
+// C[r][c] = act(scale[c] * sum_s P[s][r][c]) (+ R[r][c]), splits added in order.
 template <typename TOut, int ACT, bool SCALE>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int splits,
                                                             int M, int N, const float* __restrict__ scale,
+                                                            const float* __restrict__ R, int64_t ldr,
                                                             TOut* __restrict__ C, int64_t ldc) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 columns per thread
   const int64_t total = (int64_t)M * (N / 4);
@@ -410,11 +421,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t mn = (int64_t)M * N;
   f32x4_t s = *reinterpret_cast<const f32x4_t*>(P + (int64_t)r * N + c);
   for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4_t*>(P + z * mn + (int64_t)r * N + c);
+  f32x4_t res = {0.f, 0.f, 0.f, 0.f};
+  if (R != nullptr) res = *reinterpret_cast<const f32x4_t*>(R + (int64_t)r * ldr + c);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     float val = s[v];
     if (SCALE) val *= scale[c + v];
-    store_elem<TOut>(C + (int64_t)r * ldc + c + v, apply_act<ACT>(val));
+    val = apply_act<ACT>(val);
+    if (R != nullptr) val += res[v];
+    store_elem<TOut>(C + (int64_t)r * ldc + c + v, val);
   }
 }
 
@@ -439,6 +454,10 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
   if (a.B2 && (a.g_off || a.N0 <= 0 || a.N0 >= a.N || a.N0 % BN || !part || reduce ||
                (uint64_t)a.N0 * a.ldb * sizeof(TB) >= (1ull << 31)))
     return hipErrorInvalidValue;
+  // residual: dense, whole 4-column groups, 16-byte aligned rows
+  if (a.R && (a.g_off || a.N % 4 || a.ldr % 4 || a.ldr < a.N ||
+              (reinterpret_cast<uintptr_t>(a.R) & 15u) || (part && !reduce)))
+    return hipErrorInvalidValue;
   if (a.act == kActSqRelu) {
     if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
     else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
@@ -452,11 +471,11 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
   const dim3 rg((n4 + 255) / 256);
   TOut* C = static_cast<TOut*>(a.C);
   if (a.act == kActSqRelu) {
-    if (scale) splitk_reduce_kernel<TOut, kActSqRelu, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, C, a.ldc);
-    else splitk_reduce_kernel<TOut, kActSqRelu, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, C, a.ldc);
+    if (scale) splitk_reduce_kernel<TOut, kActSqRelu, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
+    else splitk_reduce_kernel<TOut, kActSqRelu, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
   } else {
-    if (scale) splitk_reduce_kernel<TOut, kActNone, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, C, a.ldc);
-    else splitk_reduce_kernel<TOut, kActNone, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, C, a.ldc);
+    if (scale) splitk_reduce_kernel<TOut, kActNone, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
+    else splitk_reduce_kernel<TOut, kActNone, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
   }
   return hipGetLastError();
 }

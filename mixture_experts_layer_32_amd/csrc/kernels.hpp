@@ -36,6 +36,10 @@ struct GemmArgs {
   // the column tile, split-K partial output only)
   const void* B2 = nullptr;
   int N0 = 0;
+  // dense only: fp32 residual added to the output before its one rounding,
+  // C[r][c] = act(...) + R[r * ldr + c] (N, ldr multiples of 4, R 16-byte aligned)
+  const float* R = nullptr;
+  int64_t ldr = 0;
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
@@ -120,8 +124,9 @@ bool route_small_fits(int T, int N, int K);
 hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_m, int32_t* counts,
                               int32_t* offsets, int32_t* tiles, int32_t* slot_of,
                               int32_t* token_of, hipStream_t s);
+// v[t] = sum_j gate[t][j] * Y[slot_of[t][j]] (+ R[t], fp32 [T][l], when R is given)
 hipError_t launch_combine(const void* Y, const int32_t* slot_of, const float* gate, int T, int K,
-                          int l, Dt dt, void* v, hipStream_t s);
+                          int l, Dt dt, const float* R, void* v, hipStream_t s);
 
 constexpr int kRouteBlock = 64;  // tokens per routing block (one 64-bit mask per expert)
 

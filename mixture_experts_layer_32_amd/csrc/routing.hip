@@ -20,7 +20,9 @@
 //  route_small   the three steps above in one launch when all masks fit in
 //                LDS (decode-sized batches).
 //  combine       v[t] = sum_j gate[t][j] * Y[slot_of[t][j]] in fp32, fixed
-//                j order (deterministic), rounded once to the output dtype.
+//                j order (deterministic), plus an optional fp32 residual (the
+//                shared experts' sum when v is the layer output), rounded
+//                once to the output dtype.
 #include <algorithm>
 
 #include "common.hpp"
@@ -392,6 +394,7 @@ template <typename T, int U>
 __global__ __launch_bounds__(512) void combine_kernel(const T* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gate, int K, int l,
+                                                      const float* __restrict__ R,
                                                       T* __restrict__ v) {
   constexpr int EPC = 16 / sizeof(T);
   const int t = blockIdx.x;
@@ -425,6 +428,15 @@ __global__ __launch_bounds__(512) void combine_kernel(const T* __restrict__ Y,
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] += gj * __uint_as_float(y[u][i]);
         }
+      }
+    }
+    if (R != nullptr) {
+      const f32x4_t* rr = reinterpret_cast<const f32x4_t*>(R + (int64_t)t * l + c * EPC);
+#pragma unroll
+      for (int q = 0; q < EPC / 4; ++q) {
+        const f32x4_t r4 = rr[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * q + i] += r4[i];
       }
     }
     u32x4 o;
@@ -530,24 +542,26 @@ hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_
 
 template <typename T>
 void launch_combine_t(const T* Y, const int32_t* slot_of, const float* gate, int T_, int K, int l,
-                      T* v, hipStream_t s) {
+                      const float* R, T* v, hipStream_t s) {
   // one thread per 16-byte chunk of the row (up to 512 threads, then a
   // loop); as many expert rows in flight as the token has (8, 16 or 32)
   const int chunks = l / (16 / static_cast<int>(sizeof(T)));
   const dim3 grid(T_), block(std::min(512, (chunks + 63) / 64 * 64));
-  if (K <= 8) combine_kernel<T, 8><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, v);
-  else if (K <= 16) combine_kernel<T, 16><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, v);
-  else combine_kernel<T, 32><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, v);
+  if (K <= 8) combine_kernel<T, 8><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
+  else if (K <= 16) combine_kernel<T, 16><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
+  else combine_kernel<T, 32><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
 }
 
 hipError_t launch_combine(const void* Y, const int32_t* slot_of, const float* gate, int T, int K,
-                          int l, Dt dt, void* v, hipStream_t s) {
+                          int l, Dt dt, const float* R, void* v, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (R && (reinterpret_cast<uintptr_t>(R) & 15u)) return hipErrorInvalidValue;
   if (dt == Dt::BF16)
-    launch_combine_t(static_cast<const uint16_t*>(Y), slot_of, gate, T, K, l,
+    launch_combine_t(static_cast<const uint16_t*>(Y), slot_of, gate, T, K, l, R,
                      static_cast<uint16_t*>(v), s);
   else
-    launch_combine_t(static_cast<const float*>(Y), slot_of, gate, T, K, l, static_cast<float*>(v), s);
+    launch_combine_t(static_cast<const float*>(Y), slot_of, gate, T, K, l, R,
+                     static_cast<float*>(v), s);
   return hipGetLastError();
 }
 

@@ -71,6 +71,10 @@ WORKLOADS = {
                                    gating="softmax_topk", act_dtype="f32", expert_dtype="f32",
                                    identity_projections=True),
         64, "tiny", "tiny layer with l = d and identity W_down/W_up"),
+    "tiny_shared": Workload(
+        "tiny_shared", LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4, gating="softmax_topk",
+                                 act_dtype="f32", expert_dtype="f32", n_shared=2, m_shared=64),
+        64, "tiny", "tiny LatentMoE with two shared experts in the d space, fp32"),
     "tiny_std": Workload(
         "tiny_std", LayerSpec(d=256, l=256, m=128, n_experts=16, top_k=4, gating="softmax_topk",
                               act_dtype="f32", expert_dtype="f32", has_projections=False),
@@ -83,6 +87,11 @@ WORKLOADS = {
         "latent_decode", LayerSpec(d=4096, l=1024, m=1536, n_experts=512, top_k=32,
                                    gating="sigmoid_topk_norm"),
         512, "decode", "LatentMoE at iso-cost (alpha=4), bf16, T=512"),
+    "latent_decode_shared": Workload(
+        "latent_decode_shared", LayerSpec(d=4096, l=1024, m=1536, n_experts=512, top_k=32,
+                                          gating="sigmoid_topk_norm", n_shared=2, m_shared=1536),
+        512, "decode", "LatentMoE at iso-cost (alpha=4) with S=2 shared experts of width m, "
+        "bf16, T=512"),
     "latent_prefill_zipf": Workload(
         "latent_prefill_zipf", LayerSpec(d=4096, l=1024, m=2048, n_experts=512, top_k=22,
                                          gating="softmax_all", has_router_bias=True),

@@ -32,14 +32,14 @@ def to_f64(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu(spec, w_np, x_np, device="cuda:0", layer=None):
+def run_gpu(spec, w_np, x_np, device="cuda:0", layer=None, overlap=None):
     import torch
     import mixture_experts_layer_32_amd as pkg
     layer = layer or pkg.LatentMoELayer(spec)
     T = x_np.shape[0]
     dev = pkg.to_device(dict(w_np, x=x_np), device)
     dbg = pkg.debug_buffers(spec, T, device)
-    out = layer.forward(dev["x"], dev, debug=dbg)
+    out = layer.forward(dev["x"], dev, debug=dbg, overlap=overlap)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() if v.dtype != torch.bfloat16 else to_f64(v) for k, v in dbg.items()}
     res["out"] = to_f64(out)

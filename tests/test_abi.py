@@ -74,6 +74,8 @@ def test_regime_choice():
     ("activation", 1, -2),        # gated experts not built
     ("expert_kernel", 4, -1),
     ("expert_kernel", 3, -2),     # fused kernel: bf16 only (the tiny layer is fp32)
+    ("n_shared", -1, -1),
+    ("n_shared", 2, -1),          # shared experts without a width
 ])
 def test_create_rejects(field, value, status):
     cfg = pkg.make_config(workload("tiny").spec)
@@ -97,6 +99,55 @@ def test_create_rejects_unsupported_dtypes_and_sizes():
     std = pkg.make_config(workload("tiny_std").spec)
     std.l = 128                                        # standard MoE needs l == d
     assert _create(std)[0] == -1
+
+
+def test_create_checks_shared_expert_sizes():
+    cfg = pkg.make_config(workload("tiny_shared").spec)
+    st, h = _create(cfg)
+    assert st == 0
+    pkg.lib().latentmoe_destroy(h)
+    for m_s, status in ((0, -1), (-16, -1), (72, -2), ((1 << 20) + 16, -2)):
+        cfg = pkg.make_config(workload("tiny_shared").spec)
+        cfg.m_shared = m_s
+        assert _create(cfg)[0] == status, m_s
+    cfg = pkg.make_config(workload("tiny_shared").spec)
+    cfg.n_shared = 65
+    assert _create(cfg)[0] == -2
+    cfg = pkg.make_config(workload("tiny").spec)
+    cfg.m_shared = 72                     # ignored without shared experts
+    st, h = _create(cfg)
+    assert st == 0
+    pkg.lib().latentmoe_destroy(h)
+
+
+def test_shared_experts_need_their_weights_and_a_side_stream_object():
+    lib = pkg.lib()
+    st, h = _create(pkg.make_config(workload("tiny_shared").spec))
+    assert st == 0
+    w = pkg.LmoeWeights()
+    w.w_router = w.w1 = w.w2 = w.w_down = w.w_up = 4096
+    w.w_shared1 = 4096                   # w_shared2 missing
+    assert lib.latentmoe_forward(h, ctypes.byref(w), ctypes.c_void_p(4096), 4,
+                                 ctypes.c_void_p(4096), None, ctypes.c_void_p(4096),
+                                 1 << 30, None) == -1
+    assert b"shared" in lib.latentmoe_last_error()
+    assert lib.latentmoe_forward_overlap(h, ctypes.byref(w), ctypes.c_void_p(4096), 0,
+                                         ctypes.c_void_p(4096), None, None, 0, None, None) == 0
+    ov = ctypes.c_void_p()
+    assert lib.latentmoe_overlap_create(None, ctypes.byref(ov)) == -1
+    assert not ov.value
+    assert lib.latentmoe_overlap_destroy(None) == 0
+    lib.latentmoe_destroy(h)
+
+
+def test_workspace_grows_with_shared_experts():
+    base = pkg.LatentMoELayer(workload("latent_decode").spec)
+    sh = pkg.LatentMoELayer(workload("latent_decode_shared").spec)
+    T = 512
+    extra = sh.workspace_size(T) - base.workspace_size(T)
+    # at least Hs [T][S*m_s] bf16 and the fp32 sum R [T][d]
+    assert extra >= T * 2 * 1536 * 2 + T * 4096 * 4
+    assert sh.expert_regime(T) == "fused"
 
 
 def test_forward_argument_errors_need_no_gpu():
