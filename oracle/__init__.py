@@ -33,6 +33,7 @@ _lib = None
 
 _DT = {"f32": 0, "bf16": 1, "fp8_e4m3_rowscale": 2}
 _GATE = {"softmax_all": 0, "softmax_topk": 1, "sigmoid_topk_norm": 2}
+_ACT = {"sqrelu": 0, "swiglu": 1}
 
 
 class _Layer(ctypes.Structure):
@@ -41,7 +42,8 @@ class _Layer(ctypes.Structure):
                 ("router_on_latent", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("has_projections", ctypes.c_int32), ("has_router_bias", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
-                ("n_shared", ctypes.c_int64), ("m_shared", ctypes.c_int64)]
+                ("n_shared", ctypes.c_int64), ("m_shared", ctypes.c_int64),
+                ("activation", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -49,7 +51,9 @@ class _Weights(ctypes.Structure):
                 ("router_bias", ctypes.c_void_p), ("w1", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
-                ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p)]
+                ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p),
+                ("w_gate", ctypes.c_void_p), ("w_gate_scale", ctypes.c_void_p),
+                ("w_shared_gate", ctypes.c_void_p)]
 
 
 def build(force: bool = True) -> str:
@@ -92,14 +96,15 @@ def _layer(spec) -> _Layer:
     return _Layer(spec.d, spec.l, spec.m, spec.n_experts, spec.top_k,
                   int(spec.router_on_latent), _GATE[spec.gating], int(spec.has_projections),
                   int(spec.has_router_bias), _DT[spec.act_dtype], _DT[spec.expert_dtype],
-                  spec.n_shared, spec.m_shared)
+                  spec.n_shared, spec.m_shared, _ACT[spec.activation])
 
 
 def _weights(w: dict):
     keep = {k: np.ascontiguousarray(v) for k, v in w.items()}
     cw = _Weights(*(_p(keep.get(k)) for k in ("w_down", "w_router", "router_bias", "w1", "w2",
                                                "w1_scale", "w2_scale", "w_up",
-                                               "w_shared1", "w_shared2")))
+                                               "w_shared1", "w_shared2", "w_gate",
+                                               "w_gate_scale", "w_shared_gate")))
     return cw, keep
 
 

@@ -8,8 +8,11 @@
  * routing weights p' = Softmax(W'_r x) from the d-dimensional x; top-K set
  * T_{K,N'}) and Eq. (1)/(2).  The expert nonlinearity is the non-gated
  * Squared-ReLU FFN, W_FC2 . (max(0, W_FC1 . u))^2 (Table 2 lists Squared-ReLU
- * for the 4096-wide models).  The shared experts E_j(x; d) of Eq. (1)/(2)
- * are the same FFN on x in the d space, added to the output ungated.
+ * for the 4096-wide models), or the gated SwiGLU FFN over the three matrices
+ * §3 gives an expert, W_FC2 . ((W_FC1 . u) * SiLU(W_gate . u)) (Table 2 lists
+ * SwiGLU for the 2048-wide model).  The shared experts E_j(x; d) of
+ * Eq. (1)/(2) are the same FFN on x in the d space, added to the output
+ * ungated.
  */
 #define _GNU_SOURCE /* qsort_r */
 #include "latentmoe_oracle.h"
@@ -73,6 +76,12 @@ static int check(const orc_layer *L, const orc_weights *W, const void *x, int64_
   if (L->gating < 0 || L->gating > 2) return -1;
   if (L->n_shared < 0) return -1;
   if (L->n_shared > 0 && (L->m_shared <= 0 || !W->w_shared1 || !W->w_shared2)) return -1;
+  if (L->activation != ORC_SQRELU && L->activation != ORC_SWIGLU) return -1;
+  if (L->activation == ORC_SWIGLU) {
+    if (!W->w_gate) return -1;
+    if (L->expert_dtype == ORC_FP8_E4M3_ROWSCALE && !W->w_gate_scale) return -1;
+    if (L->n_shared > 0 && !W->w_shared_gate) return -1;
+  }
   return 0;
 }
 
@@ -108,17 +117,27 @@ static void latent_and_logits(const orc_layer *L, const orc_weights *W, const vo
   }
 }
 
-/* y = W2_e . (max(0, W1_e . u))^2 : one latent expert E_e(u; l). */
+/* The nonlinearity between the two expert matrices: a = W_FC1 row . input,
+ * b = W_gate row . input (SwiGLU only). */
+static double act_fn(int activation, double a, double b) {
+  if (activation == ORC_SWIGLU) return a * (b / (1.0 + exp(-b)));  /* a * SiLU(b) */
+  double r = a > 0.0 ? a : 0.0;
+  return r * r;
+}
+
+/* y = W2_e . f(W1_e . u, Wg_e . u) : one latent expert E_e(u; l). */
 static void expert_ffn(const orc_layer *L, const orc_weights *W, int64_t e, const double *u,
                        double *h, double *y) {
   const int64_t l = L->l, m = L->m;
   const int dt = L->expert_dtype;
   for (int64_t r = 0; r < m; ++r) {
-    double s = 0.0;
+    double s = 0.0, sg = 0.0;
     const int64_t row = e * m + r;
     for (int64_t c = 0; c < l; ++c) s += ld(W->w1, dt, row * l + c, W->w1_scale, row) * u[c];
-    double a = s > 0.0 ? s : 0.0;
-    h[r] = a * a;
+    if (L->activation == ORC_SWIGLU)
+      for (int64_t c = 0; c < l; ++c)
+        sg += ld(W->w_gate, dt, row * l + c, W->w_gate_scale, row) * u[c];
+    h[r] = act_fn(L->activation, s, sg);
   }
   for (int64_t r = 0; r < l; ++r) {
     double s = 0.0;
@@ -150,10 +169,12 @@ static void add_shared(const orc_layer *L, const orc_weights *W, const double *x
                        double *out) {
   const int64_t d = L->d, H = L->n_shared * L->m_shared;
   for (int64_t k = 0; k < H; ++k) {
-    double s = 0.0;
+    double s = 0.0, sg = 0.0;
     for (int64_t c = 0; c < d; ++c) s += ld(W->w_shared1, L->act_dtype, k * d + c, NULL, 0) * xt[c];
-    double a = s > 0.0 ? s : 0.0;
-    hs[k] = a * a;
+    if (L->activation == ORC_SWIGLU)
+      for (int64_t c = 0; c < d; ++c)
+        sg += ld(W->w_shared_gate, L->act_dtype, k * d + c, NULL, 0) * xt[c];
+    hs[k] = act_fn(L->activation, s, sg);
   }
   for (int64_t r = 0; r < d; ++r) {
     double s = 0.0;
@@ -311,10 +332,13 @@ int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
         const int64_t ms = L->m_shared, H = L->n_shared * ms;
         for (int64_t j = 0; j < L->n_shared; ++j) {
           for (int64_t r = 0; r < ms; ++r) {
-            double s = 0.0;
+            double s = 0.0, sg = 0.0;
             for (int64_t c = 0; c < d; ++c)
               s += ld(W->w_shared1, L->act_dtype, (j * ms + r) * d + c, NULL, 0) * xt[c];
-            hs[r] = s > 0.0 ? s * s : 0.0;
+            if (L->activation == ORC_SWIGLU)
+              for (int64_t c = 0; c < d; ++c)
+                sg += ld(W->w_shared_gate, L->act_dtype, (j * ms + r) * d + c, NULL, 0) * xt[c];
+            hs[r] = act_fn(L->activation, s, sg);
           }
           for (int64_t r = 0; r < d; ++r) {
             double s = 0.0;

@@ -12,9 +12,14 @@
  *   z      = W_r . x  (or W_r . u)  [+ b]   router logits
  *   T      = indices of the K largest z     (ties: lower expert id first)
  *   g_i    = gate of expert i in T           (three gating rules, below)
- *   v      = sum_{i in T, ascending i} g_i * W2_i . (max(0, W1_i . u))^2
+ *   v      = sum_{i in T, ascending i} g_i * W2_i . f(W1_i . u, Wg_i . u)
  *   out    = W_up . v                        (out = v for the standard MoE)
- *            + sum_{j < S} Ws2_j . (max(0, Ws1_j . x))^2   shared experts
+ *            + sum_{j < S} Ws2_j . f(Ws1_j . x, Wsg_j . x)   shared experts
+ *
+ * Expert nonlinearity f (§3 parameterises an expert by W_FC1, W_gate and
+ * W_FC2; Table 2 names SwiGLU and Squared-ReLU): activation 0, the
+ * Squared-ReLU FFN, f(a, .) = (max(0, a))^2 with no gate matrix; activation
+ * 1, SwiGLU, f(a, b) = a * SiLU(b) = a * b / (1 + exp(-b)), b the gate.
  *
  * The S shared experts run on x in the d space, ungated (the second sum of
  * Eq. (1)/(2)); their nonlinearity is the routed experts' Squared-ReLU FFN
@@ -40,6 +45,7 @@ extern "C" {
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_E4M3_ROWSCALE = 2 };
 enum { ORC_SOFTMAX_ALL = 0, ORC_SOFTMAX_TOPK = 1, ORC_SIGMOID_TOPK_NORM = 2 };
+enum { ORC_SQRELU = 0, ORC_SWIGLU = 1 };
 
 typedef struct {
   int64_t d, l, m, n_experts, top_k;
@@ -51,13 +57,16 @@ typedef struct {
   int32_t expert_dtype;      /* ORC_F32 | ORC_BF16 | ORC_FP8_E4M3_ROWSCALE: W1, W2 */
   int64_t n_shared;          /* S >= 0 shared experts */
   int64_t m_shared;          /* their hidden width (> 0 when S > 0) */
+  int32_t activation;        /* ORC_SQRELU | ORC_SWIGLU */
 } orc_layer;
 
 /* Host pointers, row-major [out][in]: w_down [l][d], w_router [N][d or l],
  * router_bias [N] fp32, w1 [N][m][l], w2 [N][l][m], w1_scale [N][m],
  * w2_scale [N][l] (fp8 only), w_up [d][l]; shared experts in the activation
  * dtype: w_shared1 [S*m_shared][d] (expert j owns rows j*m_shared ..),
- * w_shared2 [d][S*m_shared] (expert j owns columns j*m_shared ..). */
+ * w_shared2 [d][S*m_shared] (expert j owns columns j*m_shared ..).  SwiGLU
+ * only: w_gate [N][m][l] in the expert dtype (+ w_gate_scale [N][m] for
+ * fp8), w_shared_gate [S*m_shared][d] in the activation dtype. */
 typedef struct {
   const void *w_down, *w_router;
   const float *router_bias;
@@ -65,6 +74,9 @@ typedef struct {
   const float *w1_scale, *w2_scale;
   const void *w_up;
   const void *w_shared1, *w_shared2;
+  const void *w_gate;
+  const float *w_gate_scale;
+  const void *w_shared_gate;
 } orc_weights;
 
 /* Sparse forward (the definition).  x holds all tokens ([*][d], act dtype).

@@ -7,8 +7,8 @@ both the fp64 oracle (``oracle/``) and the GPU library's tests and benchmark
 use, so that both sides see bit-identical inputs.
 
 Tensor stream ids: x = 0, W_down = 1, W_router = 2, W1 = 3, W2 = 4, W_up = 5,
-router-bias permutation = 6, shared W1 = 7, shared W2 = 8.  Every weight
-~ N(0, 1/fan_in); x ~ N(0, 1).
+router-bias permutation = 6, shared W1 = 7, shared W2 = 8, W_gate = 9,
+shared W_gate = 10.  Every weight ~ N(0, 1/fan_in); x ~ N(0, 1).
 """
 from __future__ import annotations
 
@@ -27,7 +27,8 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lock = threading.Lock()
 _lib = None
 
-TID_X, TID_WDOWN, TID_WROUTER, TID_W1, TID_W2, TID_WUP, TID_BIAS, TID_WS1, TID_WS2 = range(9)
+(TID_X, TID_WDOWN, TID_WROUTER, TID_W1, TID_W2, TID_WUP, TID_BIAS, TID_WS1, TID_WS2, TID_WGATE,
+ TID_WSGATE) = range(11)
 
 
 def build(force: bool = True) -> str:
@@ -135,7 +136,10 @@ def make_weights(spec: LayerSpec, seed: int = 0) -> dict:
     Keys: w_down [l][d], w_up [d][l] (absent without projections; the
     identity matrix when spec.identity_projections), w_router [N][d or l],
     router_bias [N] (fp32, only with spec.has_router_bias), w1 [N][m][l],
-    w2 [N][l][m] (+ w1_scale [N][m], w2_scale [N][l] for fp8 experts).
+    w2 [N][l][m] (+ w1_scale [N][m], w2_scale [N][l] for fp8 experts);
+    SwiGLU experts add w_gate [N][m][l] (+ w_gate_scale [N][m]); shared
+    experts w_shared1 [S*ms][d], w_shared2 [d][S*ms] and, with SwiGLU,
+    w_shared_gate [S*ms][d].
     """
     d, l, m, N = spec.d, spec.l, spec.m, spec.n_experts
     act = spec.act_dtype
@@ -162,13 +166,20 @@ def make_weights(spec: LayerSpec, seed: int = 0) -> dict:
         q2, s2 = normal_fp8_rows(seed, TID_W2, N * l, m, m ** -0.5)
         w["w1"], w["w1_scale"] = q1.reshape(N, m, l), s1.reshape(N, m)
         w["w2"], w["w2_scale"] = q2.reshape(N, l, m), s2.reshape(N, l)
+        if spec.activation == "swiglu":
+            qg, sg = normal_fp8_rows(seed, TID_WGATE, N * m, l, l ** -0.5)
+            w["w_gate"], w["w_gate_scale"] = qg.reshape(N, m, l), sg.reshape(N, m)
     else:
         w["w1"] = normal(seed, TID_W1, (N, m, l), l ** -0.5, spec.expert_dtype)
         w["w2"] = normal(seed, TID_W2, (N, l, m), m ** -0.5, spec.expert_dtype)
+        if spec.activation == "swiglu":
+            w["w_gate"] = normal(seed, TID_WGATE, (N, m, l), l ** -0.5, spec.expert_dtype)
     if spec.n_shared:
         # shared experts, in the activation dtype: w_shared1 [S*ms][d] (expert
         # j's rows j*ms ..), w_shared2 [d][S*ms] (expert j's columns j*ms ..)
         S, ms = spec.n_shared, spec.m_shared
         w["w_shared1"] = normal(seed, TID_WS1, (S * ms, d), d ** -0.5, act)
         w["w_shared2"] = normal(seed, TID_WS2, (d, S * ms), ms ** -0.5, act)
+        if spec.activation == "swiglu":
+            w["w_shared_gate"] = normal(seed, TID_WSGATE, (S * ms, d), d ** -0.5, act)
     return w

@@ -13,6 +13,7 @@ import dataclasses
 
 
 GATINGS = ("softmax_all", "softmax_topk", "sigmoid_topk_norm")
+ACTIVATIONS = ("sqrelu", "swiglu")
 ACT_DTYPES = ("f32", "bf16")
 EXPERT_DTYPES = ("f32", "bf16", "fp8_e4m3_rowscale")
 
@@ -34,11 +35,13 @@ class LayerSpec:
     zipf_s: float = 1.1                  # exponent of the log-Zipf router bias
     n_shared: int = 0                    # shared experts S (Eq. (1)/(2)), in the d space
     m_shared: int = 0                    # their hidden width
+    activation: str = "sqrelu"           # expert FFN: squared ReLU, or SwiGLU (W_FC1, W_gate, W_FC2)
 
     def __post_init__(self):
         assert self.gating in GATINGS, self.gating
         assert self.act_dtype in ACT_DTYPES, self.act_dtype
         assert self.expert_dtype in EXPERT_DTYPES, self.expert_dtype
+        assert self.activation in ACTIVATIONS, self.activation
 
     def replace(self, **kw) -> "LayerSpec":
         return dataclasses.replace(self, **kw)
