@@ -40,22 +40,24 @@ def expert_kernel_work(spec, T, counts, stage):
     amount of expert weights, the T*K activated rows, and writes T*K latent
     rows.  FLOPs: 2 * T*K * l * m per launch.  The fused kernel reads both
     weight sets and each latent row once and writes the T*K latent rows; the
-    activated rows stay on chip.
+    activated rows stay on chip.  SwiGLU experts: FC1 reads 2m weight rows
+    (up and gate) per expert and does twice the FLOPs.
     """
     touched = int((counts > 0).sum())
     eb = spec.expert_bytes
     ab = spec.act_bytes
     l, m, K = spec.l, spec.m, spec.top_k
-    w = touched * l * m * eb
+    m1 = 2 * m if spec.activation == "swiglu" else m
+    w1 = touched * l * m1 * eb
+    w2 = touched * l * m * eb
     if spec.expert_dtype == "fp8_e4m3_rowscale":
-        w += touched * (m if stage == "fc1" else l) * 4
+        w1 += touched * m1 * 4
+        w2 += touched * l * 4
     if stage == "ffn":
-        return float(2 * w + T * l * ab + T * K * l * ab), 4.0 * T * K * l * m
+        return float(w1 + w2 + T * l * ab + T * K * l * ab), 2.0 * T * K * l * (m1 + m)
     if stage == "fc1":
-        b = w + T * l * ab + T * K * m * ab
-    else:
-        b = w + T * K * m * ab + T * K * l * ab
-    return float(b), 2.0 * T * K * l * m
+        return float(w1 + T * l * ab + T * K * m * ab), 2.0 * T * K * l * m1
+    return float(w2 + T * K * m * ab + T * K * l * ab), 2.0 * T * K * l * m
 
 
 def layer_work(spec, T, counts):
@@ -65,24 +67,26 @@ def layer_work(spec, T, counts):
     intermediates a fused implementation keeps on chip, so they are not
     counted); FLOPs 2*T*d*l per projection, 2*T*r_in*N for the router,
     4*T*K*l*m for the routed experts and 4*T*d*S*m_s for the shared ones
-    (whose weights, 2*d*S*m_s elements, are read once)."""
+    (whose weights, 2*d*S*m_s elements, are read once); SwiGLU experts have
+    a third matrix of the FC1 shape (6*T*K*l*m, 3*d*S*m_s)."""
     d, l, m, N, K = spec.d, spec.l, spec.m, spec.n_experts, spec.top_k
     a, eb = spec.act_bytes, spec.expert_bytes
     r_in = l if spec.router_on_latent else d
     touched = int((counts > 0).sum())
-    per_expert = 2.0 * l * m * eb
+    nmat = 3 if spec.activation == "swiglu" else 2   # m x l matrices per expert
+    per_expert = nmat * l * m * eb
     if spec.expert_dtype == "fp8_e4m3_rowscale":
-        per_expert += 4.0 * (m + l)
+        per_expert += 4.0 * ((nmat - 1) * m + l)
     nbytes = touched * per_expert + N * r_in * a + 2.0 * T * d * a
     if spec.has_router_bias:
         nbytes += 4.0 * N
-    flops = 2.0 * T * r_in * N + 4.0 * T * K * l * m
+    flops = 2.0 * T * r_in * N + 2.0 * nmat * T * K * l * m
     if spec.has_projections:
         nbytes += 2.0 * l * d * a
         flops += 4.0 * T * d * l
     hs = spec.n_shared * spec.m_shared
-    nbytes += 2.0 * d * hs * a
-    flops += 4.0 * T * d * hs
+    nbytes += nmat * d * hs * a
+    flops += 2.0 * nmat * T * d * hs
     return nbytes, flops
 
 
@@ -116,6 +120,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--overlap", choices=("on", "off"), default="on",
                     help="shared experts on a side stream (on) or first on the launch stream")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per call (default: the workload's batch)")
+    ap.add_argument("--expert-kernel", choices=("auto", "tiled", "stream", "fused"),
+                    default="auto", help="force one expert-FFN kernel (default: the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known HBM traffic: "
                          "1 GiB read + 1 GiB written per launch) to scale rocprofv3 "
@@ -143,17 +151,17 @@ def main():
         return
 
     wl = synth.workload(args.workload)
-    spec, T = wl.spec, wl.T
+    spec, T = wl.spec, (args.tokens or wl.T)
     dev = torch.device("cuda:0")
     log("bench: workload %s T=%d: generating inputs" % (wl.name, T))
     t0 = time.perf_counter()
     w_np = synth.make_weights(spec, seed=0)
     x_np = synth.make_tokens(spec, T, seed=0)
-    d_all = pkg.to_device(dict(w_np, x=x_np), dev)
+    d_all = pkg.to_device(pkg.pack_gated(dict(w_np, x=x_np)), dev)
     torch.cuda.synchronize()
     log("bench: inputs on device in %.1f s" % (time.perf_counter() - t0))
 
-    layer = pkg.LatentMoELayer(spec)
+    layer = pkg.LatentMoELayer(spec, expert_kernel=args.expert_kernel)
     cw = layer.weights_struct(d_all)
     x = d_all["x"]
     act = torch.float32 if spec.act_dtype == "f32" else torch.bfloat16
@@ -273,7 +281,9 @@ def main():
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "gating": spec.gating,
                    "expert_dtype": spec.expert_dtype, "parallelism": "single GPU",
                    "n_shared": spec.n_shared, "m_shared": spec.m_shared,
-                   "shared_on_side_stream": overlap is not None},
+                   "activation": spec.activation,
+                   "shared_on_side_stream": overlap is not None,
+                   "expert_kernel": layer.expert_regime(T)},
         "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
         "latency_ms": {k: round(v, 5) for k, v in pct.items()},
         "roofline": roof,
@@ -283,8 +293,9 @@ def main():
         # the shared experts' two dense GEMMs (their stage's events, on the
         # stream they ran on; beside the routed path they share the GPU)
         hs = spec.n_shared * spec.m_shared
-        sf = 4.0 * T * spec.d * hs
-        sb = 2.0 * spec.d * hs * spec.act_bytes + T * spec.d * spec.act_bytes + \
+        nmat = 3 if spec.activation == "swiglu" else 2
+        sf = 2.0 * nmat * T * spec.d * hs
+        sb = nmat * spec.d * hs * spec.act_bytes + T * spec.d * spec.act_bytes + \
             2.0 * T * hs * spec.act_bytes + T * spec.d * 4.0
         t_sh = stage_avg["shared"] * 1e-3
         res["shared_stage"] = {"ms": round(stage_avg["shared"], 5),

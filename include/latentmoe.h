@@ -9,6 +9,8 @@
  *   T   = K experts with the largest z  ties go to the lower expert id
  *   v   = sum_{i in T} g_i E_i(u; l)    E_i(u) = W2_i . (max(0, W1_i . u))^2,
  *                                       W1_i in R^{m x l}, W2_i in R^{l x m}
+ *                                       (SwiGLU experts, §3's W_FC1, W_gate, W_FC2:
+ *                                       E_i(u) = W2_i . ((W1_i . u) * SiLU(Wg_i . u)))
  *   out = W_up . v + sum_{j < S} E_j(x; d)       W_up in R^{d x l}
  *
  * The S shared experts (the second sum of Eq. (1)/(2)) run on x in the d
@@ -75,7 +77,10 @@ typedef enum {
 } lmoe_gating;
 
 typedef enum {
-  LMOE_ACT_SQRELU = 0             /* non-gated expert FFN with (max(0, a))^2 (Table 2: Squared-ReLU) */
+  LMOE_ACT_SQRELU = 0,            /* non-gated expert FFN with (max(0, a))^2 (Table 2: Squared-ReLU) */
+  LMOE_ACT_SWIGLU = 1             /* gated: (W_FC1 . u) * SiLU(W_gate . u), SiLU(b) = b / (1 + e^-b)
+                                     (§3's expert matrices; Table 2: SwiGLU).  The FC1 and gate
+                                     matrices are passed interleaved by rows, see lmoe_weights */
 } lmoe_activation;
 
 /* Expert-FFN kernels (the grouped latent expert FFN of Eq. (2)).  AUTO picks
@@ -114,7 +119,12 @@ typedef struct {
   int64_t m_shared;         /* their FFN width, a multiple of 16 (read when n_shared > 0) */
 } lmoe_config;
 
-/* Device pointers; shapes use the config's d, l, m, N. */
+/* Device pointers; shapes use the config's d, l, m, N.  With SwiGLU experts
+ * (activation LMOE_ACT_SWIGLU) the up-projection and gate matrices travel
+ * as one interleaved matrix: w1 is [N][2m][l] with row 2i = W_FC1 row i and
+ * row 2i + 1 = W_gate row i of the expert (w1_scale [N][2m] likewise), and
+ * w_shared1 is [2*S*m_shared][d] with row 2k = Ws_FC1 row k and row 2k + 1 =
+ * Ws_gate row k (expert j's rows start at 2*j*m_shared). */
 typedef struct {
   const void *w_down;       /* [l][d] act dtype; NULL without projections */
   const void *w_router;     /* [N][d] (ROUTER_ON_X) or [N][l] (ROUTER_ON_LATENT), act dtype */

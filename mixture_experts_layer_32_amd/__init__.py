@@ -23,7 +23,8 @@ LIB_PATH = os.environ.get("LATENTMOE_LIB") or os.path.join(HERE, "liblatentmoe.s
 LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE = 0, 1, 2
 ROUTER_ON_X, ROUTER_ON_LATENT = 0, 1
 GATE_SOFTMAX_ALL, GATE_SOFTMAX_TOPK, GATE_SIGMOID_TOPK_NORM = 0, 1, 2
-ACT_SQRELU = 0
+ACT_SQRELU, ACT_SWIGLU = 0, 1
+_ACT = {"sqrelu": ACT_SQRELU, "swiglu": ACT_SWIGLU}
 # expert-FFN kernel choice (lmoe_expert_kernel); every choice computes the same layer
 EXPERTS_AUTO, EXPERTS_TILED, EXPERTS_STREAM, EXPERTS_FUSED = 0, 1, 2, 3
 _EXPERT_KERNEL = {"auto": EXPERTS_AUTO, "tiled": EXPERTS_TILED, "stream": EXPERTS_STREAM,
@@ -86,6 +87,12 @@ def lib():
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError("liblatentmoe.so is not built (run __graft_entry__.build() or "
                                    "python mixture_experts_layer_32_amd/build.py)")
+            # torch carries its own HIP runtime under the same soname as the
+            # system one: load it first, so that the library binds to the
+            # runtime that owns the tensors' memory (loaded the other way
+            # round, the process holds two runtimes and the library's sees
+            # no device)
+            _torch()
             L = ctypes.CDLL(LIB_PATH)
             vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
             L.latentmoe_create.argtypes = [ctypes.POINTER(LmoeConfig), ctypes.POINTER(vp)]
@@ -129,7 +136,8 @@ def make_config(spec, expert_kernel: str = "auto") -> LmoeConfig:
     expert_kernel: "auto", "tiled", "stream" or "fused" (lmoe_expert_kernel)."""
     return LmoeConfig(spec.d, spec.l, spec.m, spec.n_experts, spec.top_k,
                       ROUTER_ON_LATENT if spec.router_on_latent else ROUTER_ON_X,
-                      _GATE[spec.gating], ACT_SQRELU, _DT[spec.act_dtype], _DT[spec.expert_dtype],
+                      _GATE[spec.gating], _ACT[getattr(spec, "activation", "sqrelu")],
+                      _DT[spec.act_dtype], _DT[spec.expert_dtype],
                       int(spec.has_projections), int(spec.has_router_bias),
                       _EXPERT_KERNEL[expert_kernel], getattr(spec, "n_shared", 0),
                       getattr(spec, "m_shared", 0))
@@ -247,9 +255,13 @@ class LatentMoELayer:
         else:
             edt = (torch.uint8, torch.float8_e4m3fn)
         r_in = s.l if s.router_on_latent else s.d
+        glu = getattr(s, "activation", "sqrelu") == "swiglu"
+        m1 = 2 * s.m if glu else s.m  # W1 rows: (up, gate) pairs with SwiGLU
+        if glu and "w_gate" in w:
+            raise ValueError("SwiGLU weights go in interleaved: pass pack_gated(weights)")
         cw = LmoeWeights()
         cw.w_router = self._expect("w_router", w.get("w_router"), (s.n_experts, r_in), act)
-        cw.w1 = self._expect("w1", w.get("w1"), (s.n_experts, s.m, s.l), edt)
+        cw.w1 = self._expect("w1", w.get("w1"), (s.n_experts, m1, s.l), edt)
         cw.w2 = self._expect("w2", w.get("w2"), (s.n_experts, s.l, s.m), edt)
         if s.has_projections:
             cw.w_down = self._expect("w_down", w.get("w_down"), (s.l, s.d), act)
@@ -258,14 +270,15 @@ class LatentMoELayer:
             cw.router_bias = self._expect("router_bias", w.get("router_bias"), (s.n_experts,),
                                           (torch.float32,))
         if s.expert_dtype == "fp8_e4m3_rowscale":
-            cw.w1_scale = self._expect("w1_scale", w.get("w1_scale"), (s.n_experts, s.m),
+            cw.w1_scale = self._expect("w1_scale", w.get("w1_scale"), (s.n_experts, m1),
                                        (torch.float32,))
             cw.w2_scale = self._expect("w2_scale", w.get("w2_scale"), (s.n_experts, s.l),
                                        (torch.float32,))
         S = getattr(s, "n_shared", 0)
         if S:
             hs = S * s.m_shared
-            cw.w_shared1 = self._expect("w_shared1", w.get("w_shared1"), (hs, s.d), act)
+            cw.w_shared1 = self._expect("w_shared1", w.get("w_shared1"),
+                                        (2 * hs if glu else hs, s.d), act)
             cw.w_shared2 = self._expect("w_shared2", w.get("w_shared2"), (s.d, hs), act)
         return cw
 
@@ -331,6 +344,32 @@ def debug_buffers(spec, T: int, device="cuda") -> dict:
     if spec.has_projections:
         d["latent"] = torch.empty((T, spec.l), dtype=act, device=device)
     return d
+
+
+def pack_gated(weights: dict) -> dict:
+    """SwiGLU weights in the interleaved layout the library reads: W_FC1 and
+    W_gate ([N][m][l]) become one [N][2m][l] matrix whose rows alternate
+    (up, gate); row scales and the shared experts' matrices likewise.  Works
+    on numpy arrays or torch tensors; other keys pass through."""
+    if "w_gate" not in weights:
+        return dict(weights)
+    out = {k: v for k, v in weights.items()
+           if k not in ("w_gate", "w_gate_scale", "w_shared_gate")}
+
+    def inter(a, g, axis):
+        if hasattr(a, "dim"):                      # torch
+            t = _torch().stack([a, g], dim=axis + 1)
+            return t.reshape(*a.shape[:axis], 2 * a.shape[axis], *a.shape[axis + 1:])
+        import numpy as np
+        t = np.stack([a, g], axis=axis + 1)
+        return t.reshape(a.shape[:axis] + (2 * a.shape[axis],) + a.shape[axis + 1:])
+
+    out["w1"] = inter(weights["w1"], weights["w_gate"], 1)
+    if "w1_scale" in weights:
+        out["w1_scale"] = inter(weights["w1_scale"], weights["w_gate_scale"], 1)
+    if "w_shared1" in weights:
+        out["w_shared1"] = inter(weights["w_shared1"], weights["w_shared_gate"], 0)
+    return out
 
 
 def to_device(arrays: dict, device="cuda") -> dict:

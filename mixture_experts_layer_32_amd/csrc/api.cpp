@@ -67,13 +67,22 @@ constexpr int64_t kMaxExperts = 2048;
 constexpr int64_t kMaxTopK = 64;
 constexpr int64_t kMaxShared = 64;
 constexpr int64_t kMaxCopies = int64_t(1) << 30;  // T * K (int32 row indices)
-constexpr double kStreamMaxRowsPerExpert = 96.0;  // mean copies per expert -> streaming kernel
+// mean copies per expert up to which the streaming kernel beats the tiled one
+// (measured on the standard MoE d 4096, m 1536, 128 experts at 32 and 40 rows
+// and on latent layers with l 512 and 1024 at 24 to 96 rows: from 48 rows on
+// the tiled kernel is as fast or faster)
+constexpr double kStreamMaxRowsPerExpert = 40.0;
 // fp8 weights: the tiled kernel (one weight tile per expert and 256 columns,
 // token rows staged once per tile) from this many rows per expert on
 #ifndef LMOE_FP8_STREAM_MAX_ROWS
 #define LMOE_FP8_STREAM_MAX_ROWS 40.0
 #endif
 constexpr double kFp8StreamMaxRowsPerExpert = LMOE_FP8_STREAM_MAX_ROWS;
+// streaming kernel: passes of 64 rows (4 MFMA row blocks, 128 columns per
+// unit) up to this mean row count per expert, of 128 rows (64 columns) above
+#ifndef LMOE_STREAM_MB4_MAX_ROWS
+#define LMOE_STREAM_MB4_MAX_ROWS 40.0
+#endif
 // fused expert FFN (bf16): up to this many copies per expert on average, so
 // that few experts exceed the kernel's 48-row pass
 constexpr double kFusedMaxRowsPerExpert = 36.0;
@@ -194,7 +203,7 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
                 lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m)) &&
                 c.n_experts >= kComputeUnits;
   }
-  p.mb_max = mean <= 40.0 ? 4 : 8;
+  p.mb_max = mean <= LMOE_STREAM_MB4_MAX_ROWS ? 4 : 8;
   p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 1;  // fp32: the 64 x 64 tile
   p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
   const size_t ab = act_bytes(c);
@@ -235,17 +244,19 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   // shared experts: their own partial region (they may run beside the routed path)
   const int64_t hs = c.n_shared * c.m_shared;
   size_t partial_sh = 0;
+  // SwiGLU: the shared FC1 computes 2 * hs columns (up, gate pairs)
+  const int64_t hs1 = c.activation == LMOE_ACT_SWIGLU ? 2 * hs : hs;
   if (hs > 0) {
     if (LMOE_SHARED_PLAN == 0 || ab != 2) {
-      p.sh1 = plan_dense(T, hs, c.d, ab, ab == 2);
+      p.sh1 = plan_dense(T, hs1, c.d, ab, ab == 2);
       p.sh2 = plan_dense(T, c.d, hs, ab, false);
     } else {
-      p.sh1 = plan_dense_128(T, hs, c.d, ab, LMOE_SHARED_PLAN);
+      p.sh1 = plan_dense_128(T, hs1, c.d, ab, LMOE_SHARED_PLAN);
       p.sh2 = plan_dense_128(T, c.d, hs, ab, LMOE_SHARED_PLAN);
-      const int64_t t256 = ((T + 255) / 256) * ((hs + 255) / 256);
-      if (t256 >= kComputeUnits) p.sh1 = plan_dense(T, hs, c.d, ab, true);
+      const int64_t t256 = ((T + 255) / 256) * ((hs1 + 255) / 256);
+      if (t256 >= kComputeUnits) p.sh1 = plan_dense(T, hs1, c.d, ab, true);
     }
-    partial_sh = std::max(size_t(p.sh1.splits > 1 ? p.sh1.splits : 0) * T * hs * 4,
+    partial_sh = std::max(size_t(p.sh1.splits > 1 ? p.sh1.splits : 0) * T * hs1 * 4,
                           size_t(p.sh2.splits > 1 ? p.sh2.splits : 0) * T * c.d * 4);
   }
   size_t o = 0;
@@ -313,8 +324,8 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
     return fail(LMOE_ERR_INVALID_ARG, "create: bad gating");
   if (c.has_router_bias != 0 && c.has_router_bias != 1)
     return fail(LMOE_ERR_INVALID_ARG, "create: has_router_bias must be 0 or 1");
-  if (c.activation != LMOE_ACT_SQRELU)
-    return fail(LMOE_ERR_UNSUPPORTED, "create: only the squared-ReLU expert FFN is implemented");
+  if (c.activation != LMOE_ACT_SQRELU && c.activation != LMOE_ACT_SWIGLU)
+    return fail(LMOE_ERR_INVALID_ARG, "create: bad activation");
   if (c.act_dtype < LMOE_F32 || c.act_dtype > LMOE_FP8_E4M3_ROWSCALE ||
       c.expert_dtype < LMOE_F32 || c.expert_dtype > LMOE_FP8_E4M3_ROWSCALE)
     return fail(LMOE_ERR_INVALID_ARG, "create: bad dtype");
@@ -486,6 +497,9 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  // expert FC1: squared ReLU, or SwiGLU over interleaved (up, gate) weight rows
+  const bool glu = c.activation == LMOE_ACT_SWIGLU;
+  const int act1 = glu ? lmoe::kActSwiGlu : lmoe::kActSqRelu;
   const lmoe::Dt adt = act_dt(c), edt = exp_dt(c);
   const int ab = static_cast<int>(act_bytes(c));
   const int Ti = static_cast<int>(T), N = static_cast<int>(c.n_experts), K = static_cast<int>(c.top_k);
@@ -547,7 +561,7 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     const int hs = static_cast<int>(c.n_shared * c.m_shared);
     lmoe::GemmArgs a;
     a.A = x; a.lda = d; a.B = w->w_shared1; a.ldb = d; a.C = Hs; a.ldc = hs;
-    a.M = Ti; a.N = hs; a.K = d; a.act = lmoe::kActSqRelu;
+    a.M = Ti; a.N = glu ? 2 * hs : hs; a.K = d; a.act = act1;
     LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.sh1.tile, ss, p.sh1.splits, partial_sh),
              "shared FC1 GEMM");
     lmoe::GemmArgs b;
@@ -639,16 +653,18 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.Y = Y; a.ldy = l;
     a.g_off = offsets; a.G = N;
     a.l = static_cast<int>(l); a.m = static_cast<int>(m);
+    a.act = act1;
     LMOE_TRY(lmoe::launch_ffn_stream(a, s), "FC1 + FC2 (fused)");
   } else {
     lmoe::GemmArgs a;
     a.A = u; a.lda = l; a.a_rows = token_of; a.a_nrows = Ti;
-    a.B = w->w1; a.ldb = l; a.b_gstride = int64_t(m) * l;
-    a.b_scale = edt == lmoe::Dt::FP8 ? w->w1_scale : nullptr; a.s_gstride = m;
+    const int n1 = glu ? 2 * m : m;  // W1 rows
+    a.B = w->w1; a.ldb = l; a.b_gstride = int64_t(n1) * l;
+    a.b_scale = edt == lmoe::Dt::FP8 ? w->w1_scale : nullptr; a.s_gstride = n1;
     a.C = H; a.ldc = m;
-    a.N = m; a.K = l;
+    a.N = n1; a.K = l;
     a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);
-    a.act = lmoe::kActSqRelu;
+    a.act = act1;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC1 (tiled, fp8)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");

@@ -208,6 +208,12 @@ struct MmaF32 {
 
 // ---------------------------------------------------------------- epilogue
 
+// SwiGLU output from an up-projection value and its gate: up * SiLU(gate),
+// SiLU(b) = b / (1 + e^-b)
+__device__ __forceinline__ float swiglu(float up, float gate) {
+  return up * (gate / (1.f + expf(-gate)));
+}
+
 template <int ACT>
 __device__ __forceinline__ float apply_act(float v) {
   if constexpr (ACT == kActSqRelu) {

@@ -4,7 +4,9 @@
 //   Y = H W2_g^T             rows of expert g  x  l   (written to HBM, bf16)
 //
 // (the expert FFN of the LatentMoE paper, Eq. (2): both expert GEMMs run in
-// the latent width l, with the squared-ReLU activation of Table 2).
+// the latent width l, with the squared-ReLU activation of Table 2).  With
+// SwiGLU experts W1 holds 2m rows, up-projection and gate rows interleaved,
+// and H[i] = up_i * SiLU(gate_i): FC1 streams twice the rows.
 //
 // With a few dozen token rows per expert both GEMMs are bound by streaming
 // the expert weights from HBM.  Writing H out and reading it back, as two
@@ -84,6 +86,7 @@ struct FfnUnit {
   }
 };
 
+template <bool GLU>
 __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   __shared__ u32x4 Hs[kRows * kMaxM / 8];  // H, 16-byte chunk c of row r at c ^ (r & 7)
   __shared__ u32x4 As[2][kAChunks];        // FC1 token stages, chunk c of row r at c ^ ((r >> 1) & 7)
@@ -93,13 +96,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   const int L = p.l, M = p.m;
+  const int N1 = GLU ? 2 * M : M;            // FC1 weight rows (H columns x 2 with SwiGLU)
   const int mh = (M + kKE - 1) / kKE * kKE;  // H row length: m rounded up to a stage
   const int hcpr = mh / 8;                   // 16-byte chunks per H row
   const int s1 = (L + kKE - 1) / kKE;        // FC1 stages (reduction over l)
   const int s2 = mh / kKE;                   // FC2 stages (reduction over m)
   const int s1p = (s1 + kP - 1) / kP * kP;
   const int s2p = (s2 + kP - 1) / kP * kP;
-  const int t1 = (M + kTileN - 1) / kTileN;  // FC1 tiles (H columns)
+  const int t1 = (N1 + kTileN - 1) / kTileN; // FC1 tiles (of W1 rows)
   const int t2 = (L + kTileN - 1) / kTileN;  // FC2 tiles (Y columns)
   const uint32_t rb1 = static_cast<uint32_t>(L) * 2u;  // W1 row bytes
   const uint32_t rb2 = static_cast<uint32_t>(M) * 2u;  // W2 row bytes
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
     u.e = e;
     u.valid = e < p.G;
     const int64_t ee = u.valid ? e : 0;
-    u.w1 = make_rsrc(w1g + ee * M * L, (uint64_t)M * rb1);
+    u.w1 = make_rsrc(w1g + ee * N1 * L, (uint64_t)N1 * rb1);
     u.w2 = make_rsrc(w2g + ee * L * M, (uint64_t)L * rb2);
     u.gs = 0;
     u.cnt = 0;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   // weight chunks of stage ks of tile t of GEMM ph
   auto load_w = [&](const FfnUnit& u, int ph, int t, int ks, bool live,
                     u32x4 (&br)[kNWB][kNLD]) {
-    const int N = ph == 0 ? M : L;
+    const int N = ph == 0 ? N1 : L;
     const uint32_t rb = ph == 0 ? rb1 : rb2;
     const bool lv = live && ks < (ph == 0 ? s1 : s2);
     const uint32_t so = static_cast<uint32_t>(ks) * (kKE * 2) + 16u * fq;
@@ -328,7 +332,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
             const int n0 = t * kTileN + wave * (kNWB * 16) + nb * 16 + 4 * fq;
             const f32x4_t a = acc[mb][nb];
             if (ph == 0) {
-              if (n0 < M) {
+              if (GLU) {
+                // columns (n0, n0 + 1), (n0 + 2, n0 + 3) are (up, gate) pairs:
+                // H columns n0 / 2 and n0 / 2 + 1, one 4-byte piece
+                const int c = n0 >> 1;
+                if (n0 < N1)
+                  *(reinterpret_cast<uint32_t*>(&Hs[r * hcpr + ((c >> 3) ^ (r & 7))]) + ((c >> 1) & 3)) =
+                      pack_bf16x2(swiglu(a[0], a[1]), swiglu(a[2], a[3]));
+              } else if (n0 < M) {
                 const uint2 h{pack_bf16x2(apply_act<kActSqRelu>(a[0]), apply_act<kActSqRelu>(a[1])),
                               pack_bf16x2(apply_act<kActSqRelu>(a[2]), apply_act<kActSqRelu>(a[3]))};
                 *(reinterpret_cast<uint2*>(&Hs[r * hcpr + ((n0 >> 3) ^ (r & 7))]) + ((n0 >> 2) & 1)) = h;
@@ -358,14 +369,16 @@ int ffn_stream_rows() { return kRows; }
 
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s) {
   if (!ffn_stream_fits(a.l, a.m) || a.G < 1 || !a.g_off || !a.a_rows || a.ldy % 4 ||
-      a.lda < a.l)
+      a.lda < a.l || (a.act != kActSqRelu && a.act != kActSwiGlu))
     return hipErrorInvalidValue;
+  const bool glu = a.act == kActSwiGlu;
   // 32-bit buffer offsets: token rows and one expert matrix stay below 2 GiB
   if ((uint64_t)a.a_nrows * a.lda * 2u >= (1ull << 31) ||
-      (uint64_t)a.m * a.l * 2u >= (1ull << 31))
+      (uint64_t)(glu ? 2 : 1) * a.m * a.l * 2u >= (1ull << 31))
     return hipErrorInvalidValue;
   const int grid = std::min(a.G, device_compute_units());
-  ffn_stream_kernel<<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+  if (glu) ffn_stream_kernel<true><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+  else ffn_stream_kernel<false><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

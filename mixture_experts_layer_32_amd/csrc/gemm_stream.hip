@@ -2,6 +2,7 @@
 // receives few token copies (decode regime), for gfx950.
 //
 // C[r][n] = act(scale[g][n] * sum_k A[arow(r)][k] * W[g][n][k]),  r in group g
+// (SwiGLU: W's rows are (up, gate) pairs and C[r][i] = up_i * SiLU(gate_i))
 //
 // With a few dozen rows per expert the GEMM is bound by reading the expert
 // weights from HBM once, so the kernel is built around that stream:
@@ -148,7 +149,10 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
   constexpr int MROWS = MB_MAX * 16;
   constexpr int NT = 4 * NWB * 16;                    // output columns per unit
   constexpr int WD = S::WD, P = S::P, NLD = S::NLD, NS = S::NS, KE = S::KE, EPC = S::EPC;
-  constexpr int CPR = NT * static_cast<int>(sizeof(TOut)) / 16;  // 16-byte chunks per tile row
+  // SwiGLU: weight-row pairs (up, gate) give one output column each
+  constexpr bool GLU = ACT == kActSwiGlu;
+  constexpr int NTO = GLU ? NT / 2 : NT;               // output columns per unit
+  constexpr int CPR = NTO * static_cast<int>(sizeof(TOut)) / 16;  // 16-byte chunks per tile row
   __shared__ u32x4 As[2][MROWS * kStageChunks];
   __shared__ u32x4 Cs[MROWS * CPR];
 
@@ -364,16 +368,26 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
           for (int v = 0; v < 4; ++v) {
             float val = acc[mb][nb][v];
             if (SCALE) val *= sc;
-            store_elem<TOut>(Ct + (mb * 16 + fq * 4 + v) * NT + colt, apply_act<ACT>(val));
+            if constexpr (GLU) {
+              // a lane holds one column: the gate of an even (up) column is
+              // in the next lane, which holds the odd column
+              const float gate = __shfl_xor(val, 1);
+              if ((fr & 1) == 0)
+                store_elem<TOut>(Ct + (mb * 16 + fq * 4 + v) * NTO + colt / 2, swiglu(val, gate));
+            } else {
+              store_elem<TOut>(Ct + (mb * 16 + fq * 4 + v) * NT + colt, apply_act<ACT>(val));
+            }
           }
         }
       }
       lds_barrier();
       const int64_t row0 = (int64_t)cur.gs + cur.p0;
+      const int n_out = GLU ? p.N / 2 : p.N;
+      const int col0_out = GLU ? cur.col0 / 2 : cur.col0;
       for (int q = tid; q < cur.rows * CPR; q += 256) {
         const int r = q / CPR, ch = q % CPR;
-        const int col = cur.col0 + ch * (16 / static_cast<int>(sizeof(TOut)));
-        if (col < p.N)  // N is a multiple of 16 elements: a chunk is all in or all out
+        const int col = col0_out + ch * (16 / static_cast<int>(sizeof(TOut)));
+        if (col < n_out)  // the output width is a multiple of 16 elements: a chunk is all in or all out
           *reinterpret_cast<u32x4*>(C + (row0 + r) * p.ldc + col) = Cs[q];
       }
     }
@@ -408,6 +422,7 @@ hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   // the epilogue stores whole 16-byte chunks: output width and stride are
   // multiples of 16 elements (true of the expert widths m and l)
   if (a.N % 16 || a.ldc % 16) return hipErrorInvalidValue;
+  if (a.act == kActSwiGlu && (a.N % 32 || a.ldc < a.N / 2)) return hipErrorInvalidValue;
   // 32-bit buffer offsets: token rows and one expert matrix stay below 2 GiB
   const uint64_t a_rows = a.a_rows ? (uint64_t)a.a_nrows : (uint64_t)a.max_rows;
   if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) ||
@@ -422,6 +437,9 @@ hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
   if (a.act == kActSqRelu) {
     if (scale) gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActSqRelu, true><<<dim3(grid), dim3(256), 0, s>>>(a);
     else gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActSqRelu, false><<<dim3(grid), dim3(256), 0, s>>>(a);
+  } else if (a.act == kActSwiGlu) {
+    if (scale) gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActSwiGlu, true><<<dim3(grid), dim3(256), 0, s>>>(a);
+    else gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActSwiGlu, false><<<dim3(grid), dim3(256), 0, s>>>(a);
   } else {
     if (scale) gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActNone, true><<<dim3(grid), dim3(256), 0, s>>>(a);
     else gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, kActNone, false><<<dim3(grid), dim3(256), 0, s>>>(a);

@@ -97,6 +97,17 @@ template <>
 __device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
   *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
 }
+// two consecutive output values (4 or 8 bytes, aligned)
+template <typename TOut>
+__device__ __forceinline__ void store2(TOut* p, float a, float b);
+template <>
+__device__ __forceinline__ void store2<uint16_t>(uint16_t* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+}
+template <>
+__device__ __forceinline__ void store2<float>(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = float2{a, b};
+}
 
 // TB: element type of B (TA, or uint8_t for OCP E4M3 weights with one fp32
 // scale per row of B, applied in the epilogue; fp8 fragments are widened to
@@ -324,7 +335,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   // ---- epilogue through LDS: direct output (scale, act, convert) or fp32 partial
   const float* sc = SCALE ? p.b_scale + (int64_t)g * p.s_gstride : nullptr;
   if (partial == nullptr) {
-    constexpr int LDT = BN + OPAD;  // LDS tile row stride (elements)
+    // SwiGLU: column pairs (up, gate) become one output column, the tile is
+    // BN / 2 wide
+    constexpr bool GLU = ACT == kActSwiGlu;
+    constexpr int BNO = GLU ? BN / 2 : BN;
+    constexpr int LDT = BNO + OPAD;  // LDS tile row stride (elements)
     static_assert(OUT_T <= sizeof(smem), "output tile must fit LDS");
     TOut* Ct = reinterpret_cast<TOut*>(smem);
     // blocks are held transposed (B fragment first in the MFMA): each group of
@@ -349,6 +364,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
             if (SCALE) val[e] *= s4[e];
             val[e] = apply_act<ACT>(val[e]);
           }
+          if constexpr (GLU) {
+            store2<TOut>(Ct + (wm * WM + i * BLK + trow) * LDT + colt / 2, swiglu(val[0], val[1]),
+                         swiglu(val[2], val[3]));
+            continue;
+          }
           // residual (dense, N % 4 == 0: the 4 columns are in or out together)
           const int lr = wm * WM + i * BLK + trow;
           if (p.R != nullptr && lr < rows && col0 + colt < p.N) {
@@ -362,20 +382,22 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
       }
     __syncthreads();
     constexpr int EPO = 16 / sizeof(TOut);
-    constexpr int CPR = BN / EPO;
+    constexpr int CPR = BNO / EPO;
     TOut* C = static_cast<TOut*>(p.C);
+    const int n_out = GLU ? p.N / 2 : p.N;
+    const int col_out = GLU ? col0 / 2 : col0;
     // whole 16-byte chunks where the row stride keeps them aligned and the
     // chunk lies inside N; element stores otherwise (e.g. N = expert count)
     const bool aligned = (p.ldc % EPO) == 0;
     for (int q = tid; q < rows * CPR; q += NT) {
       const int r = q / CPR, ch = q % CPR;
-      const int col = col0 + ch * EPO;
+      const int col = col_out + ch * EPO;
       TOut* dst = C + (int64_t)(row0 + r) * p.ldc + col;
       const TOut* src = Ct + r * LDT + ch * EPO;
-      if (aligned && col + EPO <= p.N) {
+      if (aligned && col + EPO <= n_out) {
         *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
       } else {
-        for (int e = 0; e < EPO && col + e < p.N; ++e) dst[e] = src[e];
+        for (int e = 0; e < EPO && col + e < n_out; ++e) dst[e] = src[e];
       }
     }
   } else if constexpr (PARTIAL_OK) {
@@ -421,6 +443,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t mn = (int64_t)M * N;
   f32x4_t s = *reinterpret_cast<const f32x4_t*>(P + (int64_t)r * N + c);
   for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4_t*>(P + z * mn + (int64_t)r * N + c);
+  if constexpr (ACT == kActSwiGlu) {  // columns (c, c+1), (c+2, c+3) -> c/2, c/2 + 1
+    float v4[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) v4[v] = SCALE ? s[v] * scale[c + v] : s[v];
+    store_elem<TOut>(C + (int64_t)r * ldc + c / 2, swiglu(v4[0], v4[1]));
+    store_elem<TOut>(C + (int64_t)r * ldc + c / 2 + 1, swiglu(v4[2], v4[3]));
+    return;
+  }
   f32x4_t res = {0.f, 0.f, 0.f, 0.f};
   if (R != nullptr) res = *reinterpret_cast<const f32x4_t*>(R + (int64_t)r * ldr + c);
 #pragma unroll
@@ -455,12 +485,17 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
                (uint64_t)a.N0 * a.ldb * sizeof(TB) >= (1ull << 31)))
     return hipErrorInvalidValue;
   // residual: dense, whole 4-column groups, 16-byte aligned rows
-  if (a.R && (a.g_off || a.N % 4 || a.ldr % 4 || a.ldr < a.N ||
+  if (a.R && (a.g_off || a.N % 4 || a.ldr % 4 || a.ldr < a.N || a.act != kActNone ||
               (reinterpret_cast<uintptr_t>(a.R) & 15u) || (part && !reduce)))
     return hipErrorInvalidValue;
+  // SwiGLU: whole column pairs, output N / 2 wide
+  if (a.act == kActSwiGlu && (a.N % 4 || a.ldc < a.N / 2 || a.B2)) return hipErrorInvalidValue;
   if (a.act == kActSqRelu) {
     if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
     else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+  } else if (a.act == kActSwiGlu) {
+    if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSwiGlu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+    else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSwiGlu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   } else {
     if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
     else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
@@ -473,6 +508,9 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
   if (a.act == kActSqRelu) {
     if (scale) splitk_reduce_kernel<TOut, kActSqRelu, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
     else splitk_reduce_kernel<TOut, kActSqRelu, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
+  } else if (a.act == kActSwiGlu) {
+    if (scale) splitk_reduce_kernel<TOut, kActSwiGlu, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
+    else splitk_reduce_kernel<TOut, kActSwiGlu, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
   } else {
     if (scale) splitk_reduce_kernel<TOut, kActNone, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
     else splitk_reduce_kernel<TOut, kActNone, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);

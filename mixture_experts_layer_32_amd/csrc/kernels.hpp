@@ -7,7 +7,10 @@
 namespace lmoe {
 
 enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };
-enum ActKind : int { kActNone = 0, kActSqRelu = 1 };
+// kActSwiGlu: the B rows are interleaved pairs (row 2i the up projection
+// W_FC1 row i, row 2i + 1 the gate W_gate row i) and output column i is
+// C[2i] * SiLU(C[2i + 1]): the output is N / 2 wide.
+enum ActKind : int { kActNone = 0, kActSqRelu = 1, kActSwiGlu = 2 };
 
 // C = act(scale . (A x B^T)), all operands K-contiguous ("[rows][K]").
 // Dense: one group of M rows.  Grouped: group g owns logical rows
@@ -83,6 +86,7 @@ struct FfnArgs {
   const int32_t* g_off = nullptr;   // [G+1] first grouped row of each group
   int G = 0;
   int l = 0, m = 0;
+  int act = kActSqRelu;             // or kActSwiGlu: W1 is [G][2m][l], rows interleaved
 };
 // Whether the fused kernel takes this shape (the hidden rows fit in LDS).
 bool ffn_stream_fits(int l, int m);

@@ -95,6 +95,12 @@ WORKLOADS = {
                                           gating="sigmoid_topk_norm", n_shared=2, m_shared=1536),
         512, "decode", "LatentMoE at iso-cost (alpha=4) with S=2 shared experts of width m, "
         "bf16, T=512"),
+    "latent_swiglu_decode": Workload(
+        "latent_swiglu_decode", LayerSpec(d=2048, l=512, m=1408, n_experts=256, top_k=24,
+                                          gating="softmax_all", activation="swiglu", n_shared=2,
+                                          m_shared=1408),
+        512, "decode", "LatentMoE variant of the paper's 2048-wide SwiGLU model (alpha=4: "
+        "N 64 -> 256, K 6 -> 24), two shared SwiGLU experts, bf16, T=512"),
     "latent_prefill_zipf": Workload(
         "latent_prefill_zipf", LayerSpec(d=4096, l=1024, m=2048, n_experts=512, top_k=22,
                                          gating="softmax_all", has_router_bias=True),

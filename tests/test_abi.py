@@ -50,10 +50,15 @@ def test_create_accepts_every_workload_and_destroys():
 def test_regime_choice():
     lay = pkg.LatentMoELayer(workload("latent_decode").spec)
     assert lay.expert_regime(512) == "fused"     # 32 rows per expert, 512 experts, m 1536
-    assert lay.expert_regime(1024) == "stream"   # 64 rows per expert
+    assert lay.expert_regime(640) == "stream"    # 40 rows per expert
+    assert lay.expert_regime(1024) == "tiled"    # 64 rows per expert
     assert lay.expert_regime(16384) == "tiled"
     std = pkg.LatentMoELayer(workload("std_decode").spec)
     assert std.expert_regime(512) == "stream"    # 128 experts: fewer than compute units
+    assert std.expert_regime(768) == "tiled"     # 48 rows per expert
+    sw = pkg.LatentMoELayer(workload("latent_swiglu_decode").spec)
+    assert sw.expert_regime(512) == "tiled"      # 48 rows per expert
+    assert sw.expert_regime(256) == "fused"      # 24 rows, 256 experts
     fp8 = pkg.LatentMoELayer(workload("latent_fp8_sparse").spec)
     assert fp8.expert_regime(4096) == "tiled"    # 73 rows per expert
     assert fp8.expert_regime(512) == "stream"    # 9 rows per expert
@@ -71,7 +76,7 @@ def test_regime_choice():
     ("has_projections", 2, -1),
     ("l", 264, -1),               # l > d with projections
     ("m", 120, -2),               # not a multiple of 16
-    ("activation", 1, -2),        # gated experts not built
+    ("activation", 2, -1),
     ("expert_kernel", 4, -1),
     ("expert_kernel", 3, -2),     # fused kernel: bf16 only (the tiny layer is fp32)
     ("n_shared", -1, -1),

@@ -101,6 +101,16 @@ FORCED = {
                                  gating="softmax_topk"), 256, "tiled"),
     "stream_many_rows": (LayerSpec(d=256, l=128, m=192, n_experts=8, top_k=2,
                                    gating="softmax_topk"), 1000, "stream"),
+    # the streaming kernel's 128-row passes (more than 40 rows per expert)
+    # and multi-pass experts, on shapes the automatic choice gives to the
+    # tiled kernel
+    "stream_mb8_ragged": (LayerSpec(d=272, l=80, m=208, n_experts=7, top_k=3,
+                                    gating="softmax_all"), 133, "stream"),
+    "stream_sigmoid_mb8": (LayerSpec(d=512, l=128, m=320, n_experts=24, top_k=5,
+                                     gating="sigmoid_topk_norm"), 300, "stream"),
+    "stream_zipf_multipass": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
+                                        gating="softmax_all", has_router_bias=True), 1024,
+                              "stream"),
 }
 
 
