@@ -247,7 +247,7 @@ def main():
     # WRITE_SIZE, copy-calibrated), only while the kernel sources are the
     # ones the counters were taken on
     from mixture_experts_layer_32_amd import profiling
-    hbm = profiling.read_hbm(wl.name, dom)
+    hbm = profiling.read_hbm(wl.name, dom, regime) if T == wl.T else None
     roof["traffic"] = round(hbm) if hbm is not None else None
     roof["kernel"] = ("expert FFN, FC1 + FC2 (fused kernel)" if dom == "ffn" else
                       "expert GEMM %s (%s kernel)" % (dom.upper(), regime))

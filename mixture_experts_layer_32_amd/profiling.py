@@ -51,15 +51,32 @@ def short_name(name: str) -> str:
     return n.replace("lmoe::", "").replace("unsigned short", "bf16").replace("unsigned char", "u8")
 
 
-def expert_stage(name: str) -> str | None:
-    """gemm_stream_kernel<Mma, TA, TW, TOut, MB, NWB, ACT, SCALE>: ACT 1 = FC1;
-    ffn_stream_kernel: the fused FC1 + FC2 kernel."""
+def expert_kernel_kind(name: str) -> str | None:
+    """Which expert-FFN kernel a profiled kernel name is: "ffn_stream" (fused
+    FC1 + FC2), "gemm_stream" (weight streaming) or "gemm_tiled" (grouped
+    LDS-tiled: the 128 x 256 tile, or fp8 weights), else None (dense GEMMs
+    and routing kernels)."""
     if "ffn_stream_kernel" in name:
-        return "ffn"
-    if "gemm_stream_kernel<" not in name:
+        return "ffn_stream"
+    if "gemm_stream_kernel<" in name:
+        return "gemm_stream"
+    if "gemm_tiled_kernel<" in name and ("TileCfg<128, 256" in name or "unsigned char" in name
+                                         or ", u8," in name):
+        return "gemm_tiled"
+    return None
+
+
+def expert_stage(name: str) -> str | None:
+    """The stage an expert kernel runs: "ffn" for the fused kernel, else
+    "fc1" when its activation template argument (ACT, second to last) is
+    not 0 (squared ReLU 1, SwiGLU 2), "fc2" when it is."""
+    kind = expert_kernel_kind(name)
+    if kind is None:
         return None
+    if kind == "ffn_stream":
+        return "ffn"
     args = [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")]
-    return "fc1" if args[-2] == "1" else "fc2"
+    return "fc1" if args[-2] != "0" else "fc2"
 
 
 def _one(path_dir: str, suffix: str) -> str:
@@ -164,16 +181,19 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
         f.write("\n".join(lines) + "\n")
 
 
-def hbm_file(workload: str, stage: str) -> str:
-    kernel = "ffn_stream" if stage == "ffn" else "gemm_stream"
-    return os.path.join(PROFILES, "%s_%s_hbm.txt" % (kernel, workload))
+REGIME_KERNEL = {"fused": "ffn_stream", "stream": "gemm_stream", "tiled": "gemm_tiled"}
 
 
-def read_hbm(workload: str, stage: str):
-    """HBM bytes per launch of the FC1/FC2 (or fused, stage "ffn") kernel from
-    the committed summary, or None when there is none or the kernel sources
-    changed since."""
-    path = hbm_file(workload, stage)
+def hbm_file(workload: str, kind: str) -> str:
+    """kind: "ffn_stream", "gemm_stream" or "gemm_tiled"."""
+    return os.path.join(PROFILES, "%s_%s_hbm.txt" % (kind, workload))
+
+
+def read_hbm(workload: str, stage: str, regime: str):
+    """HBM bytes per launch of the FC1/FC2 (or fused, stage "ffn") kernel of
+    the expert regime ("fused", "stream", "tiled") from the committed
+    summary, or None when there is none or the kernel sources changed since."""
+    path = hbm_file(workload, REGIME_KERNEL[regime])
     if not os.path.exists(path):
         return None
     kv = {}
@@ -204,8 +224,11 @@ def main():
         write_trace_md(a.workload, a.trace, a.bench_json, out)
         print(out)
     if a.fetch and a.write and a.copy_fetch and a.copy_write:
-        stages = {expert_stage(n) for n in counter_per_dispatch(a.fetch, "FETCH_SIZE")}
-        out = hbm_file(a.workload, "ffn" if "ffn" in stages else "fc1")
+        kinds = {expert_kernel_kind(n) for n in counter_per_dispatch(a.fetch, "FETCH_SIZE")}
+        kinds.discard(None)
+        if len(kinds) != 1:
+            raise RuntimeError("expected one expert kernel kind, found %s" % sorted(kinds))
+        out = hbm_file(a.workload, kinds.pop())
         write_hbm_txt(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out)
         print(out)
 
