@@ -31,7 +31,7 @@ _LIB_PATH = os.path.join(_HERE, "liblatentmoe_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-_DT = {"f32": 0, "bf16": 1, "fp8_e4m3_rowscale": 2}
+_DT = {"f32": 0, "bf16": 1, "fp8_e4m3_rowscale": 2, "mxfp4_e2m1": 3}
 _GATE = {"softmax_all": 0, "softmax_topk": 1, "sigmoid_topk_norm": 2}
 _ACT = {"sqrelu": 0, "swiglu": 1}
 
@@ -53,7 +53,8 @@ class _Weights(ctypes.Structure):
                 ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p),
                 ("w_gate", ctypes.c_void_p), ("w_gate_scale", ctypes.c_void_p),
-                ("w_shared_gate", ctypes.c_void_p)]
+                ("w_shared_gate", ctypes.c_void_p), ("w1_mx", ctypes.c_void_p),
+                ("w2_mx", ctypes.c_void_p), ("w_gate_mx", ctypes.c_void_p)]
 
 
 def build(force: bool = True) -> str:
@@ -84,6 +85,10 @@ def _load():
             lib.orc_bf16_to_f64.restype = ctypes.c_double
             lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
             lib.orc_e4m3_to_f64.restype = ctypes.c_double
+            lib.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+            lib.orc_e2m1_to_f64.restype = ctypes.c_double
+            lib.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+            lib.orc_e8m0_to_f64.restype = ctypes.c_double
             _lib = lib
     return _lib
 
@@ -104,7 +109,8 @@ def _weights(w: dict):
     cw = _Weights(*(_p(keep.get(k)) for k in ("w_down", "w_router", "router_bias", "w1", "w2",
                                                "w1_scale", "w2_scale", "w_up",
                                                "w_shared1", "w_shared2", "w_gate",
-                                               "w_gate_scale", "w_shared_gate")))
+                                               "w_gate_scale", "w_shared_gate", "w1_mx",
+                                               "w2_mx", "w_gate_mx")))
     return cw, keep
 
 
@@ -164,10 +170,24 @@ def e4m3_to_f64(code: int) -> float:
     return float(_load().orc_e4m3_to_f64(int(code)))
 
 
+def e2m1_to_f64(code: int) -> float:
+    return float(_load().orc_e2m1_to_f64(int(code)))
+
+
+def e8m0_to_f64(e: int) -> float:
+    return float(_load().orc_e8m0_to_f64(int(e)))
+
+
 def upcast(a: np.ndarray, dtype: str, scale=None) -> np.ndarray:
-    """Exact fp64 values of a stored tensor (bf16 bits / e4m3 codes x row scale)."""
+    """Exact fp64 values of a stored tensor (bf16 bits / e4m3 codes x row
+    scale / MXFP4 pairs x E8M0 block scales, `scale` then the block scales)."""
     if dtype == "f32":
         return a.astype(np.float64)
+    if dtype == "mxfp4_e2m1":
+        codes = np.stack([a & 15, a >> 4], axis=-1).reshape(a.shape[:-1] + (2 * a.shape[-1],))
+        vals = np.array([e2m1_to_f64(c) for c in range(16)])[codes]
+        sc = np.array([e8m0_to_f64(e) for e in range(256)])[scale]
+        return vals * np.repeat(sc, 32, axis=-1)
     if dtype == "bf16":
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     table = np.array([e4m3_to_f64(c) for c in range(256)])

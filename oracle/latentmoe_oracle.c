@@ -54,12 +54,33 @@ static double round_bf16(double v) {
   return ldexp(nearbyint(ldexp(m, bits)), e - bits);
 }
 
-/* element i of a tensor stored as `dtype` (fp8: times the row scale) */
-static inline double ld(const void *p, int dtype, int64_t i, const float *scale, int64_t srow) {
+/* OCP MX FP4 element, E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit;
+ * exponent field 0 is subnormal (m * 0.5); no infinities or NaN.  The eight
+ * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double orc_e2m1_to_f64(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP MX shared scale, E8M0: 2^(e - 127); 0xFF is NaN. */
+double orc_e8m0_to_f64(uint8_t e) { return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* element i of a tensor stored as `dtype`: fp8 times its row's scale; MXFP4
+ * two elements per byte (element 2j in the low nibble of byte j) times the
+ * E8M0 scale of its block of 32 (block i / 32: rows hold whole blocks) */
+static inline double ld(const void *p, int dtype, int64_t i, const float *scale, int64_t srow,
+                        const uint8_t *mx) {
   switch (dtype) {
     case ORC_F32: return (double)((const float *)p)[i];
     case ORC_BF16: return orc_bf16_to_f64(((const uint16_t *)p)[i]);
-    default: return orc_e4m3_to_f64(((const uint8_t *)p)[i]) * (double)scale[srow];
+    case ORC_FP8_E4M3_ROWSCALE:
+      return orc_e4m3_to_f64(((const uint8_t *)p)[i]) * (double)scale[srow];
+    default: {
+      const uint8_t b = ((const uint8_t *)p)[i >> 1];
+      return orc_e2m1_to_f64((i & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15)) *
+             orc_e8m0_to_f64(mx[i >> 5]);
+    }
   }
 }
 
@@ -72,6 +93,11 @@ static int check(const orc_layer *L, const orc_weights *W, const void *x, int64_
   if (!W->w_router || !W->w1 || !W->w2) return -1;
   if (L->has_router_bias && !W->router_bias) return -1;
   if (L->expert_dtype == ORC_FP8_E4M3_ROWSCALE && (!W->w1_scale || !W->w2_scale)) return -1;
+  if (L->expert_dtype == ORC_MXFP4) {
+    if (!W->w1_mx || !W->w2_mx || L->l % 32 || L->m % 32) return -1;
+    if (L->activation == ORC_SWIGLU && !W->w_gate_mx) return -1;
+  }
+  if (L->expert_dtype < ORC_F32 || L->expert_dtype > ORC_MXFP4) return -1;
   if (L->act_dtype != ORC_F32 && L->act_dtype != ORC_BF16) return -1;
   if (L->gating < 0 || L->gating > 2) return -1;
   if (L->n_shared < 0) return -1;
@@ -90,11 +116,11 @@ static int check(const orc_layer *L, const orc_weights *W, const void *x, int64_
 static void latent_and_logits(const orc_layer *L, const orc_weights *W, const void *x, int64_t t,
                               double *xt, double *u, double *z) {
   const int64_t d = L->d, l = L->l, N = L->n_experts;
-  for (int64_t c = 0; c < d; ++c) xt[c] = ld(x, L->act_dtype, t * d + c, NULL, 0);
+  for (int64_t c = 0; c < d; ++c) xt[c] = ld(x, L->act_dtype, t * d + c, NULL, 0, NULL);
   if (L->has_projections) {
     for (int64_t r = 0; r < l; ++r) {        /* u = W_down . x, W_down in R^{l x d} */
       double s = 0.0;
-      for (int64_t c = 0; c < d; ++c) s += ld(W->w_down, L->act_dtype, r * d + c, NULL, 0) * xt[c];
+      for (int64_t c = 0; c < d; ++c) s += ld(W->w_down, L->act_dtype, r * d + c, NULL, 0, NULL) * xt[c];
       u[r] = s;
     }
   } else {
@@ -110,7 +136,7 @@ static void latent_and_logits(const orc_layer *L, const orc_weights *W, const vo
        * kernel's; everything else stays unrounded */
       double r = rin[c];
       if (L->router_on_latent && L->act_dtype == ORC_BF16) r = round_bf16(r);
-      s += ld(W->w_router, L->act_dtype, e * rw + c, NULL, 0) * r;
+      s += ld(W->w_router, L->act_dtype, e * rw + c, NULL, 0, NULL) * r;
     }
     if (L->has_router_bias) s += (double)W->router_bias[e];
     z[e] = s;
@@ -133,16 +159,16 @@ static void expert_ffn(const orc_layer *L, const orc_weights *W, int64_t e, cons
   for (int64_t r = 0; r < m; ++r) {
     double s = 0.0, sg = 0.0;
     const int64_t row = e * m + r;
-    for (int64_t c = 0; c < l; ++c) s += ld(W->w1, dt, row * l + c, W->w1_scale, row) * u[c];
+    for (int64_t c = 0; c < l; ++c) s += ld(W->w1, dt, row * l + c, W->w1_scale, row, W->w1_mx) * u[c];
     if (L->activation == ORC_SWIGLU)
       for (int64_t c = 0; c < l; ++c)
-        sg += ld(W->w_gate, dt, row * l + c, W->w_gate_scale, row) * u[c];
+        sg += ld(W->w_gate, dt, row * l + c, W->w_gate_scale, row, W->w_gate_mx) * u[c];
     h[r] = act_fn(L->activation, s, sg);
   }
   for (int64_t r = 0; r < l; ++r) {
     double s = 0.0;
     const int64_t row = e * l + r;
-    for (int64_t c = 0; c < m; ++c) s += ld(W->w2, dt, row * m + c, W->w2_scale, row) * h[c];
+    for (int64_t c = 0; c < m; ++c) s += ld(W->w2, dt, row * m + c, W->w2_scale, row, W->w2_mx) * h[c];
     y[r] = s;
   }
 }
@@ -156,7 +182,7 @@ static void up_project(const orc_layer *L, const orc_weights *W, const double *v
   }
   for (int64_t r = 0; r < d; ++r) {
     double s = 0.0;
-    for (int64_t c = 0; c < l; ++c) s += ld(W->w_up, L->act_dtype, r * l + c, NULL, 0) * v[c];
+    for (int64_t c = 0; c < l; ++c) s += ld(W->w_up, L->act_dtype, r * l + c, NULL, 0, NULL) * v[c];
     out[r] = s;
   }
 }
@@ -170,15 +196,15 @@ static void add_shared(const orc_layer *L, const orc_weights *W, const double *x
   const int64_t d = L->d, H = L->n_shared * L->m_shared;
   for (int64_t k = 0; k < H; ++k) {
     double s = 0.0, sg = 0.0;
-    for (int64_t c = 0; c < d; ++c) s += ld(W->w_shared1, L->act_dtype, k * d + c, NULL, 0) * xt[c];
+    for (int64_t c = 0; c < d; ++c) s += ld(W->w_shared1, L->act_dtype, k * d + c, NULL, 0, NULL) * xt[c];
     if (L->activation == ORC_SWIGLU)
       for (int64_t c = 0; c < d; ++c)
-        sg += ld(W->w_shared_gate, L->act_dtype, k * d + c, NULL, 0) * xt[c];
+        sg += ld(W->w_shared_gate, L->act_dtype, k * d + c, NULL, 0, NULL) * xt[c];
     hs[k] = act_fn(L->activation, s, sg);
   }
   for (int64_t r = 0; r < d; ++r) {
     double s = 0.0;
-    for (int64_t k = 0; k < H; ++k) s += ld(W->w_shared2, L->act_dtype, r * H + k, NULL, 0) * hs[k];
+    for (int64_t k = 0; k < H; ++k) s += ld(W->w_shared2, L->act_dtype, r * H + k, NULL, 0, NULL) * hs[k];
     out[r] += s;
   }
 }
@@ -334,16 +360,16 @@ int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
           for (int64_t r = 0; r < ms; ++r) {
             double s = 0.0, sg = 0.0;
             for (int64_t c = 0; c < d; ++c)
-              s += ld(W->w_shared1, L->act_dtype, (j * ms + r) * d + c, NULL, 0) * xt[c];
+              s += ld(W->w_shared1, L->act_dtype, (j * ms + r) * d + c, NULL, 0, NULL) * xt[c];
             if (L->activation == ORC_SWIGLU)
               for (int64_t c = 0; c < d; ++c)
-                sg += ld(W->w_shared_gate, L->act_dtype, (j * ms + r) * d + c, NULL, 0) * xt[c];
+                sg += ld(W->w_shared_gate, L->act_dtype, (j * ms + r) * d + c, NULL, 0, NULL) * xt[c];
             hs[r] = act_fn(L->activation, s, sg);
           }
           for (int64_t r = 0; r < d; ++r) {
             double s = 0.0;
             for (int64_t c = 0; c < ms; ++c)
-              s += ld(W->w_shared2, L->act_dtype, r * H + j * ms + c, NULL, 0) * hs[c];
+              s += ld(W->w_shared2, L->act_dtype, r * H + j * ms + c, NULL, 0, NULL) * hs[c];
             ys[r] = s;
           }
           for (int64_t r = 0; r < d; ++r) out[i * d + r] += ys[r];

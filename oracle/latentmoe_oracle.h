@@ -30,7 +30,8 @@
  * experts with no renormalisation (Eq. (1)); 1 = softmax over the K selected
  * logits; 2 = sigmoid of the selected logits normalised to sum to one.
  * Every sum runs in ascending index order, in fp64, with no intermediate
- * rounding; stored bf16 and fp8 values are upcast exactly (fp8 as q * scale).
+ * rounding; stored bf16, fp8 and MXFP4 values are upcast exactly (fp8 as
+ * q * row scale, MXFP4 as e2m1 * 2^(e8m0 - 127)).
  * One exception: a router placed on the latent u reads u rounded to bf16
  * when activations are bf16, so that the top-K decision is taken on the
  * values the GPU kernel routes on.
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_E4M3_ROWSCALE = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_E4M3_ROWSCALE = 2, ORC_MXFP4 = 3 };
 enum { ORC_SOFTMAX_ALL = 0, ORC_SOFTMAX_TOPK = 1, ORC_SIGMOID_TOPK_NORM = 2 };
 enum { ORC_SQRELU = 0, ORC_SWIGLU = 1 };
 
@@ -54,7 +55,7 @@ typedef struct {
   int32_t has_projections;   /* 0: standard MoE, requires l == d */
   int32_t has_router_bias;
   int32_t act_dtype;         /* ORC_F32 | ORC_BF16: x, W_down, W_router, W_up */
-  int32_t expert_dtype;      /* ORC_F32 | ORC_BF16 | ORC_FP8_E4M3_ROWSCALE: W1, W2 */
+  int32_t expert_dtype;      /* ORC_F32 | ORC_BF16 | ORC_FP8_E4M3_ROWSCALE | ORC_MXFP4: W1, W2 */
   int64_t n_shared;          /* S >= 0 shared experts */
   int64_t m_shared;          /* their hidden width (> 0 when S > 0) */
   int32_t activation;        /* ORC_SQRELU | ORC_SWIGLU */
@@ -66,7 +67,11 @@ typedef struct {
  * dtype: w_shared1 [S*m_shared][d] (expert j owns rows j*m_shared ..),
  * w_shared2 [d][S*m_shared] (expert j owns columns j*m_shared ..).  SwiGLU
  * only: w_gate [N][m][l] in the expert dtype (+ w_gate_scale [N][m] for
- * fp8), w_shared_gate [S*m_shared][d] in the activation dtype. */
+ * fp8), w_shared_gate [S*m_shared][d] in the activation dtype.  MXFP4
+ * experts (OCP MX, E2M1 elements, one E8M0 scale per 32 consecutive
+ * elements of a row): w1 [N][m][l/2], w2 [N][l][m/2] and w_gate bytes with
+ * element 2j in the low nibble of byte j; w1_mx [N][m][l/32], w2_mx
+ * [N][l][m/32], w_gate_mx [N][m][l/32] the scales (l, m multiples of 32). */
 typedef struct {
   const void *w_down, *w_router;
   const float *router_bias;
@@ -77,6 +82,7 @@ typedef struct {
   const void *w_gate;
   const float *w_gate_scale;
   const void *w_shared_gate;
+  const uint8_t *w1_mx, *w2_mx, *w_gate_mx;
 } orc_weights;
 
 /* Sparse forward (the definition).  x holds all tokens ([*][d], act dtype).
@@ -102,6 +108,8 @@ int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
 /* Exact upcasts of the storage formats. */
 double orc_bf16_to_f64(uint16_t bits);
 double orc_e4m3_to_f64(uint8_t code); /* OCP E4M3: bias 7, S.1111.111 = NaN */
+double orc_e2m1_to_f64(uint8_t code); /* OCP MX FP4 E2M1 (low 4 bits of code) */
+double orc_e8m0_to_f64(uint8_t e);    /* OCP MX scale 2^(e-127); 0xFF = NaN */
 
 /* Per-expert copy counts from an [n][K] id table. */
 void orc_expert_counts(const int32_t *idx, int64_t n, int64_t K, int64_t N, int64_t *counts);

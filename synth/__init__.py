@@ -104,6 +104,48 @@ def normal_fp8_rows(seed: int, tid: int, rows: int, cols: int, std: float, offse
     return q, s
 
 
+# OCP MX FP4 (E2M1) magnitudes of codes 0..7; codes 8..15 are their negatives
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_quantize(v: np.ndarray):
+    """OCP MX quantisation of v [rows][cols] (cols a multiple of 32) to FP4
+    E2M1 with one E8M0 scale per 32 consecutive elements of a row.
+
+    Per block: X = floor(log2(max |v|)) - 2 (2 = the largest E2M1 exponent),
+    clamped to the E8M0 range [-127, 127] (all-zero blocks: -127); elements
+    v / 2^X rounded to the nearest E2M1 value, ties to the even code,
+    magnitudes above 6 saturated to 6.  Returns (packed [rows][cols/2]
+    uint8, element 2j in the low nibble of byte j; scales [rows][cols/32]
+    uint8, the biased exponent X + 127).
+    """
+    v = np.asarray(v, np.float64)
+    rows, cols = v.shape
+    if cols % 32:
+        raise ValueError("MXFP4 rows must hold whole blocks of 32")
+    blk = v.reshape(rows, cols // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    X = np.clip(X, -127, 127)
+    y = blk / np.ldexp(1.0, X.astype(np.int64))[..., None]
+    a = np.minimum(np.abs(y), 6.0)
+    dist = np.abs(a[..., None] - _E2M1)
+    k = np.argmin(dist, axis=-1)                     # lower code on a tie
+    km = np.minimum(k + 1, 7)
+    d_k = np.take_along_axis(dist, k[..., None], -1)[..., 0]
+    d_n = np.take_along_axis(dist, km[..., None], -1)[..., 0]
+    k = np.where((k % 2 == 1) & (km != k) & (d_n == d_k), km, k)   # ties to the even code
+    code = (k + 8 * (y < 0) * (k > 0)).astype(np.uint8).reshape(rows, cols)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
+def normal_mxfp4_rows(seed: int, tid: int, rows: int, cols: int, std: float, offset: int = 0):
+    """rows x cols normals quantised to MXFP4 (mxfp4_quantize)."""
+    return mxfp4_quantize(normal(seed, tid, (rows, cols), std, "f64", offset))
+
+
 def f64_to_bf16(v: float) -> int:
     return int(_load().synth_f64_to_bf16(float(v)))
 
@@ -137,6 +179,8 @@ def make_weights(spec: LayerSpec, seed: int = 0) -> dict:
     identity matrix when spec.identity_projections), w_router [N][d or l],
     router_bias [N] (fp32, only with spec.has_router_bias), w1 [N][m][l],
     w2 [N][l][m] (+ w1_scale [N][m], w2_scale [N][l] for fp8 experts);
+    MXFP4 experts: w1 [N][m][l/2], w2 [N][l][m/2] packed E2M1 pairs with
+    E8M0 block scales w1_mx [N][m][l/32], w2_mx [N][l][m/32].
     SwiGLU experts add w_gate [N][m][l] (+ w_gate_scale [N][m]); shared
     experts w_shared1 [S*ms][d], w_shared2 [d][S*ms] and, with SwiGLU,
     w_shared_gate [S*ms][d].
@@ -161,7 +205,15 @@ def make_weights(spec: LayerSpec, seed: int = 0) -> dict:
     w["w_router"] = normal(seed, TID_WROUTER, (N, r_in), r_in ** -0.5, act)
     if spec.has_router_bias:
         w["router_bias"] = zipf_bias(seed, TID_BIAS, N, spec.zipf_s)
-    if spec.expert_dtype == "fp8_e4m3_rowscale":
+    if spec.expert_dtype == "mxfp4_e2m1":
+        q1, x1 = normal_mxfp4_rows(seed, TID_W1, N * m, l, l ** -0.5)
+        q2, x2 = normal_mxfp4_rows(seed, TID_W2, N * l, m, m ** -0.5)
+        w["w1"], w["w1_mx"] = q1.reshape(N, m, l // 2), x1.reshape(N, m, l // 32)
+        w["w2"], w["w2_mx"] = q2.reshape(N, l, m // 2), x2.reshape(N, l, m // 32)
+        if spec.activation == "swiglu":
+            qg, xg = normal_mxfp4_rows(seed, TID_WGATE, N * m, l, l ** -0.5)
+            w["w_gate"], w["w_gate_mx"] = qg.reshape(N, m, l // 2), xg.reshape(N, m, l // 32)
+    elif spec.expert_dtype == "fp8_e4m3_rowscale":
         q1, s1 = normal_fp8_rows(seed, TID_W1, N * m, l, l ** -0.5)
         q2, s2 = normal_fp8_rows(seed, TID_W2, N * l, m, m ** -0.5)
         w["w1"], w["w1_scale"] = q1.reshape(N, m, l), s1.reshape(N, m)

@@ -15,7 +15,7 @@ import dataclasses
 GATINGS = ("softmax_all", "softmax_topk", "sigmoid_topk_norm")
 ACTIVATIONS = ("sqrelu", "swiglu")
 ACT_DTYPES = ("f32", "bf16")
-EXPERT_DTYPES = ("f32", "bf16", "fp8_e4m3_rowscale")
+EXPERT_DTYPES = ("f32", "bf16", "fp8_e4m3_rowscale", "mxfp4_e2m1")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,7 +52,10 @@ class LayerSpec:
 
     @property
     def expert_bytes(self) -> float:
-        return {"f32": 4, "bf16": 2, "fp8_e4m3_rowscale": 1}[self.expert_dtype]
+        """Storage bytes per expert weight (MXFP4: half a byte plus a
+        one-byte scale per 32 elements)."""
+        return {"f32": 4, "bf16": 2, "fp8_e4m3_rowscale": 1,
+                "mxfp4_e2m1": 0.5 + 1.0 / 32}[self.expert_dtype]
 
 
 @dataclasses.dataclass(frozen=True)
