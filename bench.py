@@ -274,8 +274,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16"}[spec.act_dtype] + (
-            "+fp8w" if spec.expert_dtype == "fp8_e4m3_rowscale" else ""),
+        "dtype": {"f32": "f32", "bf16": "bf16"}[spec.act_dtype] + {
+            "fp8_e4m3_rowscale": "+fp8w", "mxfp4_e2m1": "+mxfp4w"}.get(spec.expert_dtype, ""),
         "data": "synthetic (seeded normals, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name, "T": T, "d": spec.d, "l": spec.l, "m": spec.m,
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "gating": spec.gating,

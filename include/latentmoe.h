@@ -25,7 +25,8 @@
  *  - Every tensor is row-major "[out][in]" (y = W . x), dense, with the
  *    shapes given on each field.  All data pointers are DEVICE pointers owned
  *    by the caller; they must be 16-byte aligned.  bf16 values are raw
- *    IEEE bfloat16 bit patterns (uint16), fp8 values raw OCP E4M3 bytes.
+ *    IEEE bfloat16 bit patterns (uint16), fp8 values raw OCP E4M3 bytes,
+ *    MXFP4 values packed E2M1 pairs with E8M0 block-scale bytes.
  *  - The library owns only the handle (host memory).  A handle is immutable
  *    after latentmoe_create and may be shared by concurrent forward calls on
  *    different streams if each call has its own workspace and outputs.
@@ -62,7 +63,11 @@ typedef enum {
 typedef enum {
   LMOE_F32 = 0,
   LMOE_BF16 = 1,
-  LMOE_FP8_E4M3_ROWSCALE = 2  /* OCP E4M3 bytes + one fp32 scale per matrix row: w = q * s */
+  LMOE_FP8_E4M3_ROWSCALE = 2, /* OCP E4M3 bytes + one fp32 scale per matrix row: w = q * s */
+  LMOE_MXFP4_E2M1 = 3         /* OCP MX FP4: E2M1 elements, two per byte (element 2j in the low
+                                 nibble of byte j), + one E8M0 scale byte 2^(e-127) per 32
+                                 consecutive elements of a row; expert weights only, bf16
+                                 activations, l and m multiples of 32, streaming kernel */
 } lmoe_dtype;
 
 typedef enum {
@@ -110,8 +115,8 @@ typedef struct {
   int32_t gating;         /* lmoe_gating */
   int32_t activation;     /* lmoe_activation */
   int32_t act_dtype;      /* LMOE_F32 | LMOE_BF16: x, W_down, W_router, W_up, out */
-  int32_t expert_dtype;   /* LMOE_F32 | LMOE_BF16 | LMOE_FP8_E4M3_ROWSCALE: W1, W2.
-                             F32 experts need F32 activations; BF16/FP8 need BF16. */
+  int32_t expert_dtype;   /* LMOE_F32 | LMOE_BF16 | LMOE_FP8_E4M3_ROWSCALE | LMOE_MXFP4_E2M1:
+                             W1, W2.  F32 experts need F32 activations; the others BF16. */
   int32_t has_projections;  /* 0: standard MoE (requires l == d) */
   int32_t has_router_bias;  /* 1: z += b before selection and gating (fp32 b[N]) */
   int32_t expert_kernel;    /* lmoe_expert_kernel; 0 = AUTO */
@@ -122,7 +127,8 @@ typedef struct {
 /* Device pointers; shapes use the config's d, l, m, N.  With SwiGLU experts
  * (activation LMOE_ACT_SWIGLU) the up-projection and gate matrices travel
  * as one interleaved matrix: w1 is [N][2m][l] with row 2i = W_FC1 row i and
- * row 2i + 1 = W_gate row i of the expert (w1_scale [N][2m] likewise), and
+ * row 2i + 1 = W_gate row i of the expert (w1_scale [N][2m] and w1_mx
+ * [N][2m][l/32] likewise), and
  * w_shared1 is [2*S*m_shared][d] with row 2k = Ws_FC1 row k and row 2k + 1 =
  * Ws_gate row k (expert j's rows start at 2*j*m_shared). */
 typedef struct {
@@ -136,6 +142,8 @@ typedef struct {
   const void *w_up;         /* [d][l] act dtype; NULL without projections */
   const void *w_shared1;    /* [S*m_shared][d] act dtype: Ws1_j is rows j*m_shared ..; n_shared > 0 */
   const void *w_shared2;    /* [d][S*m_shared] act dtype: Ws2_j is columns j*m_shared ..; n_shared > 0 */
+  const uint8_t *w1_mx;     /* MXFP4 experts: E8M0 scales [N][m][l/32] of w1 ([N][m][l/2] bytes) */
+  const uint8_t *w2_mx;     /* MXFP4 experts: E8M0 scales [N][l][m/32] of w2 ([N][l][m/2] bytes) */
 } lmoe_weights;
 
 /* Per-stage GPU timing: an opaque object holding HIP events.  Attach one to
@@ -179,8 +187,9 @@ typedef struct lmoe_handle lmoe_handle;
  * Returns INVALID_ARG for inconsistent shapes (k > N, l != d without
  * projections, non-positive sizes), UNSUPPORTED for combinations this
  * build does not implement (d, l, m not multiples of 16; N > 2048;
- * K > 64; activation/expert dtype pairs other than f32/f32, bf16/bf16 and
- * bf16/fp8). */
+ * K > 64; activation/expert dtype pairs other than f32/f32, bf16/bf16,
+ * bf16/fp8 and bf16/MXFP4; MXFP4 with l or m not multiples of 32 or with a
+ * forced tiled or fused expert kernel). */
 lmoe_status latentmoe_create(const lmoe_config *cfg, lmoe_handle **out);
 
 /* Bytes of device workspace a forward call over T tokens needs. */

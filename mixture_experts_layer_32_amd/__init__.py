@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # compiled with different tile constants); default: the in-tree build.
 LIB_PATH = os.environ.get("LATENTMOE_LIB") or os.path.join(HERE, "liblatentmoe.so")
 
-LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE = 0, 1, 2
+LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE, LMOE_MXFP4_E2M1 = 0, 1, 2, 3
 ROUTER_ON_X, ROUTER_ON_LATENT = 0, 1
 GATE_SOFTMAX_ALL, GATE_SOFTMAX_TOPK, GATE_SIGMOID_TOPK_NORM = 0, 1, 2
 ACT_SQRELU, ACT_SWIGLU = 0, 1
@@ -32,7 +32,8 @@ _EXPERT_KERNEL = {"auto": EXPERTS_AUTO, "tiled": EXPERTS_TILED, "stream": EXPERT
 NUM_STAGES = 8
 STAGE_NAMES = ("down_router", "topk", "dispatch", "fc1", "fc2", "combine", "up", "shared")
 
-_DT = {"f32": LMOE_F32, "bf16": LMOE_BF16, "fp8_e4m3_rowscale": LMOE_FP8_E4M3_ROWSCALE}
+_DT = {"f32": LMOE_F32, "bf16": LMOE_BF16, "fp8_e4m3_rowscale": LMOE_FP8_E4M3_ROWSCALE,
+       "mxfp4_e2m1": LMOE_MXFP4_E2M1}
 _GATE = {"softmax_all": GATE_SOFTMAX_ALL, "softmax_topk": GATE_SOFTMAX_TOPK,
          "sigmoid_topk_norm": GATE_SIGMOID_TOPK_NORM}
 
@@ -58,7 +59,8 @@ class LmoeWeights(ctypes.Structure):
                 ("router_bias", ctypes.c_void_p), ("w1", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
-                ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p)]
+                ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p),
+                ("w1_mx", ctypes.c_void_p), ("w2_mx", ctypes.c_void_p)]
 
 
 class LmoeDebug(ctypes.Structure):
@@ -252,8 +254,11 @@ class LatentMoELayer:
             edt = (torch.float32,)
         elif s.expert_dtype == "bf16":
             edt = (torch.bfloat16,)
+        elif s.expert_dtype == "mxfp4_e2m1":
+            edt = (torch.uint8,)
         else:
             edt = (torch.uint8, torch.float8_e4m3fn)
+        fp4 = s.expert_dtype == "mxfp4_e2m1"   # E2M1 pairs: half the columns, in bytes
         r_in = s.l if s.router_on_latent else s.d
         glu = getattr(s, "activation", "sqrelu") == "swiglu"
         m1 = 2 * s.m if glu else s.m  # W1 rows: (up, gate) pairs with SwiGLU
@@ -261,8 +266,13 @@ class LatentMoELayer:
             raise ValueError("SwiGLU weights go in interleaved: pass pack_gated(weights)")
         cw = LmoeWeights()
         cw.w_router = self._expect("w_router", w.get("w_router"), (s.n_experts, r_in), act)
-        cw.w1 = self._expect("w1", w.get("w1"), (s.n_experts, m1, s.l), edt)
-        cw.w2 = self._expect("w2", w.get("w2"), (s.n_experts, s.l, s.m), edt)
+        cw.w1 = self._expect("w1", w.get("w1"), (s.n_experts, m1, s.l // 2 if fp4 else s.l), edt)
+        cw.w2 = self._expect("w2", w.get("w2"), (s.n_experts, s.l, s.m // 2 if fp4 else s.m), edt)
+        if fp4:
+            cw.w1_mx = self._expect("w1_mx", w.get("w1_mx"), (s.n_experts, m1, s.l // 32),
+                                    (torch.uint8,))
+            cw.w2_mx = self._expect("w2_mx", w.get("w2_mx"), (s.n_experts, s.l, s.m // 32),
+                                    (torch.uint8,))
         if s.has_projections:
             cw.w_down = self._expect("w_down", w.get("w_down"), (s.l, s.d), act)
             cw.w_up = self._expect("w_up", w.get("w_up"), (s.d, s.l), act)
@@ -354,7 +364,7 @@ def pack_gated(weights: dict) -> dict:
     if "w_gate" not in weights:
         return dict(weights)
     out = {k: v for k, v in weights.items()
-           if k not in ("w_gate", "w_gate_scale", "w_shared_gate")}
+           if k not in ("w_gate", "w_gate_scale", "w_shared_gate", "w_gate_mx")}
 
     def inter(a, g, axis):
         if hasattr(a, "dim"):                      # torch
@@ -367,6 +377,8 @@ def pack_gated(weights: dict) -> dict:
     out["w1"] = inter(weights["w1"], weights["w_gate"], 1)
     if "w1_scale" in weights:
         out["w1_scale"] = inter(weights["w1_scale"], weights["w_gate_scale"], 1)
+    if "w1_mx" in weights:
+        out["w1_mx"] = inter(weights["w1_mx"], weights["w_gate_mx"], 1)
     if "w_shared1" in weights:
         out["w_shared1"] = inter(weights["w_shared1"], weights["w_shared_gate"], 0)
     return out

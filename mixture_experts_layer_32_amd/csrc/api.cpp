@@ -92,7 +92,8 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 lmoe::Dt act_dt(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? lmoe::Dt::F32 : lmoe::Dt::BF16; }
 lmoe::Dt exp_dt(const lmoe_config& c) {
   return c.expert_dtype == LMOE_F32 ? lmoe::Dt::F32
-         : c.expert_dtype == LMOE_BF16 ? lmoe::Dt::BF16 : lmoe::Dt::FP8;
+         : c.expert_dtype == LMOE_BF16 ? lmoe::Dt::BF16
+         : c.expert_dtype == LMOE_MXFP4_E2M1 ? lmoe::Dt::MXFP4 : lmoe::Dt::FP8;
 }
 size_t act_bytes(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? 4 : 2; }
 
@@ -190,6 +191,7 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.nblk = static_cast<int>((T + lmoe::kRouteBlock - 1) / lmoe::kRouteBlock);
   const double mean = T > 0 ? double(p.copies) / double(c.n_experts) : 0.0;
   const bool fp8 = c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE;
+  const bool fp4 = c.expert_dtype == LMOE_MXFP4_E2M1;
   const bool bf16 = c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16;
   switch (c.expert_kernel) {
     case LMOE_EXPERTS_TILED: p.stream = false; break;
@@ -202,6 +204,10 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
       p.fused = p.stream && bf16 && mean <= kFusedMaxRowsPerExpert &&
                 lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m)) &&
                 c.n_experts >= kComputeUnits;
+  }
+  if (fp4) {  // MXFP4 weights: the streaming kernel only
+    p.stream = true;
+    p.fused = false;
   }
   p.mb_max = mean <= LMOE_STREAM_MB4_MAX_ROWS ? 4 : 8;
   p.expert_tile = c.act_dtype == LMOE_BF16 ? LMOE_EXPERT_TILE : 1;  // fp32: the 64 x 64 tile
@@ -326,12 +332,13 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
     return fail(LMOE_ERR_INVALID_ARG, "create: has_router_bias must be 0 or 1");
   if (c.activation != LMOE_ACT_SQRELU && c.activation != LMOE_ACT_SWIGLU)
     return fail(LMOE_ERR_INVALID_ARG, "create: bad activation");
-  if (c.act_dtype < LMOE_F32 || c.act_dtype > LMOE_FP8_E4M3_ROWSCALE ||
-      c.expert_dtype < LMOE_F32 || c.expert_dtype > LMOE_FP8_E4M3_ROWSCALE)
+  if (c.act_dtype < LMOE_F32 || c.act_dtype > LMOE_MXFP4_E2M1 ||
+      c.expert_dtype < LMOE_F32 || c.expert_dtype > LMOE_MXFP4_E2M1)
     return fail(LMOE_ERR_INVALID_ARG, "create: bad dtype");
   const bool ok_pair = (c.act_dtype == LMOE_F32 && c.expert_dtype == LMOE_F32) ||
                        (c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16) ||
-                       (c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE);
+                       (c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE) ||
+                       (c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_MXFP4_E2M1);
   if (!ok_pair)
     return fail(LMOE_ERR_UNSUPPORTED, "create: dtype pair (act %d, experts %d) not implemented",
                 c.act_dtype, c.expert_dtype);
@@ -344,6 +351,12 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
     return fail(LMOE_ERR_UNSUPPORTED, "create: widths above 2^20");
   if (c.expert_kernel < LMOE_EXPERTS_AUTO || c.expert_kernel > LMOE_EXPERTS_FUSED)
     return fail(LMOE_ERR_INVALID_ARG, "create: bad expert_kernel");
+  if (c.expert_dtype == LMOE_MXFP4_E2M1) {
+    if (c.l % 32 || c.m % 32)
+      return fail(LMOE_ERR_UNSUPPORTED, "create: MXFP4 experts need l and m multiples of 32");
+    if (c.expert_kernel == LMOE_EXPERTS_TILED || c.expert_kernel == LMOE_EXPERTS_FUSED)
+      return fail(LMOE_ERR_UNSUPPORTED, "create: MXFP4 experts run in the streaming kernel only");
+  }
   if (c.n_shared < 0 || (c.n_shared > 0 && c.m_shared <= 0))
     return fail(LMOE_ERR_INVALID_ARG, "create: n_shared < 0, or shared experts without a width");
   if (c.n_shared > kMaxShared || (c.n_shared > 0 && (c.m_shared % 16 || c.m_shared > (int64_t(1) << 20))))
@@ -479,6 +492,8 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     return fail(LMOE_ERR_INVALID_ARG, "forward: NULL router bias");
   if (c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE && (!w->w1_scale || !w->w2_scale))
     return fail(LMOE_ERR_INVALID_ARG, "forward: NULL fp8 scales");
+  if (c.expert_dtype == LMOE_MXFP4_E2M1 && (!w->w1_mx || !w->w2_mx))
+    return fail(LMOE_ERR_INVALID_ARG, "forward: NULL MXFP4 block scales");
   const bool shared = c.n_shared > 0;
   if (shared && (!w->w_shared1 || !w->w_shared2))
     return fail(LMOE_ERR_INVALID_ARG, "forward: NULL shared-expert weights");
@@ -661,6 +676,10 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     const int n1 = glu ? 2 * m : m;  // W1 rows
     a.B = w->w1; a.ldb = l; a.b_gstride = int64_t(n1) * l;
     a.b_scale = edt == lmoe::Dt::FP8 ? w->w1_scale : nullptr; a.s_gstride = n1;
+    if (edt == lmoe::Dt::MXFP4) {  // E2M1 pairs: byte strides; a scale per 32
+      a.ldb = l / 2; a.b_gstride = int64_t(n1) * (l / 2);
+      a.b_mx = w->w1_mx; a.mx_ld = l / 32; a.mx_gstride = int64_t(n1) * (l / 32);
+    }
     a.C = H; a.ldc = m;
     a.N = n1; a.K = l;
     a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);
@@ -676,6 +695,10 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.A = H; a.lda = m; a.a_nrows = static_cast<int>(p.copies);
     a.B = w->w2; a.ldb = m; a.b_gstride = int64_t(l) * m;
     a.b_scale = edt == lmoe::Dt::FP8 ? w->w2_scale : nullptr; a.s_gstride = l;
+    if (edt == lmoe::Dt::MXFP4) {
+      a.ldb = m / 2; a.b_gstride = int64_t(l) * (m / 2);
+      a.b_mx = w->w2_mx; a.mx_ld = m / 32; a.mx_gstride = int64_t(l) * (m / 32);
+    }
     a.C = Y; a.ldc = l;
     a.N = l; a.K = m;
     a.g_off = offsets; a.g_tiles = tiles; a.G = N; a.max_rows = static_cast<int>(p.copies);

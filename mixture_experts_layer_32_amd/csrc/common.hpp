@@ -122,6 +122,33 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t q) {
   return r;
 }
 
+// MXFP4 weights (OCP MX: FP4 E2M1 elements, element 2j in the low nibble of
+// byte j, one E8M0 power-of-two scale per 32 elements).  The storage type of
+// a pair of elements:
+struct fp4x2_t {
+  uint8_t v;
+};
+
+// E8M0 scale byte -> fp32 2^(e - 127) (e = 0, the one subnormal scale, reads
+// as 0; the generator never writes it for a block holding a non-zero value)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Eight E2M1 elements (one dword) times the block scale -> eight bf16 (one
+// 16-byte MFMA operand), with the gfx950 scaled conversion
+// v_cvt_scalef32_pk_bf16_fp4 (byte b -> elements 2b, 2b + 1; exact: an E2M1
+// value times a power of two is a bf16 value)
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t q, float scale) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3))};
+}
+
+// one byte through a buffer resource (out-of-range offsets read 0)
+__device__ __forceinline__ uint32_t buffer_load_byte(BufRsrc r, uint32_t voff) {
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(voff), 0, 0));
+}
+
 // 16 E4M3 bytes (one chunk) -> 16 bf16 (two chunks).
 __device__ __forceinline__ void fp8_chunk_to_bf16(u32x4 q, u32x4& lo, u32x4& hi) {
   uint2 a = fp8x4_to_bf16x4(q.x), b = fp8x4_to_bf16x4(q.y);

@@ -40,6 +40,7 @@
 // token values.  Every offset is carried in the per-lane offset, which is
 // what the range check applies to.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -61,6 +62,13 @@ template <> struct StreamTraits<uint16_t, uint8_t> {   // bf16 tokens, fp8 weigh
   static constexpr int KSTEP = 32;                      // indices of one fp8 chunk, used
   __device__ __forceinline__ static int elem_of(int s, int q) {  // by steps 2j and 2j+1
     return 64 * (s >> 1) + 16 * q + 8 * (s & 1);
+  }
+};
+template <> struct StreamTraits<uint16_t, fp4x2_t> {   // bf16 tokens, MXFP4 weights: a
+  static constexpr int EPC = 8;                         // lane owns the 32 consecutive
+  static constexpr int KSTEP = 32;                      // indices of one 16-byte chunk (one
+  __device__ __forceinline__ static int elem_of(int s, int q) {  // scale block), used by the
+    return 32 * q + 8 * s;                              // stage's 4 steps
   }
 };
 template <> struct StreamTraits<float, float> {        // fp32 tokens and weights
@@ -92,11 +100,13 @@ struct StreamShape {
   static constexpr int EPC = Tr::EPC;
   static constexpr int KE = kStageChunks * EPC;    // reduction elements per stage
   static constexpr int NS = KE / Tr::KSTEP;        // MFMA steps per stage (4)
-  static constexpr bool FP8 = sizeof(TW) == 1;
-  static constexpr int NLD = FP8 ? NS / 2 : NS;    // 16-byte weight loads per n-block per stage
-  static constexpr uint32_t W_STAGE_BYTES = KE * sizeof(TW);
+  static constexpr bool FP8 = std::is_same_v<TW, uint8_t>;
+  static constexpr bool FP4 = std::is_same_v<TW, fp4x2_t>;
+  // 16-byte weight loads per n-block per stage
+  static constexpr int NLD = FP8 ? NS / 2 : FP4 ? NS / 4 : NS;
+  static constexpr uint32_t W_STAGE_BYTES = FP4 ? KE / 2 : KE * sizeof(TW);
   static constexpr uint32_t A_STAGE_BYTES = KE * sizeof(TA);
-  static constexpr int WD = FP8 ? LMOE_W_DEPTH_FP8 : LMOE_W_DEPTH;
+  static constexpr int WD = (FP8 || FP4) ? LMOE_W_DEPTH_FP8 : LMOE_W_DEPTH;
   // Register sets rotate: weights modulo WD + 1 stages, token rows modulo 2.
   // Units are padded to a multiple of this period, so every unit starts at
   // rotation phase 0 and the rotation stays in compile-time indices.
@@ -113,6 +123,8 @@ struct Unit {
   int valid;          // 0: past the end of the sequence (nothing to load or store)
   BufRsrc w_rsrc;            // the group's weight matrix
   uint32_t w_off[NWB];       // byte offset of this lane's chunk in its weight row, per n-block
+  BufRsrc s_rsrc;            // MXFP4: the group's block scales
+  uint32_t s_off[NWB];       // MXFP4: this lane's scale byte at stage 0, per n-block
   uint32_t a_off[MB_MAX];    // byte offset of this thread's chunk column in token row ar0 + 16 i
 
   // field by field, so that the compiler keeps every field in registers
@@ -126,8 +138,11 @@ struct Unit {
     rows = o.rows;
     valid = o.valid;
     w_rsrc = o.w_rsrc;
+    s_rsrc = o.s_rsrc;
 #pragma unroll
     for (int i = 0; i < NWB; ++i) w_off[i] = o.w_off[i];
+#pragma unroll
+    for (int i = 0; i < NWB; ++i) s_off[i] = o.s_off[i];
 #pragma unroll
     for (int i = 0; i < MB_MAX; ++i) a_off[i] = o.a_off[i];
   }
@@ -192,11 +207,16 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
     u.cnt = 0;
     u.rows = 0;
     u.w_rsrc = make_rsrc(wglob + (int64_t)u.g * p.b_gstride, (uint64_t)p.N * w_row_bytes);
+    if constexpr (S::FP4)
+      u.s_rsrc = make_rsrc(p.b_mx + (int64_t)u.g * p.mx_gstride, (uint64_t)p.N * p.mx_ld);
 #pragma unroll
     for (int nb = 0; nb < NWB; ++nb) {
       const int n = u.col0 + wave * NWB * 16 + nb * 16 + fr;
       u.w_off[nb] = (u.valid && n < p.N) ? static_cast<uint32_t>(n) * w_row_bytes + 16u * fq
                                          : kOutOfRange;
+      // the lane's chunk of stage s is block 4 s + fq of its row
+      if constexpr (S::FP4)
+        u.s_off[nb] = (u.valid && n < p.N) ? static_cast<uint32_t>(n * p.mx_ld) + fq : kOutOfRange;
     }
   };
   // group bounds g_off[g], g_off[g + 1]: a vector load, so that waiting for
@@ -235,7 +255,7 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
   // ---- loads of one stage
   // weight chunks of stage s; the chunk's position inside the stage is a
   // compile-time constant
-  auto load_w = [&](const U& u, int s, bool live, u32x4 (&br)[NWB][NLD]) {
+  auto load_w = [&](const U& u, int s, bool live, u32x4 (&br)[NWB][NLD], uint32_t (&bs)[NWB]) {
     const uint32_t so = static_cast<uint32_t>(s) * S::W_STAGE_BYTES;
 #pragma unroll
     for (int nb = 0; nb < NWB; ++nb) {
@@ -243,6 +263,8 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
         br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(u.w_rsrc, vo + 64u * j, 0u);
+      if constexpr (S::FP4)
+        bs[nb] = buffer_load_byte(u.s_rsrc, live ? u.s_off[nb] + 4u * s : kOutOfRange);
     }
   };
   // token chunk (row ar0 + 16 i, column ac) of stage s; past K -> zero
@@ -267,13 +289,16 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
 #pragma unroll
     for (int j = 0; j < NWB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const u32x4 (&br)[NWB][NLD]) {
+  auto compute = [&](int buf, const u32x4 (&br)[NWB][NLD], const uint32_t (&bs)[NWB]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4 bfr[NWB];
 #pragma unroll
       for (int nb = 0; nb < NWB; ++nb) {
-        if constexpr (S::FP8) {
+        if constexpr (S::FP4) {
+          // dword s of the lane's chunk: elements 32 fq + 8 s .. + 7
+          bfr[nb] = fp4x8_to_bf16x8(br[nb][0][s], e8m0_to_f32(bs[nb]));
+        } else if constexpr (S::FP8) {
           u32x4 lo, hi;
           fp8_chunk_to_bf16(br[nb][s >> 1], lo, hi);
           bfr[nb] = (s & 1) ? hi : lo;
@@ -298,9 +323,10 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
   set_item(cur, blockIdx.x / kNumXcd);
   if (!cur.valid) return;
   u32x4 bw[WD + 1][NWB][NLD];
+  uint32_t bsw[WD + 1][NWB];  // MXFP4 block scales of each weight stage
   u32x4 ra[2][MB_MAX];
 #pragma unroll
-  for (int i = 0; i < WD; ++i) load_w(cur, i, i < nst, bw[i]);
+  for (int i = 0; i < WD; ++i) load_w(cur, i, i < nst, bw[i], bsw[i]);
   issue_bounds(cur);
   take_bounds(cur);
   issue_rows(cur);
@@ -339,13 +365,16 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
         if (st == nsp - 2) take_rows(nxt);
         // weights of stage st + WD, token rows of stage st + 2
         const int sw = st + WD;
-        if (sw < nsp) load_w(cur, sw, sw < nst && cur.rows > 0, bw[(u + WD) % (WD + 1)]);
-        else load_w(nxt, sw - nsp, sw - nsp < nst && nxt.rows > 0, bw[(u + WD) % (WD + 1)]);
+        if (sw < nsp)
+          load_w(cur, sw, sw < nst && cur.rows > 0, bw[(u + WD) % (WD + 1)], bsw[(u + WD) % (WD + 1)]);
+        else
+          load_w(nxt, sw - nsp, sw - nsp < nst && nxt.rows > 0, bw[(u + WD) % (WD + 1)],
+                 bsw[(u + WD) % (WD + 1)]);
         const int sa = st + 2;
         if (sa < nsp) load_a(cur, sa, ra[u % 2]);
         else load_a(nxt, sa - nsp, ra[u % 2]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(u % 2, bw[u % (WD + 1)]);
+        compute(u % 2, bw[u % (WD + 1)], bsw[u % (WD + 1)]);
         store_a((u + 1) % 2, ra[(u + 1) % 2]);
         lds_barrier();
       }
@@ -456,6 +485,13 @@ hipError_t launch_mb(const GemmArgs& a, Dt a_dt, Dt w_dt, Dt out_dt, hipStream_t
   if (out_dt != Dt::BF16) return hipErrorInvalidValue;
   if (w_dt == Dt::BF16) return launch_s<MmaBf16, uint16_t, uint16_t, uint16_t, MB>(a, s);
   if (w_dt == Dt::FP8) return launch_s<MmaBf16, uint16_t, uint8_t, uint16_t, MB>(a, s);
+  if (w_dt == Dt::MXFP4) {
+    // whole scale blocks per row; one scale byte per block
+    if (!a.b_mx || a.K % 32 || a.mx_ld < a.K / 32 || a.ldb < a.K / 2 ||
+        (uint64_t)a.N * a.mx_ld >= (1ull << 31))
+      return hipErrorInvalidValue;
+    return launch_s<MmaBf16, uint16_t, fp4x2_t, uint16_t, MB>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -6,7 +6,7 @@
 
 namespace lmoe {
 
-enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };
+enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2, MXFP4 = 3 };
 // kActSwiGlu: the B rows are interleaved pairs (row 2i the up projection
 // W_FC1 row i, row 2i + 1 the gate W_gate row i) and output column i is
 // C[2i] * SiLU(C[2i + 1]): the output is N / 2 wide.
@@ -43,6 +43,11 @@ struct GemmArgs {
   // C[r][c] = act(...) + R[r * ldr + c] (N, ldr multiples of 4, R 16-byte aligned)
   const float* R = nullptr;
   int64_t ldr = 0;
+  // MXFP4 weights (streaming kernel): B holds E2M1 pairs (ldb, b_gstride in
+  // bytes), b_mx the E8M0 scales of each row's blocks of 32 (mx_ld bytes per
+  // row, mx_gstride per group)
+  const uint8_t* b_mx = nullptr;
+  int64_t mx_gstride = 0, mx_ld = 0;
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
@@ -63,7 +68,8 @@ int tiled_block_m_fp8w();
 // MI355X), for persistent grids.
 int device_compute_units();
 
-// Weight-streaming grouped GEMM for few rows per group (decode regime):
+// Weight-streaming grouped GEMM for few rows per group (decode regime), bf16,
+// fp8 (per-row scales) or MXFP4 (block scales, K a multiple of 32) weights:
 // every group's weight matrix is streamed from HBM once per pass of up to
 // mrows_max rows.  mb_max: 4 or 8 (rows per pass = 16 * mb_max).
 hipError_t launch_gemm_stream(const GemmArgs& a, Dt a_dt, Dt w_dt, Dt out_dt, int mb_max,

@@ -98,6 +98,11 @@ WORKLOADS = {
                                           gating="sigmoid_topk_norm", n_shared=2, m_shared=1536),
         512, "decode", "LatentMoE at iso-cost (alpha=4) with S=2 shared experts of width m, "
         "bf16, T=512"),
+    "latent_mxfp4_decode": Workload(
+        "latent_mxfp4_decode", LayerSpec(d=4096, l=1024, m=1536, n_experts=512, top_k=32,
+                                         gating="sigmoid_topk_norm", expert_dtype="mxfp4_e2m1"),
+        512, "decode", "LatentMoE at iso-cost (alpha=4), MXFP4 (E2M1 + E8M0 per 32) experts, "
+        "bf16 activations, T=512"),
     "latent_swiglu_decode": Workload(
         "latent_swiglu_decode", LayerSpec(d=2048, l=512, m=1408, n_experts=256, top_k=24,
                                           gating="softmax_all", activation="swiglu", n_shared=2,

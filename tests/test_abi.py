@@ -106,6 +106,18 @@ def test_create_rejects_unsupported_dtypes_and_sizes():
     assert _create(std)[0] == -1
 
 
+def test_create_checks_mxfp4_constraints():
+    mx = LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4, expert_dtype="mxfp4_e2m1")
+    st, h = _create(pkg.make_config(mx))
+    assert st == 0
+    assert pkg.lib().latentmoe_expert_regime(h, 4096) == b"stream"   # streaming kernel only
+    pkg.lib().latentmoe_destroy(h)
+    for spec, kind in ((mx.replace(l=48), "auto"), (mx.replace(m=144), "auto"),
+                       (mx, "tiled"), (mx, "fused"), (mx.replace(act_dtype="f32"), "auto")):
+        st, _ = _create(pkg.make_config(spec, kind))
+        assert st == -2, (spec, kind)
+
+
 def test_create_checks_shared_expert_sizes():
     cfg = pkg.make_config(workload("tiny_shared").spec)
     st, h = _create(cfg)
