@@ -288,6 +288,10 @@ def main():
         "latency_ms": {k: round(v, 5) for k, v in pct.items()},
         "roofline": roof,
         "layer_roofline": layer_roof,
+        "experts": {"touched": int((counts > 0).sum()),
+                    "algorithmic_bytes": ({"ffn": nbytes} if dom == "ffn" else
+                                          {st: expert_kernel_work(spec, T, counts, st)[0]
+                                           for st in ("fc1", "fc2")})},
     }
     if spec.n_shared:
         # the shared experts' two dense GEMMs (their stage's events, on the

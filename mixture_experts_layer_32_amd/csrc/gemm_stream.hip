@@ -177,7 +177,9 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
   const int fr = lane & 15, fq = lane >> 4;
   const int ac = tid & 15, ar0 = tid >> 4;  // A staging: chunk column ac of rows ar0 + 16 i
   const int n_tiles = (p.N + NT - 1) / NT;
-  const int total = p.G * n_tiles;
+  // groups visited: all, or (sparse batches) the listed ones with rows
+  const int g_count = p.g_active ? __builtin_amdgcn_readfirstlane(p.g_tiles[p.G]) : p.G;
+  const int total = g_count * n_tiles;
   const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
   const int slots = gridDim.x / kNumXcd;
   const int item_base = (blockIdx.x % kNumXcd) * per_xcd;
@@ -201,6 +203,7 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
     u.valid = local < per_xcd && item < total;
     const int it = u.valid ? item : 0;
     u.g = it / n_tiles;
+    if (p.g_active && u.valid) u.g = __builtin_amdgcn_readfirstlane(p.g_active[u.g]);
     u.col0 = (it % n_tiles) * NT;
     u.p0 = 0;
     u.gs = 0;
@@ -439,11 +442,22 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
 #define LMOE_STREAM_NWB_MB8 1
 #endif
 
+// MXFP4 weights: a stage is half the bytes of an fp8 one and one register
+// chunk per n-block, so units can be wider against the staged token rows
+#ifndef LMOE_STREAM_NWB_FP4
+#define LMOE_STREAM_NWB_FP4 2
+#endif
+#ifndef LMOE_STREAM_NWB_FP4_MB8
+#define LMOE_STREAM_NWB_FP4_MB8 1
+#endif
+
 template <typename Mma, typename TA, typename TW, typename TOut, int MB>
 hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
-  constexpr int NWB = MB >= 8 ? LMOE_STREAM_NWB_MB8 : LMOE_STREAM_NWB;
+  constexpr bool fp4 = std::is_same_v<TW, fp4x2_t>;
+  constexpr int NWB = fp4 ? (MB >= 8 ? LMOE_STREAM_NWB_FP4_MB8 : LMOE_STREAM_NWB_FP4)
+                          : (MB >= 8 ? LMOE_STREAM_NWB_MB8 : LMOE_STREAM_NWB);
   constexpr int NT = 4 * NWB * 16;
-  if (a.g_off == nullptr || a.G < 1) return hipErrorInvalidValue;
+  if (a.g_off == nullptr || a.G < 1 || (a.g_active && !a.g_tiles)) return hipErrorInvalidValue;
   const int64_t n_tiles = (a.N + NT - 1) / NT;
   const int64_t total = n_tiles * a.G;
   if (total <= 0) return hipSuccess;

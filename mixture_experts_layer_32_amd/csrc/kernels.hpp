@@ -48,6 +48,9 @@ struct GemmArgs {
   // row, mx_gstride per group)
   const uint8_t* b_mx = nullptr;
   int64_t mx_gstride = 0, mx_ld = 0;
+  // streaming kernel, sparse batches: g_active[0 .. g_tiles[G]) lists the
+  // groups with rows, and only those are visited
+  const int32_t* g_active = nullptr;
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
@@ -123,8 +126,13 @@ struct TopkArgs {
 hipError_t launch_topk_gate(const TopkArgs& a, hipStream_t s);
 hipError_t launch_route_masks(const int32_t* idx, int T, int N, int K, uint64_t* masks,
                               hipStream_t s);
+// active (optional, with tile_m = kActiveTile): the ids of the experts with
+// copies in ascending order, [tiles[N]] of them (tiles[e] is then the number
+// of such experts before e)
+constexpr int kActiveTile = 1 << 30;
 hipError_t launch_route_scan(const uint64_t* masks, int nblk, int N, int tile_m, int32_t* counts,
-                             int32_t* offsets, int32_t* base, int32_t* tiles, hipStream_t s);
+                             int32_t* offsets, int32_t* base, int32_t* tiles, hipStream_t s,
+                             int32_t* active = nullptr);
 hipError_t launch_route_assign(const int32_t* idx, const uint64_t* masks, const int32_t* base,
                                const int32_t* offsets, int T, int N, int K, int32_t* slot_of,
                                int32_t* token_of, hipStream_t s);
@@ -133,7 +141,7 @@ hipError_t launch_route_assign(const int32_t* idx, const uint64_t* masks, const 
 bool route_small_fits(int T, int N, int K);
 hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_m, int32_t* counts,
                               int32_t* offsets, int32_t* tiles, int32_t* slot_of,
-                              int32_t* token_of, hipStream_t s);
+                              int32_t* token_of, hipStream_t s, int32_t* active = nullptr);
 // v[t] = sum_j gate[t][j] * Y[slot_of[t][j]] (+ R[t], fp32 [T][l], when R is given)
 hipError_t launch_combine(const void* Y, const int32_t* slot_of, const float* gate, int T, int K,
                           int l, Dt dt, const float* R, void* v, hipStream_t s);

@@ -238,7 +238,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __rest
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ base,
-                                                          int32_t* __restrict__ tiles) {
+                                                          int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ active) {
   __shared__ int s_cnt[2048];
   __shared__ int s_til[2048];
   __shared__ int s_wsum[2][16];
@@ -276,6 +277,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __rest
       counts[e] = cnt[h];
       offsets[e] = s_cnt[e];
       if (tiles) tiles[e] = s_til[e];
+      // one "tile" per expert with copies: s_til is its rank among them
+      if (active && cnt[h] > 0) active[s_til[e]] = e;
     }
   }
   if (tid == 0) {
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ tiles,
                                                            int32_t* __restrict__ slot_of,
-                                                           int32_t* __restrict__ token_of) {
+                                                           int32_t* __restrict__ token_of,
+                                                           int32_t* __restrict__ active) {
   __shared__ unsigned long long sm[kSmallRouteMasks];
   __shared__ int s_cnt[2048];
   __shared__ int s_til[2048];
@@ -369,6 +373,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
         counts[e] = cnt[h];
         offsets[e] = s_cnt[e];
         if (tiles) tiles[e] = s_til[e];
+        if (active && cnt[h] > 0) active[s_til[e]] = e;
       }
     }
     if (tid == 0) {
@@ -512,10 +517,12 @@ hipError_t launch_route_masks(const int32_t* idx, int T, int N, int K, uint64_t*
 }
 
 hipError_t launch_route_scan(const uint64_t* masks, int nblk, int N, int tile_m, int32_t* counts,
-                             int32_t* offsets, int32_t* base, int32_t* tiles, hipStream_t s) {
+                             int32_t* offsets, int32_t* base, int32_t* tiles, hipStream_t s,
+                             int32_t* active) {
   if (N > 2048 || tile_m <= 0) return hipErrorInvalidValue;
+  if (active && (!tiles || tile_m < kActiveTile)) return hipErrorInvalidValue;
   route_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(masks, nblk, N, tile_m, counts, offsets, base,
-                                                   tiles);
+                                                   tiles, active);
   return hipGetLastError();
 }
 
@@ -531,12 +538,13 @@ hipError_t launch_route_assign(const int32_t* idx, const uint64_t* masks, const 
 
 hipError_t launch_route_small(const int32_t* idx, int T, int N, int K, int tile_m, int32_t* counts,
                               int32_t* offsets, int32_t* tiles, int32_t* slot_of,
-                              int32_t* token_of, hipStream_t s) {
+                              int32_t* token_of, hipStream_t s, int32_t* active) {
   if (T <= 0) return hipSuccess;
   if (!route_small_fits(T, N, K) || tile_m <= 0) return hipErrorInvalidValue;
+  if (active && (!tiles || tile_m < kActiveTile)) return hipErrorInvalidValue;
   const int grid = (T * K + 1023) / 1024;
   route_small_kernel<<<dim3(grid), dim3(1024), 0, s>>>(idx, T, N, K, tile_m, counts, offsets,
-                                                       tiles, slot_of, token_of);
+                                                       tiles, slot_of, token_of, active);
   return hipGetLastError();
 }
 

@@ -137,7 +137,7 @@ def write_trace_md(workload: str, trace_dir: str, bench_json: str | None, out: s
 
 
 def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cwrite: str,
-                  trace_dir: str | None, out: str):
+                  trace_dir: str | None, out: str, tokens: int = 0):
     # factor: true KiB per counted KiB, from the copy's known 1 GiB each way
     cf, cw = copy_reading(cfetch, "FETCH_SIZE"), copy_reading(cwrite, "WRITE_SIZE")
     ff, fw = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
@@ -146,12 +146,14 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
     avg = {}
     if trace_dir:
         avg = {r["name"]: r["avg_us"] for r in kernel_stats(trace_dir)}
-    lines = ["# HBM traffic of the expert GEMM kernels, workload %s" % workload,
+    tk = " --tokens %d" % tokens if tokens else ""
+    lines = ["# HBM traffic of the expert GEMM kernels, workload %s%s" % (
+                 workload, " at T=%d" % tokens if tokens else ""),
              "# commands (from a scratch directory, TMPDIR=/tmp):",
              "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- "
-             "python3 bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline" % workload,
+             "python3 bench.py --workload %s%s --steps 2 --warmup 1 --no-cpu-baseline" % (workload, tk),
              "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- "
-             "python3 bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline" % workload,
+             "python3 bench.py --workload %s%s --steps 2 --warmup 1 --no-cpu-baseline" % (workload, tk),
              "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o cf --output-format csv -- "
              "python3 bench.py --copy-calibration",
              "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o cw --output-format csv -- "
@@ -159,6 +161,7 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
              "# a 1 GiB device copy (1048576 KiB each way) reads FETCH_SIZE %.1f and WRITE_SIZE"
              " %.1f KiB per dispatch: scale factors %.4f and %.4f" % (cf, cw, ff, fw),
              "workload=%s" % workload,
+             "tokens=%d" % tokens,
              "sources_sha256=%s" % sources_hash(),
              "fetch_scale=%.6f" % ff,
              "write_scale=%.6f" % fw]
@@ -208,6 +211,53 @@ def read_hbm(workload: str, stage: str, regime: str):
     return float(v) if v is not None else None
 
 
+def _read_kv(path):
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k] = v
+    return kv
+
+
+def write_sweep_md(entries, out):
+    """Table of the alpha sweep: per (workload, T) the step time, the expert
+    stages' event times, their algorithmic bytes (from the bench line) and
+    their HBM bytes measured by FETCH_SIZE + WRITE_SIZE (copy-calibrated,
+    from profiles/<kernel>_<workload>[_T<T>]_hbm.txt)."""
+    rows = ["# LatentMoE cost curve: measured expert bytes across the compression ratio",
+            "",
+            "Per entry, from the repository root:",
+            "",
+            "    python3 bench.py --workload W --tokens T --steps 20 --warmup 3 --no-cpu-baseline",
+            "    rocprofv3 --pmc FETCH_SIZE ... / --pmc WRITE_SIZE ... -- python3 bench.py "
+            "--workload W --tokens T --steps 2 --warmup 1 --no-cpu-baseline",
+            "",
+            "(the HBM files name their exact commands).  Bytes are per layer call, "
+            "FC1 + FC2 of the expert GEMMs.",
+            "",
+            "| workload | l | N' | K | T | touched experts | ms/step | FC1+FC2 us | "
+            "algorithmic expert MB | measured HBM MB | measured / algorithmic |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for e in entries:
+        wl, T, bj = e.split(":", 2)
+        with open(bj) as f:
+            b = json.loads(f.read().strip().splitlines()[-1])
+        cfg = b["config"]
+        alg = sum(b["experts"]["algorithmic_bytes"].values())
+        kind = REGIME_KERNEL[cfg["expert_kernel"]]
+        name = wl + ("" if int(T) == 512 else "_T%s" % T)
+        kv = _read_kv(hbm_file(name, kind))
+        meas = sum(float(kv[k]) for k in kv if k.endswith("_hbm_bytes"))
+        st = b["stage_ms"]
+        rows.append("| %s | %d | %d | %d | %d | %d | %.3f | %.1f | %.1f | %.1f | %.3f |" % (
+            wl, cfg["l"], cfg["n_experts"], cfg["top_k"], int(T), b["experts"]["touched"],
+            b["ms_per_step"], 1e3 * (st["fc1"] + st["fc2"]), alg / 1e6, meas / 1e6, meas / alg))
+    with open(out, "w") as f:
+        f.write("\n".join(rows) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -217,7 +267,16 @@ def main():
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--bench-json")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="batch of a run at a non-default T (names the HBM file ..._T<T>)")
+    ap.add_argument("--sweep-summary", help="write the alpha-sweep summary (markdown) here")
+    ap.add_argument("--sweep", action="append", default=[],
+                    help="WORKLOAD:T:BENCH_JSON entry of the sweep summary (repeatable)")
     a = ap.parse_args()
+    if a.sweep_summary:
+        write_sweep_md(a.sweep, a.sweep_summary)
+        print(a.sweep_summary)
+        return
     os.makedirs(PROFILES, exist_ok=True)
     if a.trace:
         out = os.path.join(PROFILES, "%s_kernels_trace.md" % a.workload)
@@ -228,8 +287,10 @@ def main():
         kinds.discard(None)
         if len(kinds) != 1:
             raise RuntimeError("expected one expert kernel kind, found %s" % sorted(kinds))
-        out = hbm_file(a.workload, kinds.pop())
-        write_hbm_txt(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out)
+        wl = a.workload + ("_T%d" % a.tokens if a.tokens else "")
+        out = hbm_file(wl, kinds.pop())
+        write_hbm_txt(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out,
+                      a.tokens)
         print(out)
 
 

@@ -120,6 +120,30 @@ WORKLOADS = {
 }
 
 
+# Table 2's 95BT-8BA MoE layer (d 4096, N 128, K 6, S 2 shared experts, m 2688,
+# Squared-ReLU) and its LatentMoE variants (§3): l-MoE_eff at alpha = d / l
+# keeps K and scales N by alpha (Eq. (1)); l-MoE_acc also scales K (Eq. (2)).
+def _table2_95b(alpha: int, acc: bool = False) -> LayerSpec:
+    d, N, K, m = 4096, 128, 6, 2688
+    if alpha == 1:
+        return LayerSpec(d=d, l=d, m=m, n_experts=N, top_k=K, gating="softmax_all",
+                         has_projections=False, n_shared=2, m_shared=m)
+    return LayerSpec(d=d, l=d // alpha, m=m, n_experts=N * alpha, top_k=K * alpha if acc else K,
+                     gating="softmax_all", n_shared=2, m_shared=m)
+
+
+for _a in (1, 2, 4, 8):
+    _n = "t2_std" if _a == 1 else "t2_eff_a%d" % _a
+    WORKLOADS[_n] = Workload(
+        _n, _table2_95b(_a), 512, "decode",
+        "Table 2 95BT-8BA MoE layer" + ("" if _a == 1 else
+                                        " as l-MoE_eff, alpha=%d (l %d, N' %d, K 6)"
+                                        % (_a, 4096 // _a, 128 * _a)) + ", S=2, bf16, T=512")
+WORKLOADS["t2_acc_a4"] = Workload(
+    "t2_acc_a4", _table2_95b(4, acc=True), 512, "decode",
+    "Table 2 95BT-8BA MoE layer as l-MoE_acc, alpha=4 (l 1024, N' 512, K' 24), S=2, bf16, T=512")
+
+
 def workload(name: str) -> Workload:
     try:
         return WORKLOADS[name]

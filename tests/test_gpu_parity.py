@@ -111,6 +111,14 @@ FORCED = {
     "stream_zipf_multipass": (LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
                                         gating="softmax_all", has_router_bias=True), 1024,
                               "stream"),
+    # sparse batch (1 copy per expert on average): the streaming kernel works
+    # from the dispatch stage's list of experts with copies; the skewed
+    # router still gives some experts several passes
+    "stream_sparse_zipf": (LayerSpec(d=512, l=128, m=192, n_experts=512, top_k=4,
+                                     gating="softmax_all", has_router_bias=True), 128, "stream"),
+    "stream_sparse_fp8": (LayerSpec(d=256, l=64, m=128, n_experts=256, top_k=2,
+                                    gating="sigmoid_topk_norm", expert_dtype="fp8_e4m3_rowscale"),
+                          100, "stream"),
 }
 
 
