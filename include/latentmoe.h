@@ -97,7 +97,8 @@ typedef enum {
  *            unit; an expert with more than 48 rows takes several passes);
  *   TILED  - LDS-tiled MFMA grouped GEMMs (many rows per expert: prefill).
  * Every choice computes the same function; forcing one is for tests and
- * measurements.  FUSED needs bf16 activations and experts and m <= 1536. */
+ * measurements.  FUSED needs bf16 activations and experts and m <= 1536;
+ * MXFP4 experts run in STREAM only (AUTO picks it at any batch). */
 typedef enum {
   LMOE_EXPERTS_AUTO = 0,
   LMOE_EXPERTS_TILED = 1,
@@ -135,9 +136,10 @@ typedef struct {
   const void *w_down;       /* [l][d] act dtype; NULL without projections */
   const void *w_router;     /* [N][d] (ROUTER_ON_X) or [N][l] (ROUTER_ON_LATENT), act dtype */
   const float *router_bias; /* [N] fp32; only read when has_router_bias */
-  const void *w1;           /* [N][m][l] expert dtype */
-  const void *w2;           /* [N][l][m] expert dtype */
-  const float *w1_scale;    /* [N][m] fp32; FP8 experts only */
+  const void *w1;           /* [N][m][l] expert dtype ([N][2m][l] interleaved with SwiGLU;
+                               MXFP4: bytes [N][m][l/2], or [N][2m][l/2]) */
+  const void *w2;           /* [N][l][m] expert dtype (MXFP4: bytes [N][l][m/2]) */
+  const float *w1_scale;    /* [N][m] fp32 ([N][2m] with SwiGLU); FP8 experts only */
   const float *w2_scale;    /* [N][l] fp32; FP8 experts only */
   const void *w_up;         /* [d][l] act dtype; NULL without projections */
   const void *w_shared1;    /* [S*m_shared][d] act dtype: Ws1_j is rows j*m_shared ..; n_shared > 0 */
@@ -159,11 +161,12 @@ enum {
   LMOE_STAGE_DOWN_ROUTER = 0, /* W_down GEMM and router-logit GEMM */
   LMOE_STAGE_TOPK = 1,        /* top-k + gating */
   LMOE_STAGE_DISPATCH = 2,    /* expert histogram, prefix sum, stable slot assignment */
-  LMOE_STAGE_FC1 = 3,         /* grouped latent FC1 + squared ReLU (gathers u rows) */
+  LMOE_STAGE_FC1 = 3,         /* grouped latent FC1 + squared ReLU or SwiGLU (gathers u rows);
+                                 the fused kernel runs FC1 and FC2 here */
   LMOE_STAGE_FC2 = 4,         /* grouped latent FC2 */
   LMOE_STAGE_COMBINE = 5,     /* gate-weighted sum of the K expert outputs per token */
   LMOE_STAGE_UP = 6,          /* W_up GEMM (+ the shared experts' sum) */
-  LMOE_STAGE_SHARED = 7,      /* shared experts: x Ws1^T + squared ReLU, then . Ws2^T (fp32) */
+  LMOE_STAGE_SHARED = 7,      /* shared experts: x Ws1^T + activation, then . Ws2^T (fp32) */
   LMOE_NUM_STAGES = 8
 };
 
