@@ -1,9 +1,9 @@
 """Summaries of rocprofv3 output for the layer's kernels (text, for profiles/).
 
     python -m mixture_experts_layer_32_amd.profiling --workload latent_decode \
-        --trace gpurun_out/prof_latent_decode --fetch gpurun_out/pmc_fetch_latent_decode \
-        --write gpurun_out/pmc_write_latent_decode --copy-fetch gpurun_out/pmc_copy_fetch \
-        --copy-write gpurun_out/pmc_copy_write --bench-json gpurun_out/prof_latent_decode_bench.json
+        --trace <trace dir> --fetch <FETCH_SIZE dir> --write <WRITE_SIZE dir> \
+        --copy-fetch <copy FETCH_SIZE dir> --copy-write <copy WRITE_SIZE dir> \
+        --bench-json <bench.py output of the traced run>
 
 reads the CSV files of
 
@@ -15,7 +15,11 @@ reads the CSV files of
 and writes profiles/<workload>_kernels_trace.md (per-kernel durations) and
 profiles/<kernel>_<workload>_hbm.txt (HBM bytes per launch of the expert
 kernels, scaled by what the same counters read for a 1 GiB device copy;
-<kernel> is ffn_stream for the fused FC1 + FC2 kernel, else gemm_stream).
+<kernel> is ffn_stream for the fused FC1 + FC2 kernel, gemm_stream for the
+weight-streaming GEMMs and gemm_tiled for the grouped LDS-tiled ones; with
+--tokens T the workload is named <workload>_T<T>).  --sweep-summary writes
+the table of a sweep over workloads and batches from their bench lines and
+HBM files.
 The HBM file records a hash of the kernel sources; bench.py reports its
 traffic only while the sources still hash the same.
 """
