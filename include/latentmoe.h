@@ -67,7 +67,8 @@ typedef enum {
   LMOE_MXFP4_E2M1 = 3         /* OCP MX FP4: E2M1 elements, two per byte (element 2j in the low
                                  nibble of byte j), + one E8M0 scale byte 2^(e-127) per 32
                                  consecutive elements of a row; expert weights only, bf16
-                                 activations, l and m multiples of 32, streaming kernel */
+                                 activations, l and m multiples of 32, streaming or fused
+                                 kernel */
 } lmoe_dtype;
 
 typedef enum {
@@ -97,8 +98,8 @@ typedef enum {
  *            unit; an expert with more than 48 rows takes several passes);
  *   TILED  - LDS-tiled MFMA grouped GEMMs (many rows per expert: prefill).
  * Every choice computes the same function; forcing one is for tests and
- * measurements.  FUSED needs bf16 activations and experts and m <= 1536;
- * MXFP4 experts run in STREAM only (AUTO picks it at any batch). */
+ * measurements.  FUSED needs bf16 activations, bf16 or MXFP4 experts and
+ * m <= 1536; MXFP4 experts never run TILED (AUTO streams them). */
 typedef enum {
   LMOE_EXPERTS_AUTO = 0,
   LMOE_EXPERTS_TILED = 1,

@@ -215,14 +215,13 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
       p.stream = fp8 ? mean <= kFp8StreamMaxRowsPerExpert : mean <= kStreamMaxRowsPerExpert;
       // one expert per resident workgroup: the fused kernel fills the chip
       // only with at least one expert per compute unit
+      // (bf16 weights: with MXFP4 the fused kernel is issue-bound and no
+      // faster than the streaming one, measured 371 against 371 us)
       p.fused = p.stream && bf16 && mean <= kFusedMaxRowsPerExpert &&
                 lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m)) &&
                 c.n_experts >= kComputeUnits;
   }
-  if (fp4) {  // MXFP4 weights: the streaming kernel only
-    p.stream = true;
-    p.fused = false;
-  }
+  if (fp4 && !p.stream) p.stream = true;  // MXFP4 weights: no tiled kernel
   p.mb_max = mean <= LMOE_STREAM_MB4_MAX_ROWS ? 4 : 8;
   // most experts empty (expected share e^-mean > 1/8): the streaming kernel
   // visits only the experts with copies, listed by the dispatch stage
@@ -373,8 +372,8 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
   if (c.expert_dtype == LMOE_MXFP4_E2M1) {
     if (c.l % 32 || c.m % 32)
       return fail(LMOE_ERR_UNSUPPORTED, "create: MXFP4 experts need l and m multiples of 32");
-    if (c.expert_kernel == LMOE_EXPERTS_TILED || c.expert_kernel == LMOE_EXPERTS_FUSED)
-      return fail(LMOE_ERR_UNSUPPORTED, "create: MXFP4 experts run in the streaming kernel only");
+    if (c.expert_kernel == LMOE_EXPERTS_TILED)
+      return fail(LMOE_ERR_UNSUPPORTED, "create: MXFP4 experts run in the streaming or fused kernels");
   }
   if (c.n_shared < 0 || (c.n_shared > 0 && c.m_shared <= 0))
     return fail(LMOE_ERR_INVALID_ARG, "create: n_shared < 0, or shared experts without a width");
@@ -382,9 +381,12 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
     return fail(LMOE_ERR_UNSUPPORTED, "create: n_shared <= %lld and m_shared a multiple of 16 "
                 "up to 2^20 supported", (long long)kMaxShared);
   if (c.expert_kernel == LMOE_EXPERTS_FUSED &&
-      !(c.act_dtype == LMOE_BF16 && c.expert_dtype == LMOE_BF16 &&
+      !(c.act_dtype == LMOE_BF16 &&
+        (c.expert_dtype == LMOE_BF16 || c.expert_dtype == LMOE_MXFP4_E2M1) &&
         lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m))))
-    return fail(LMOE_ERR_UNSUPPORTED, "create: the fused expert kernel needs bf16 and m <= 1536");
+    return fail(LMOE_ERR_UNSUPPORTED,
+                "create: the fused expert kernel needs bf16 activations, bf16 or MXFP4 experts "
+                "and m <= 1536");
   lmoe_handle* h = new (std::nothrow) lmoe_handle;
   if (!h) return fail(LMOE_ERR_ALLOC, "create: out of host memory");
   h->cfg = c;
@@ -691,6 +693,7 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.g_off = offsets; a.G = N;
     a.l = static_cast<int>(l); a.m = static_cast<int>(m);
     a.act = act1;
+    if (edt == lmoe::Dt::MXFP4) { a.W1_mx = w->w1_mx; a.W2_mx = w->w2_mx; }
     LMOE_TRY(lmoe::launch_ffn_stream(a, s), "FC1 + FC2 (fused)");
   } else {
     lmoe::GemmArgs a;

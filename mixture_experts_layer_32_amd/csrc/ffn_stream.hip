@@ -6,7 +6,11 @@
 // (the expert FFN of the LatentMoE paper, Eq. (2): both expert GEMMs run in
 // the latent width l, with the squared-ReLU activation of Table 2).  With
 // SwiGLU experts W1 holds 2m rows, up-projection and gate rows interleaved,
-// and H[i] = up_i * SiLU(gate_i): FC1 streams twice the rows.
+// and H[i] = up_i * SiLU(gate_i): FC1 streams twice the rows.  With MXFP4
+// weights (E2M1 pairs, an E8M0 scale per 32 elements) a lane takes 16
+// consecutive elements of a row per stage (one 8-byte load and its block's
+// scale byte) and widens them to two bf16 MFMA operands; the token and H
+// fragments then take the matching reduction indices.
 //
 // With a few dozen token rows per expert both GEMMs are bound by streaming
 // the expert weights from HBM.  Writing H out and reading it back, as two
@@ -37,6 +41,7 @@
 // rows, chunks past K, loads past the last expert); tiles are padded to a
 // multiple of the register-rotation period with stages that load nothing.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -71,6 +76,7 @@ struct FfnUnit {
   int gs, cnt;       // first grouped row of the expert and its row count
   int p0, rows;      // this pass's first row (within the expert) and its rows
   BufRsrc w1, w2;    // the expert's weight matrices
+  BufRsrc s1, s2;    // MXFP4: their block scales
   uint32_t a_off;       // this thread's staged token chunk, or out of range
 
   __device__ __forceinline__ void assign(const FfnUnit& o) {
@@ -82,12 +88,25 @@ struct FfnUnit {
     rows = o.rows;
     w1 = o.w1;
     w2 = o.w2;
+    s1 = o.s1;
+    s2 = o.s2;
     a_off = o.a_off;
   }
 };
 
-template <bool GLU>
+// Weight registers of one stage: bf16 rows (kNLD 16-byte chunks per n-block),
+// or MXFP4 rows (one 8-byte piece and its scale byte per n-block)
+struct WStageBf16 {
+  u32x4 b[kNWB][kNLD];
+};
+struct WStageFp4 {
+  u32x2 b[kNWB];
+  uint32_t s[kNWB];
+};
+
+template <bool GLU, bool FP4>
 __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
+  using WS = std::conditional_t<FP4, WStageFp4, WStageBf16>;
   __shared__ u32x4 Hs[kRows * kMaxM / 8];  // H, 16-byte chunk c of row r at c ^ (r & 7)
   __shared__ u32x4 As[2][kAChunks];        // FC1 token stages, chunk c of row r at c ^ ((r >> 1) & 7)
 
@@ -105,13 +124,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   const int s2p = (s2 + kP - 1) / kP * kP;
   const int t1 = (N1 + kTileN - 1) / kTileN; // FC1 tiles (of W1 rows)
   const int t2 = (L + kTileN - 1) / kTileN;  // FC2 tiles (Y columns)
-  const uint32_t rb1 = static_cast<uint32_t>(L) * 2u;  // W1 row bytes
-  const uint32_t rb2 = static_cast<uint32_t>(M) * 2u;  // W2 row bytes
+  const uint32_t rb1 = FP4 ? static_cast<uint32_t>(L) / 2u : static_cast<uint32_t>(L) * 2u;  // W1 row bytes
+  const uint32_t rb2 = FP4 ? static_cast<uint32_t>(M) / 2u : static_cast<uint32_t>(M) * 2u;  // W2 row bytes
+  const uint32_t sb1 = static_cast<uint32_t>(L) / 32u;  // MXFP4: scale bytes per W1 row
+  const uint32_t sb2 = static_cast<uint32_t>(M) / 32u;  // and per W2 row
   const uint32_t a_row_bytes = static_cast<uint32_t>(p.lda) * 2u;
   const BufRsrc a_rsrc = make_rsrc(p.A, (uint64_t)p.a_nrows * p.lda * 2u);
   const BufRsrc goff_rsrc = make_rsrc(p.g_off, (uint64_t)(p.G + 1) * sizeof(int32_t));
-  const uint16_t* const w1g = static_cast<const uint16_t*>(p.W1);
-  const uint16_t* const w2g = static_cast<const uint16_t*>(p.W2);
+  const uint8_t* const w1g = static_cast<const uint8_t*>(p.W1);
+  const uint8_t* const w2g = static_cast<const uint8_t*>(p.W2);
   uint16_t* const Y = static_cast<uint16_t*>(p.Y);
   const int nl = wave * (kNWB * 16) + fr;    // weight row of n-block 0 within a tile
   const int ar = tid >> 3, ac = tid & 7;     // staged token chunk of this thread
@@ -122,8 +143,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
     u.e = e;
     u.valid = e < p.G;
     const int64_t ee = u.valid ? e : 0;
-    u.w1 = make_rsrc(w1g + ee * N1 * L, (uint64_t)N1 * rb1);
-    u.w2 = make_rsrc(w2g + ee * L * M, (uint64_t)L * rb2);
+    u.w1 = make_rsrc(w1g + ee * N1 * rb1, (uint64_t)N1 * rb1);
+    u.w2 = make_rsrc(w2g + ee * L * rb2, (uint64_t)L * rb2);
+    if constexpr (FP4) {
+      u.s1 = make_rsrc(p.W1_mx + ee * N1 * sb1, (uint64_t)N1 * sb1);
+      u.s2 = make_rsrc(p.W2_mx + ee * L * sb2, (uint64_t)L * sb2);
+    }
     u.gs = 0;
     u.cnt = 0;
     u.p0 = 0;
@@ -182,22 +207,39 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   };
 
   // weight chunks of stage ks of tile t of GEMM ph
-  auto load_w = [&](const FfnUnit& u, int ph, int t, int ks, bool live,
-                    u32x4 (&br)[kNWB][kNLD]) {
+  auto load_w = [&](const FfnUnit& u, int ph, int t, int ks, bool live, WS& ws) {
     const int N = ph == 0 ? N1 : L;
     const uint32_t rb = ph == 0 ? rb1 : rb2;
     const bool lv = live && ks < (ph == 0 ? s1 : s2);
-    const uint32_t so = static_cast<uint32_t>(ks) * (kKE * 2) + 16u * fq;
+    if constexpr (FP4) {
+      // elements 16 fq .. 16 fq + 15 of the stage: 8 bytes, one scale block
+      const uint32_t sb = ph == 0 ? sb1 : sb2;
+      const uint32_t so = static_cast<uint32_t>(ks) * (kKE / 2) + 8u * fq;
+      const uint32_t ss = static_cast<uint32_t>(ks) * (kKE / 32) + (fq >> 1);
 #pragma unroll
-    for (int nb = 0; nb < kNWB; ++nb) {
-      const int n = t * kTileN + nl + nb * 16;
-      const uint32_t vo = (lv && n < N) ? static_cast<uint32_t>(n) * rb + so : kOutOfRange;
-      if (ph == 0) {
+      for (int nb = 0; nb < kNWB; ++nb) {
+        const int n = t * kTileN + nl + nb * 16;
+        const bool in = lv && n < N;
+        const uint32_t vo = in ? static_cast<uint32_t>(n) * rb + so : kOutOfRange;
+        const uint32_t vs = in ? static_cast<uint32_t>(n) * sb + ss : kOutOfRange;
+        ws.b[nb] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(ph == 0 ? u.w1 : u.w2,
+                                                        static_cast<int>(vo), 0, 0));
+        ws.s[nb] = buffer_load_byte(ph == 0 ? u.s1 : u.s2, vs);
+      }
+    } else {
+      const uint32_t so = static_cast<uint32_t>(ks) * (kKE * 2) + 16u * fq;
 #pragma unroll
-        for (int j = 0; j < kNLD; ++j) br[nb][j] = buffer_load_chunk(u.w1, vo + 64u * j, 0u);
-      } else {
+      for (int nb = 0; nb < kNWB; ++nb) {
+        const int n = t * kTileN + nl + nb * 16;
+        const uint32_t vo = (lv && n < N) ? static_cast<uint32_t>(n) * rb + so : kOutOfRange;
+        if (ph == 0) {
 #pragma unroll
-        for (int j = 0; j < kNLD; ++j) br[nb][j] = buffer_load_chunk(u.w2, vo + 64u * j, 0u);
+          for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(u.w1, vo + 64u * j, 0u);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(u.w2, vo + 64u * j, 0u);
+        }
       }
     }
   };
@@ -219,17 +261,25 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
 
   // one stage: weights first (rows n), token rows second, so that a lane
   // ends with D[n = 4 fq + v][row = fr] of each 16 x 16 block
-  auto compute = [&](int ph, int ks, int buf, const u32x4 (&br)[kNWB][kNLD]) {
+  auto compute = [&](int ph, int ks, int buf, const WS& ws) {
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
+      // chunk of the stage: reduction elements 32 s + 8 fq .. (bf16 weights),
+      // 16 fq + 8 s .. (MXFP4: a lane's 16 consecutive elements)
+      const int c = FP4 ? 2 * fq + s : 4 * s + fq;
+      u32x4 bfr[kNWB];
+#pragma unroll
+      for (int nb = 0; nb < kNWB; ++nb) {
+        if constexpr (FP4) bfr[nb] = fp4x8_to_bf16x8(ws.b[nb][s], e8m0_to_f32(ws.s[nb]));
+        else bfr[nb] = ws.b[nb][s];
+      }
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const int r = mb * 16 + fr;
-        const int c = 4 * s + fq;  // chunk of the stage: reduction elements 32 s + 8 fq ..
         const u32x4 a = ph == 0 ? As[buf][r * 8 + (c ^ ((r >> 1) & 7))]
                                 : Hs[r * hcpr + ((ks * 8 + c) ^ (r & 7))];
 #pragma unroll
-        for (int nb = 0; nb < kNWB; ++nb) MmaBf16::mma(acc[mb][nb], br[nb][s], a);
+        for (int nb = 0; nb < kNWB; ++nb) MmaBf16::mma(acc[mb][nb], bfr[nb], a);
       }
     }
   };
@@ -238,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   FfnUnit cur, nxt;
   set_expert(cur, blockIdx.x);
   if (!cur.valid) return;
-  u32x4 bw[kWD + 1][kNWB][kNLD];
+  WS bw[kWD + 1];
   u32x4 ra[2];
   // its first weight stages depend on the expert alone
 #pragma unroll
@@ -372,13 +422,21 @@ hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s) {
       a.lda < a.l || (a.act != kActSqRelu && a.act != kActSwiGlu))
     return hipErrorInvalidValue;
   const bool glu = a.act == kActSwiGlu;
+  const bool fp4 = a.W1_mx != nullptr;
+  // MXFP4: both scale arrays, whole scale blocks per row
+  if (fp4 && (!a.W2_mx || a.l % 32 || a.m % 32)) return hipErrorInvalidValue;
   // 32-bit buffer offsets: token rows and one expert matrix stay below 2 GiB
   if ((uint64_t)a.a_nrows * a.lda * 2u >= (1ull << 31) ||
       (uint64_t)(glu ? 2 : 1) * a.m * a.l * 2u >= (1ull << 31))
     return hipErrorInvalidValue;
   const int grid = std::min(a.G, device_compute_units());
-  if (glu) ffn_stream_kernel<true><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
-  else ffn_stream_kernel<false><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+  if (fp4) {
+    if (glu) ffn_stream_kernel<true, true><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+    else ffn_stream_kernel<false, true><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+  } else {
+    if (glu) ffn_stream_kernel<true, false><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+    else ffn_stream_kernel<false, false><<<dim3(grid), dim3(kThreads), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

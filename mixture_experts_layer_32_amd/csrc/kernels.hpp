@@ -96,6 +96,10 @@ struct FfnArgs {
   int G = 0;
   int l = 0, m = 0;
   int act = kActSqRelu;             // or kActSwiGlu: W1 is [G][2m][l], rows interleaved
+  // MXFP4 weights: W1, W2 hold E2M1 pairs, W1_mx [G][m or 2m][l/32] and
+  // W2_mx [G][l][m/32] their E8M0 block scales (l, m multiples of 32)
+  const uint8_t* W1_mx = nullptr;
+  const uint8_t* W2_mx = nullptr;
 };
 // Whether the fused kernel takes this shape (the hidden rows fit in LDS).
 bool ffn_stream_fits(int l, int m);

@@ -113,9 +113,15 @@ def test_create_checks_mxfp4_constraints():
     assert pkg.lib().latentmoe_expert_regime(h, 4096) == b"stream"   # streaming kernel only
     pkg.lib().latentmoe_destroy(h)
     for spec, kind in ((mx.replace(l=48), "auto"), (mx.replace(m=144), "auto"),
-                       (mx, "tiled"), (mx, "fused"), (mx.replace(act_dtype="f32"), "auto")):
+                       (mx, "tiled"), (mx.replace(m=1600), "fused"),
+                       (mx.replace(act_dtype="f32"), "auto")):
         st, _ = _create(pkg.make_config(spec, kind))
         assert st == -2, (spec, kind)
+    fused = pkg.LatentMoELayer(mx, expert_kernel="fused")     # MXFP4 in the fused kernel
+    assert fused.expert_regime(64) == "fused"
+    auto = pkg.LatentMoELayer(workload("latent_mxfp4_decode").spec)
+    assert auto.expert_regime(512) == "stream"                 # fused only when forced
+    assert auto.expert_regime(4096) == "stream"
 
 
 def test_create_checks_shared_expert_sizes():

@@ -2,8 +2,9 @@
 32) against the fp64 oracle, through the C ABI.
 
 The streaming expert kernel widens each 16-byte chunk (32 elements, one
-scale block) to bf16 with the gfx950 scaled conversion; the oracle decodes
-the same codes exactly.  Small cases: ragged shapes, 64- and 128-row passes,
+scale block) to bf16 with the gfx950 scaled conversion, the fused decode
+FFN each 8-byte piece (16 elements); the oracle decodes the same codes
+exactly.  Small cases: ragged shapes, 64- and 128-row passes,
 multi-pass experts under a skewed router, K not a multiple of the 128-element
 stage, SwiGLU with shared experts, the standard MoE, one token.  Full size:
 the iso-cost LatentMoE decode layer with MXFP4 experts on sampled tokens.
@@ -90,3 +91,44 @@ def test_full_size_mxfp4_decode():
     check_routing_structure(spec, g, T)
     st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T))
     print(wl.name, st, flush=True)
+
+
+# the fused FC1 + FC2 kernel with MXFP4 weights, forced on shapes the
+# automatic choice would not give it: ragged l and m (last 64-element stage
+# partly past K), multi-pass experts with SwiGLU, the widest hidden layer,
+# a skewed router with empty experts
+FUSED = {
+    "fused_ragged": (_mx(LayerSpec(d=1056, l=1056, m=544, n_experts=24, top_k=4,
+                                   gating="sigmoid_topk_norm")), 200),
+    "fused_multipass_swiglu": (_mx(LayerSpec(d=256, l=128, m=192, n_experts=8, top_k=4,
+                                             gating="softmax_topk", activation="swiglu")), 300),
+    "fused_m1536": (_mx(LayerSpec(d=512, l=256, m=1536, n_experts=300, top_k=2,
+                                  gating="softmax_topk")), 600),
+    "fused_zipf_empty": (_mx(LayerSpec(d=256, l=64, m=128, n_experts=64, top_k=4,
+                                       gating="softmax_all", has_router_bias=True)), 256),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_mxfp4_fused_matches_oracle(name):
+    import mixture_experts_layer_32_amd as pkg
+    spec, T = FUSED[name]
+    layer = pkg.LatentMoELayer(spec, expert_kernel="fused")
+    assert layer.expert_regime(T) == "fused"
+    w, x = _case(spec, T, seed=9)
+    g, _ = run_gpu(spec, w, x, layer=layer)
+    check_routing_structure(spec, g, T)
+    st = check_against_oracle(spec, w, x, g)
+    print(name, st, flush=True)
+
+
+def test_mxfp4_fused_and_stream_agree():
+    import mixture_experts_layer_32_amd as pkg
+    spec, T = _mx(LayerSpec(d=512, l=256, m=384, n_experts=32, top_k=4,
+                            gating="sigmoid_topk_norm")), 256
+    w, x = _case(spec, T, seed=3)
+    a, _ = run_gpu(spec, w, x, layer=pkg.LatentMoELayer(spec, expert_kernel="fused"))
+    b, _ = run_gpu(spec, w, x, layer=pkg.LatentMoELayer(spec, expert_kernel="stream"))
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    rel = np.linalg.norm(a["out"] - b["out"], axis=1) / np.linalg.norm(b["out"], axis=1)
+    assert rel.max() < 2e-2, rel.max()
