@@ -119,6 +119,10 @@ FORCED = {
     "stream_sparse_fp8": (LayerSpec(d=256, l=64, m=128, n_experts=256, top_k=2,
                                     gating="sigmoid_topk_norm", expert_dtype="fp8_e4m3_rowscale"),
                           100, "stream"),
+    # sparse, with the dispatch in three kernels (4 token blocks x 2048 experts
+    # exceed the single-workgroup route): the scan kernel writes the list
+    "stream_sparse_route_scan": (LayerSpec(d=256, l=64, m=128, n_experts=2048, top_k=8,
+                                           gating="softmax_all"), 200, "stream"),
 }
 
 
