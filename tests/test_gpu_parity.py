@@ -233,3 +233,30 @@ def test_mid_size_large_tiles_sampled_tokens(name):
     st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T, n=40, seed=9))
     print(name, st, flush=True)
 
+
+
+def test_one_handle_on_two_streams_at_once():
+    """The handle is immutable: two calls in flight on two streams, each with
+    its own workspace and output, give the results of separate calls."""
+    import torch
+    import mixture_experts_layer_32_amd as pkg
+    spec, T = SMALL["bf16_zipf_bias_tiled"]
+    layer = pkg.LatentMoELayer(spec)
+    w = synth.make_weights(spec, 0)
+    dev = pkg.to_device(w, "cuda:0")
+    xs = [pkg.to_device({"x": synth.make_tokens(spec, T, seed)}, "cuda:0")["x"] for seed in (1, 2)]
+    ref = []
+    for x in xs:
+        ref.append(layer.forward(x, dev).clone())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(r) for r in ref]
+    wss = [torch.empty((layer.workspace_size(T),), dtype=torch.uint8, device="cuda:0")
+           for _ in xs]
+    cw = layer.weights_struct(dev)
+    for _ in range(3):
+        for x, o, ws, st in zip(xs, outs, wss, streams):
+            layer.forward(x, None, out=o, workspace=ws, cweights=cw, stream=st)
+    torch.cuda.synchronize()
+    for o, r in zip(outs, ref):
+        assert torch.equal(o, r)
