@@ -67,7 +67,17 @@ def expert_kernel_kind(name: str) -> str | None:
     if "gemm_tiled_kernel<" in name and ("TileCfg<128, 256" in name or "unsigned char" in name
                                          or ", u8," in name):
         return "gemm_tiled"
+    # the 256 x 256 tile serves the dense projections too: only an instance
+    # with an activation (the experts' FC1; the dense GEMMs have none, the
+    # shared experts run on other tiles) is attributed
+    if "gemm_tiled_kernel<" in name and "TileCfg<256, 256" in name and _act_arg(name) != "0":
+        return "gemm_tiled"
     return None
+
+
+def _act_arg(name: str) -> str:
+    """ACT, the second to last template argument of a GEMM kernel name."""
+    return [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")][-2]
 
 
 def expert_stage(name: str) -> str | None:
@@ -79,8 +89,7 @@ def expert_stage(name: str) -> str | None:
         return None
     if kind == "ffn_stream":
         return "ffn"
-    args = [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")]
-    return "fc1" if args[-2] != "0" else "fc2"
+    return "fc1" if _act_arg(name) != "0" else "fc2"
 
 
 def _one(path_dir: str, suffix: str) -> str:

@@ -45,6 +45,13 @@ NAMES = {
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned char, unsigned short, lmoe::TileCfg<96, 256, 1, 4, 8, 2, 2>, 0, true>"
     "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc2"),
+    "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
+    "unsigned short, unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 1, false>"
+    "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc1"),
+    # the same tile without activation is shared with the dense projections
+    "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
+    "unsigned short, unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 0, false>"
+    "(lmoe::GemmArgs, int, float*)": (None, None),
     # dense GEMMs (projections, router, shared experts) and routing are not expert kernels
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, float, lmoe::TileCfg<128, 128, 2, 2, 8, 2, 2>, 1, false>"
