@@ -78,9 +78,16 @@ def _load():
             lib.orc_forward.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_Weights), vp, vp,
                                         i64, vp, vp, vp, vp, vp, vp, vp]
             lib.orc_forward.restype = ctypes.c_int
+            lib.orc_route.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_Weights), vp, i64,
+                                      vp, vp, vp]
+            lib.orc_route.restype = ctypes.c_int
             lib.orc_forward_dense.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_Weights),
                                               vp, vp, i64, vp, vp]
             lib.orc_forward_dense.restype = ctypes.c_int
+            lib.orc_set_threads.argtypes = [ctypes.c_int]
+            lib.orc_set_threads.restype = None
+            lib.orc_max_threads.argtypes = []
+            lib.orc_max_threads.restype = ctypes.c_int
             lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
             lib.orc_bf16_to_f64.restype = ctypes.c_double
             lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
@@ -145,6 +152,26 @@ def forward(spec, weights: dict, x: np.ndarray, tokens=None, forced=None,
     return res
 
 
+def route(spec, weights: dict, x: np.ndarray, want_logits: bool = False) -> dict:
+    """Routing alone for every row of x: idx [T][K] (z desc, id asc), margin
+    [T] (z_(K) - z_(K+1)) and optionally the fp64 logits [T][N] (with the
+    router bias); no expert is evaluated."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    n = x.shape[0]
+    K, N = spec.top_k, spec.n_experts
+    res = {"idx": np.empty((n, K), np.int32), "margin": np.empty((n,))}
+    res["logits"] = np.empty((n, N)) if want_logits else None
+    L = _layer(spec)
+    cw, keep = _weights(weights)
+    rc = lib.orc_route(ctypes.byref(L), ctypes.byref(cw), _p(x), n, _p(res["idx"]),
+                       _p(res["margin"]), _p(res["logits"]))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle rejected the layer configuration or inputs")
+    return res
+
+
 def forward_dense(spec, weights: dict, x: np.ndarray, tokens=None) -> dict:
     """Brute-force reference: all experts evaluated, dense masked gate mix."""
     lib = _load()
@@ -160,6 +187,16 @@ def forward_dense(spec, weights: dict, x: np.ndarray, tokens=None) -> dict:
     if rc != 0:
         raise ValueError("oracle rejected the layer configuration or inputs")
     return {"out": out, "gate_dense": G}
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP token loops."""
+    _load().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    """Threads the next oracle call will use."""
+    return int(_load().orc_max_threads())
 
 
 def bf16_to_f64(bits: int) -> float:

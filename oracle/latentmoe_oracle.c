@@ -18,6 +18,7 @@
 #include "latentmoe_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -40,18 +41,6 @@ double orc_e4m3_to_f64(uint8_t code) {
   else
     v = ldexp(1.0 + m / 8.0, e - 7);
   return s ? -v : v;
-}
-
-/* fp64 -> nearest bf16 value (ties to even), finite inputs: keep 8
- * significant bits of the binary significand. */
-static double round_bf16(double v) {
-  if (v == 0.0 || !isfinite(v)) return v;
-  int e;
-  double m = frexp(v, &e);             /* v = m 2^e, 0.5 <= |m| < 1 */
-  int bits = 8;
-  if (e - 1 < -126) bits -= -126 - (e - 1);  /* bf16 subnormals */
-  if (bits < 0) return copysign(0.0, v);
-  return ldexp(nearbyint(ldexp(m, bits)), e - bits);
 }
 
 /* OCP MX FP4 element, E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit;
@@ -111,11 +100,25 @@ static int check(const orc_layer *L, const orc_weights *W, const void *x, int64_
   return 0;
 }
 
-/* Steps shared by the sparse and the dense evaluation of one token:
- * latent u (l) and router logits z (N). */
-static void latent_and_logits(const orc_layer *L, const orc_weights *W, const void *x, int64_t t,
-                              double *xt, double *u, double *z) {
-  const int64_t d = L->d, l = L->l, N = L->n_experts;
+/* z = W_r . r [+ b], r = x (d wide) or the latent u (l wide): the router
+ * logits over the N experts, from the unrounded fp64 input. */
+static void router_logits(const orc_layer *L, const orc_weights *W, const double *xt,
+                          const double *u, double *z) {
+  const double *rin = L->router_on_latent ? u : xt;
+  const int64_t rw = L->router_on_latent ? L->l : L->d;
+  for (int64_t e = 0; e < L->n_experts; ++e) {
+    double s = 0.0;
+    for (int64_t c = 0; c < rw; ++c) s += ld(W->w_router, L->act_dtype, e * rw + c, NULL, 0, NULL) * rin[c];
+    if (L->has_router_bias) s += (double)W->router_bias[e];
+    z[e] = s;
+  }
+}
+
+/* Token t's input x_t (d) and latent u_t = W_down . x_t (l; u = x for the
+ * standard MoE). */
+static void input_and_latent(const orc_layer *L, const orc_weights *W, const void *x, int64_t t,
+                             double *xt, double *u) {
+  const int64_t d = L->d, l = L->l;
   for (int64_t c = 0; c < d; ++c) xt[c] = ld(x, L->act_dtype, t * d + c, NULL, 0, NULL);
   if (L->has_projections) {
     for (int64_t r = 0; r < l; ++r) {        /* u = W_down . x, W_down in R^{l x d} */
@@ -126,21 +129,14 @@ static void latent_and_logits(const orc_layer *L, const orc_weights *W, const vo
   } else {
     for (int64_t c = 0; c < d; ++c) u[c] = xt[c];
   }
-  const double *rin = L->router_on_latent ? u : xt;
-  const int64_t rw = L->router_on_latent ? l : d;
-  for (int64_t e = 0; e < N; ++e) {          /* z = W_r . (x or u) [+ b] */
-    double s = 0.0;
-    for (int64_t c = 0; c < rw; ++c) {
-      /* a router on the latent reads u as stored in the activation dtype, so
-       * the expert selection is decided on the same input values as the
-       * kernel's; everything else stays unrounded */
-      double r = rin[c];
-      if (L->router_on_latent && L->act_dtype == ORC_BF16) r = round_bf16(r);
-      s += ld(W->w_router, L->act_dtype, e * rw + c, NULL, 0, NULL) * r;
-    }
-    if (L->has_router_bias) s += (double)W->router_bias[e];
-    z[e] = s;
-  }
+}
+
+/* Steps shared by the sparse and the dense evaluation of one token:
+ * latent u (l) and router logits z (N). */
+static void latent_and_logits(const orc_layer *L, const orc_weights *W, const void *x, int64_t t,
+                              double *xt, double *u, double *z) {
+  input_and_latent(L, W, x, t, xt, u);
+  router_logits(L, W, xt, u, z);
 }
 
 /* The nonlinearity between the two expert matrices: a = W_FC1 row . input,
@@ -380,8 +376,51 @@ int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
   return bad ? -1 : 0;
 }
 
+/* Routing alone: for tokens 0 .. n-1, the fp64 router logits (+ bias), the
+ * top-K ids ordered by (z desc, id asc) and the margin z_(K) - z_(K+1),
+ * exactly as orc_forward takes them, without the experts.  The latent is
+ * computed only when the router reads it. */
+int orc_route(const orc_layer *L, const orc_weights *W, const void *x, int64_t n, int32_t *idx,
+              double *margin, double *logits) {
+  if (check(L, W, x, n) || !idx || !margin) return -1;
+  const int64_t d = L->d, l = L->l, N = L->n_experts, K = L->top_k;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *xt = malloc(sizeof(double) * (size_t)d);
+    double *u = malloc(sizeof(double) * (size_t)(l > d ? l : d));
+    double *z = malloc(sizeof(double) * (size_t)N);
+    int32_t *ord = malloc(sizeof(int32_t) * (size_t)N);
+    const int ok = xt && u && z && ord;
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t t = 0; t < n; ++t) {
+        if (!ok) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        if (L->router_on_latent) {
+          input_and_latent(L, W, x, t, xt, u);
+        } else {
+          for (int64_t c = 0; c < d; ++c) xt[c] = ld(x, L->act_dtype, t * d + c, NULL, 0, NULL);
+        }
+        router_logits(L, W, xt, u, z);
+        if (logits) memcpy(logits + t * N, z, sizeof(double) * (size_t)N);
+        sort_by_score(ord, N, z);
+        margin[t] = K < N ? z[ord[K - 1]] - z[ord[K]] : INFINITY;
+        for (int64_t j = 0; j < K; ++j) idx[t * K + j] = ord[j];
+      }
+    free(xt); free(u); free(z); free(ord);
+  }
+  return bad ? -1 : 0;
+}
+
 void orc_expert_counts(const int32_t *idx, int64_t n, int64_t K, int64_t N, int64_t *counts) {
   for (int64_t e = 0; e < N; ++e) counts[e] = 0;
   for (int64_t i = 0; i < n * K; ++i)
     if (idx[i] >= 0 && idx[i] < N) ++counts[idx[i]];
 }
+
+/* OpenMP threads of the token loops (results do not depend on it). */
+void orc_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+int orc_max_threads(void) { return omp_get_max_threads(); }

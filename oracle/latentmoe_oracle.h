@@ -32,9 +32,7 @@
  * Every sum runs in ascending index order, in fp64, with no intermediate
  * rounding; stored bf16, fp8 and MXFP4 values are upcast exactly (fp8 as
  * q * row scale, MXFP4 as e2m1 * 2^(e8m0 - 127)).
- * One exception: a router placed on the latent u reads u rounded to bf16
- * when activations are bf16, so that the top-K decision is taken on the
- * values the GPU kernel routes on.
+ * The router reads the unrounded fp64 x or u, like every other step.
  */
 #ifndef LATENTMOE_ORACLE_H
 #define LATENTMOE_ORACLE_H
@@ -105,11 +103,23 @@ int orc_forward(const orc_layer *L, const orc_weights *W, const void *x, const i
 int orc_forward_dense(const orc_layer *L, const orc_weights *W, const void *x,
                       const int64_t *tok, int64_t n, double *out, double *gate_dense);
 
+/* Routing only (§3: logits, then the top-K set T_{K,N'}), for tokens 0 .. n-1:
+ * idx [n][K] ordered by (z desc, id asc), margin [n] = z_(K) - z_(K+1)
+ * (+inf when K == N), logits [n][N] (nullable), the same values orc_forward
+ * returns for them.  No expert is evaluated.  Returns 0, or -1 on invalid
+ * arguments. */
+int orc_route(const orc_layer *L, const orc_weights *W, const void *x, int64_t n, int32_t *idx,
+              double *margin, double *logits);
+
 /* Exact upcasts of the storage formats. */
 double orc_bf16_to_f64(uint16_t bits);
 double orc_e4m3_to_f64(uint8_t code); /* OCP E4M3: bias 7, S.1111.111 = NaN */
 double orc_e2m1_to_f64(uint8_t code); /* OCP MX FP4 E2M1 (low 4 bits of code) */
 double orc_e8m0_to_f64(uint8_t e);    /* OCP MX scale 2^(e-127); 0xFF = NaN */
+
+/* Threads of the OpenMP token loops (the results do not depend on them). */
+void orc_set_threads(int n);
+int orc_max_threads(void);
 
 /* Per-expert copy counts from an [n][K] id table. */
 void orc_expert_counts(const int32_t *idx, int64_t n, int64_t K, int64_t N, int64_t *counts);

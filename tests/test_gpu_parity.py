@@ -14,7 +14,8 @@ import pytest
 import synth
 from synth import LayerSpec, workload
 
-from parity_util import check_against_oracle, check_routing_structure, run_gpu
+from parity_util import (check_against_oracle, check_routing_all_tokens,
+                         check_routing_structure, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -168,7 +169,10 @@ def test_identity_projections_equal_standard_moe_bit_exact(act):
     b, _ = run_gpu(std, w_std, x)
     assert np.array_equal(a["topk_idx"], b["topk_idx"])
     assert np.array_equal(a["out"], b["out"])
-    assert np.array_equal(a["latent"], x.astype(np.float64) if act == "f32" else a["latent"])
+    # W_down = I: the stored latent is x itself, bit for bit
+    xv = x.astype(np.float64) if act == "f32" else \
+        (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(a["latent"], xv)
     check_against_oracle(std, w_std, x, b)
 
 
@@ -211,8 +215,64 @@ def test_full_size_sampled_tokens(name):
     g, layer = run_gpu(spec, w, x)
     print(name, "regime", layer.expert_regime(T), flush=True)
     check_routing_structure(spec, g, T)
+    # every token: ids (unflagged) and per-expert counts bit-exact, logits
+    rt = check_routing_all_tokens(spec, w, x, g)
+    print(name, "routing", rt, flush=True)
     st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T))
     print(name, st, flush=True)
+
+
+def _tie_router(N, d, scen):
+    """Router rows and one-hot token columns so that every logit is an exact
+    small integer (sums of a few +-1, 2, 3 terms: no rounding in any order).
+    Scenario s uses column s of x; the values a_s[e] are W_r[e][s]."""
+    wr = np.zeros((N, d), np.float32)
+    for s, vals in enumerate(scen):
+        wr[:, s] = vals
+    return wr
+
+
+def _tie_scenarios(N, K, rng):
+    sc = [np.zeros(N)]                                        # all-zero router
+    a = np.zeros(N); a[rng.choice(N, 1)] = 3.0                 # one leader, then
+    tied = rng.choice(np.setdiff1d(np.arange(N), np.nonzero(a)[0]), K + 2, replace=False)
+    a[tied] = 2.0; sc.append(a)                                # K + 2 tied across the K-th place
+    b = np.full(N, -1.0); b[rng.choice(N, K + 5, replace=False)] = 1.0
+    sc.append(b)                                               # K + 5 tied at the top
+    c = rng.integers(-2, 3, N).astype(np.float64); sc.append(c)  # many ties everywhere
+    e = np.zeros(N); e[-(K - 1):] = 1.0; sc.append(e)          # top K-1 at the highest ids,
+    return sc                                                  # the rest from the zeros
+
+
+@pytest.mark.parametrize("N,K,gating", [(32, 4, "softmax_all"), (200, 6, "sigmoid_topk_norm"),
+                                        (512, 22, "softmax_topk"), (2048, 16, "softmax_all")])
+def test_crafted_ties_go_to_the_lower_expert_id(N, K, gating):
+    """Exact logit ties on the GPU (the kernel's single- and multi-holder
+    branches, ties within a lane and across lanes): the set taken is the K
+    best under (logit desc, id asc), fixed by construction."""
+    rng = np.random.default_rng(N + K)
+    spec = LayerSpec(d=128, l=64, m=64, n_experts=N, top_k=K, gating=gating)
+    scen = _tie_scenarios(N, K, rng)
+    w = synth.make_weights(spec, 0)
+    wr = _tie_router(N, spec.d, scen)
+    w = dict(w, w_router=(wr.view(np.uint32) >> 16).astype(np.uint16))   # exact in bf16
+    T = 4 * len(scen)
+    x32 = np.zeros((T, spec.d), np.float32)
+    for t in range(T):
+        x32[t, t % len(scen)] = 1.0
+    x = (x32.view(np.uint32) >> 16).astype(np.uint16)
+    g, _ = run_gpu(spec, w, x)
+    check_routing_structure(spec, g, T)
+    for t in range(T):
+        z = wr[:, t % len(scen)].astype(np.float64)
+        want = sorted(np.lexsort((np.arange(N), -z))[:K].tolist())
+        assert sorted(g["topk_idx"][t].tolist()) == want, (t, scen[t % len(scen)][:8])
+        assert np.array_equal(g["logits"][t], z.astype(np.float32))
+    # the oracle takes the same sets, and the outputs agree (every token is
+    # flagged, margin 0, so outputs are compared with the GPU's sets)
+    ref = __import__("oracle").route(spec, w, x)
+    assert np.array_equal(np.sort(ref["idx"], 1), np.sort(g["topk_idx"], 1))
+    check_against_oracle(spec, w, x, g)
 
 
 # Sizes that select the large GEMM tiles (256 x 256 dense, 128 x 256 grouped,

@@ -316,19 +316,67 @@ def test_bf16_generator_rounds_to_nearest_even(orc, syn):
     assert syn.f64_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82
 
 
-def test_latent_router_bf16_reads_rounded_latent(orc):
-    """A bf16 latent router decides on u rounded to bf16 (the stored latent)."""
-    spec = LayerSpec(d=64, l=32, m=16, n_experts=9, top_k=3, gating="softmax_all",
+def test_latent_router_reads_unrounded_latent(orc):
+    """Closed form: l = d = 2, W_down = [[1, 2^-10], [1, 0]] and x = (1, 1) give
+    u = (1 + 2^-10, 1), which bf16 cannot hold (it would round u_0 to 1).
+    Router rows e0 = (0, 1) and e1 = (1, 0) on u: z = (1, 1 + 2^-10) exactly,
+    so with K = 1 expert 1 wins by a margin of exactly 2^-10.  An oracle that
+    rounded u to bf16 before routing would see a tie and pick expert 0."""
+    one, tiny = 0x3F80, 0x3A80                    # bf16 bits of 1 and 2^-10
+    spec = LayerSpec(d=2, l=2, m=1, n_experts=2, top_k=1, gating="softmax_topk",
                      act_dtype="bf16", expert_dtype="bf16", router_on_latent=True)
-    w, x = _inputs(spec, 12, seed=13)
-    r = orc.forward(spec, w, x, want_logits=True, want_latent=True)
-    u16 = np.array([[orc.bf16_to_f64(__import__("synth").f64_to_bf16(v)) for v in row]
-                    for row in r["latent"]])
-    Wr = _f64(orc, spec, w, "w_router")
-    np.testing.assert_allclose(r["logits"], u16 @ Wr.T, rtol=1e-12, atol=1e-13)
-    # with identity W_down the rounding is a no-op: same as routing on x
-    ident = workload("tiny_identity").spec.replace(act_dtype="bf16", expert_dtype="bf16")
-    wi, xi = _inputs(ident, 20, seed=6)
-    a = orc.forward(ident, wi, xi)
-    b = orc.forward(ident.replace(router_on_latent=True), wi, xi)
-    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["out"], b["out"])
+    b = lambda a: np.array(a, np.uint16)
+    w = {"w_down": b([[one, tiny], [one, 0]]), "w_router": b([[0, one], [one, 0]]),
+         "w1": b([[[one, 0]], [[one, 0]]]), "w2": b([[[one], [0]], [[one], [0]]]),
+         "w_up": b([[one, 0], [0, one]])}
+    x = b([[one, one]])
+    assert orc.bf16_to_f64(tiny) == 2.0 ** -10
+    for r in (orc.forward(spec, w, x, want_logits=True, want_latent=True),
+              orc.route(spec, w, x, want_logits=True)):
+        assert r["logits"].tolist() == [[1.0, 1.0 + 2.0 ** -10]]
+        assert r["idx"].tolist() == [[1]]
+        assert r["margin"].tolist() == [2.0 ** -10]
+    f = orc.forward(spec, w, x, want_latent=True)
+    assert f["latent"].tolist() == [[1.0 + 2.0 ** -10, 1.0]]
+    # expert 1 (gate 1): y = W2_1 (max(0, W1_1 u))^2 = ((1 + 2^-10)^2, 0), out = y
+    assert f["out"].tolist() == [[(1.0 + 2.0 ** -10) ** 2, 0.0]]
+
+
+ROUTE_SPECS = SMALL_SPECS + [
+    LayerSpec(d=96, l=48, m=16, n_experts=40, top_k=6, gating="sigmoid_topk_norm",
+              act_dtype="bf16", expert_dtype="bf16", router_on_latent=True),
+    LayerSpec(d=64, l=64, m=16, n_experts=130, top_k=9, gating="softmax_all", act_dtype="bf16",
+              expert_dtype="bf16", has_projections=False, has_router_bias=True),
+]
+
+
+@pytest.mark.parametrize("spec", ROUTE_SPECS, ids=lambda s: "N%dK%d_%s_lat%d" % (
+    s.n_experts, s.top_k, s.act_dtype, s.router_on_latent))
+def test_route_equals_forward_routing(orc, spec):
+    """The routing-only entry returns the ids, margins and logits that the
+    full evaluation takes, bit for bit, for every token."""
+    w, x = _inputs(spec, 37, seed=21)
+    a = orc.forward(spec, w, x, want_logits=True)
+    b = orc.route(spec, w, x, want_logits=True)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(a["margin"], b["margin"])
+    assert np.array_equal(a["logits"], b["logits"])
+
+
+def test_route_crafted_ties_lower_id_wins(orc):
+    """Exact ties placed across the K-th position: the lower ids are taken."""
+    spec = LayerSpec(d=16, l=8, m=8, n_experts=70, top_k=4, gating="softmax_all",
+                     act_dtype="f32", expert_dtype="f32")
+    w, _ = _inputs(spec, 1, seed=4)
+    wr = np.zeros((70, 16), np.float32)
+    wr[9, 0] = 3.0                       # a unique leader on token-column 0
+    wr[[66, 2, 64, 5, 40], 0] = 2.0      # five tied for the next places
+    wr[[1, 3], 1] = 1.0                  # token-column 1: two tied above zeros
+    x = np.zeros((3, 16), np.float32)
+    x[0, 0] = 1.0                        # leader + ties: {9} + lowest three of the five
+    x[1, 1] = 1.0                        # two, then the lowest two of 68 zeros
+    r = orc.route(spec, dict(w, w_router=wr), x)
+    assert sorted(r["idx"][0].tolist()) == [2, 5, 9, 40]
+    assert sorted(r["idx"][1].tolist()) == [0, 1, 2, 3]
+    assert r["idx"][2].tolist() == [0, 1, 2, 3]      # all-zero logits: ids in order
+    assert r["margin"].tolist() == [0.0, 0.0, 0.0]
