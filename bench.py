@@ -2,15 +2,19 @@
 """Benchmark of the LatentMoE layer forward on one MI355X.
 
 One step = one full layer forward (all stages: W_down + router GEMMs, top-k
-and gates, dispatch indices, grouped FC1 + squared ReLU, grouped FC2,
-combine, W_up, and the shared experts when the workload has them, by default
-on a side stream) over one batch of synthetic tokens already resident in HBM.
-Prints one JSON line: tokens/s (value), ms per step, the roofline of the
-dominant kernel (from HIP events recorded on the launch stream around each
-stage) and the fp64 CPU oracle's throughput on a bounded token sample.
+and gates, dispatch indices, grouped FC1 + activation, grouped FC2, combine,
+W_up, and the shared experts when the workload has them, by default on a
+side stream) over one batch of synthetic tokens already resident in HBM.
 
-Default workload: LatentMoE at iso-cost (d 4096, l 1024, m 1536, N 512,
-K 32, sigmoid gating, bf16), T = 512 tokens per call.
+The default run is the suite of the five layer configurations.  The JSON
+line's headline is the largest one, the 512-expert top-22 prefill layer
+(T 16384, d 4096, l 1024, m 2048: MFMA-bound); the line's "configs" object
+holds the same measurement for the other four (the tiny fp32 layer, the
+standard-MoE and LatentMoE decode layers, the fp8 896-expert layer).  Each
+carries tokens/s, ms per step, latency percentiles, the roofline of its
+dominant kernel (from HIP events the library records on the launch stream
+around each stage) and the fp64 CPU oracle's throughput on a bounded token
+sample.  --workload W runs one workload alone.
 """
 from __future__ import annotations
 
@@ -25,39 +29,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+HEADLINE = "latent_prefill_zipf"
+SUITE = ("latent_prefill_zipf", "tiny", "std_decode", "latent_decode", "latent_fp8_sparse")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def expert_kernel_work(spec, T, counts, stage):
-    """Algorithmic bytes and FLOPs of one FC1 or FC2 launch, or of the fused
-    FC1 + FC2 kernel (stage "ffn").
-
-    FC1 reads the weights of every expert that received tokens, reads each
-    latent row once and writes the T*K activated rows; FC2 reads the same
-    amount of expert weights, the T*K activated rows, and writes T*K latent
-    rows.  FLOPs: 2 * T*K * l * m per launch.  The fused kernel reads both
-    weight sets and each latent row once and writes the T*K latent rows; the
-    activated rows stay on chip.  SwiGLU experts: FC1 reads 2m weight rows
-    (up and gate) per expert and does twice the FLOPs.
-    """
+def expert_weight_bytes(spec, counts, stage):
+    """Expert-weight bytes one expert-FFN launch must read: both matrices
+    of every expert that received tokens for the fused kernel (stage
+    "ffn"), one matrix for FC1 / FC2 (SwiGLU FC1: up and gate rows), fp8
+    row scales and MXFP4 block scales included.  Token rows, H and Y are
+    intermediates and are not counted."""
     touched = int((counts > 0).sum())
     eb = spec.expert_bytes
-    ab = spec.act_bytes
-    l, m, K = spec.l, spec.m, spec.top_k
+    l, m = spec.l, spec.m
     m1 = 2 * m if spec.activation == "swiglu" else m
     w1 = touched * l * m1 * eb
     w2 = touched * l * m * eb
     if spec.expert_dtype == "fp8_e4m3_rowscale":
         w1 += touched * m1 * 4
         w2 += touched * l * 4
-    if stage == "ffn":
-        return float(w1 + w2 + T * l * ab + T * K * l * ab), 2.0 * T * K * l * (m1 + m)
-    if stage == "fc1":
-        return float(w1 + T * l * ab + T * K * m * ab), 2.0 * T * K * l * m1
-    return float(w2 + T * K * m * ab + T * K * l * ab), 2.0 * T * K * l * m
+    return float({"ffn": w1 + w2, "fc1": w1, "fc2": w2}[stage])
+
+
+def expert_kernel_work(spec, T, counts, stage):
+    """Algorithmic bytes (expert weights, expert_weight_bytes) and FLOPs
+    (2 * T*K * l * m per GEMM, SwiGLU FC1 twice that) of one FC1 or FC2
+    launch, or of the fused FC1 + FC2 kernel (stage "ffn")."""
+    l, m, K = spec.l, spec.m, spec.top_k
+    m1 = 2 * m if spec.activation == "swiglu" else m
+    flops = {"ffn": 2.0 * T * K * l * (m1 + m), "fc1": 2.0 * T * K * l * m1,
+             "fc2": 2.0 * T * K * l * m}[stage]
+    return expert_weight_bytes(spec, counts, stage), flops
 
 
 def layer_work(spec, T, counts):
@@ -90,68 +96,49 @@ def layer_work(spec, T, counts):
     return nbytes, flops
 
 
-def cpu_baseline(spec, w_np, x_np, budget_s=15.0):
+def cpu_baseline(spec, w_np, x_np, budget_s=10.0, threads=None):
     """The fp64 oracle on the first n tokens of the batch, n sized so that the
-    run takes about budget_s seconds on this host's cores."""
+    run takes about budget_s seconds on `threads` host threads (default: the
+    OpenMP default, all host cores)."""
     import oracle
     T = x_np.shape[0]
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    n = min(T, 2 * threads)                      # probe: two tokens per thread
-    t0 = time.perf_counter()
-    oracle.forward(spec, w_np, x_np, tokens=list(range(n)))
-    dt = time.perf_counter() - t0
-    per_tok = max(dt / n, 1e-6)
-    n2 = int(min(T, max(n, budget_s / per_tok)))
-    t0 = time.perf_counter()
-    oracle.forward(spec, w_np, x_np, tokens=list(range(n2)))
-    dt2 = time.perf_counter() - t0
-    return {"value": n2 / dt2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of the %d tokens of the same batch, full layer in fp64 "
-                      "(%.1f s)" % (n2, T, dt2)}
+    default = oracle.max_threads()
+    if threads:
+        oracle.set_threads(threads)
+    used = oracle.max_threads()
+    try:
+        n = min(T, 2 * used)                          # probe: two tokens per thread
+        t0 = time.perf_counter()
+        oracle.forward(spec, w_np, x_np, tokens=list(range(n)))
+        dt = time.perf_counter() - t0
+        per_tok = max(dt / n, 1e-7)
+        n2 = int(min(T, max(n, budget_s / per_tok)))
+        reps, dt2 = 0, 0.0
+        # a batch much shorter than the budget (the tiny layer) is repeated
+        while reps == 0 or (n2 == T and dt2 < 0.5 * budget_s):
+            t0 = time.perf_counter()
+            oracle.forward(spec, w_np, x_np, tokens=list(range(n2)))
+            dt2 += time.perf_counter() - t0
+            reps += 1
+    finally:
+        oracle.set_threads(default)
+    what = ("the %d tokens of the batch, %d times" % (T, reps) if reps > 1 else
+            "first %d of the %d tokens of the same batch" % (n2, T))
+    return {"value": reps * n2 / dt2, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "%s, full layer in fp64 (%.1f s)" % (what, dt2)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="latent_decode")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--overlap", choices=("on", "off"), default="on",
-                    help="shared experts on a side stream (on) or first on the launch stream")
-    ap.add_argument("--tokens", type=int, default=0,
-                    help="tokens per call (default: the workload's batch)")
-    ap.add_argument("--expert-kernel", choices=("auto", "tiled", "stream", "fused"),
-                    default="auto", help="force one expert-FFN kernel (default: the library's choice)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy (known HBM traffic: "
-                         "1 GiB read + 1 GiB written per launch) to scale rocprofv3 "
-                         "FETCH_SIZE / WRITE_SIZE readings")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, args, tokens=0, cpu=True, cpu_budget=10.0):
+    """One workload: inputs generated and moved to HBM, warmup, K timed
+    steps, per-step latencies, per-stage event times, the roofline of the
+    dominant kernel and of the whole step, and the oracle's CPU rate."""
     import numpy as np
     import torch
     import mixture_experts_layer_32_amd as pkg
     import synth
 
-    if args.copy_calibration:
-        a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda:0").fill_(1)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_read_per_launch": 1 << 30,
-                          "bytes_written_per_launch": 1 << 30, "launches": 5}))
-        return
-
-    wl = synth.workload(args.workload)
-    spec, T = wl.spec, (args.tokens or wl.T)
+    wl = synth.workload(name)
+    spec, T = wl.spec, (tokens or wl.T)
     dev = torch.device("cuda:0")
     log("bench: workload %s T=%d: generating inputs" % (wl.name, T))
     t0 = time.perf_counter()
@@ -231,16 +218,16 @@ def main():
         t_dom_ms = stage_avg[dom]
     nbytes, nflops = expert_kernel_work(spec, T, counts, dom)
     t_dom = t_dom_ms * 1e-3
+    mfma_peak = MFMA_PEAK_TFLOPS["f32" if spec.act_dtype == "f32" else "bf16"]
     if wl.regime == "prefill":
-        # the expert contraction runs on bf16 MFMA (fp8 weights are widened
-        # to bf16 in registers), f32 MFMA for fp32 layers
-        achieved = nflops / t_dom / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2),
-                "peak": MFMA_PEAK_TFLOPS["f32" if spec.act_dtype == "f32" else "bf16"],
-                "unit": "TFLOP/s"}
+        # the expert contraction runs on bf16 MFMA: FLOPs of the layer's
+        # definition (no tile padding) over the launch's duration
+        roof = {"bound": "mfma", "achieved": round(nflops / t_dom / 1e12, 2),
+                "peak": mfma_peak, "unit": "TFLOP/s"}
     else:
-        achieved = nbytes / t_dom / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        # expert weights streamed from HBM (the decode layers, the fp8 layer;
+        # the tiny fp32 layer is launch-latency bound and is reported the same way)
+        roof = {"bound": "hbm", "achieved": round(nbytes / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     # measured HBM bytes per launch of this kernel (rocprofv3 FETCH_SIZE and
@@ -254,10 +241,11 @@ def main():
     roof["algorithmic_bytes_per_launch"] = nbytes
     roof["algorithmic_flops_per_launch"] = nflops
     roof["launch_ms"] = round(t_dom_ms, 5)
+    if wl.regime == "tiny":
+        roof["note"] = "parity configuration; launch-latency bound"
 
     # the whole step against both ceilings
     lb, lf = layer_work(spec, T, counts)
-    mfma_peak = MFMA_PEAK_TFLOPS["f32" if spec.act_dtype == "f32" else "bf16"]
     layer_roof = {"algorithmic_bytes": lb, "algorithmic_flops": lf,
                   "hbm_frac": round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                   "mfma_frac": round(lf / (ms * 1e-3) / (mfma_peak * 1e12), 4),
@@ -283,15 +271,13 @@ def main():
                    "n_shared": spec.n_shared, "m_shared": spec.m_shared,
                    "activation": spec.activation,
                    "shared_on_side_stream": overlap is not None,
-                   "expert_kernel": layer.expert_regime(T)},
+                   "expert_kernel": regime},
         "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
         "latency_ms": {k: round(v, 5) for k, v in pct.items()},
         "roofline": roof,
         "layer_roofline": layer_roof,
         "experts": {"touched": int((counts > 0).sum()),
-                    "algorithmic_bytes": ({"ffn": nbytes} if dom == "ffn" else
-                                          {st: expert_kernel_work(spec, T, counts, st)[0]
-                                           for st in ("fc1", "fc2")})},
+                    "max_rows": int(counts.max()), "median_rows": float(np.median(counts))},
     }
     if spec.n_shared:
         # the shared experts' two dense GEMMs (their stage's events, on the
@@ -299,17 +285,78 @@ def main():
         hs = spec.n_shared * spec.m_shared
         nmat = 3 if spec.activation == "swiglu" else 2
         sf = 2.0 * nmat * T * spec.d * hs
-        sb = nmat * spec.d * hs * spec.act_bytes + T * spec.d * spec.act_bytes + \
-            2.0 * T * hs * spec.act_bytes + T * spec.d * 4.0
         t_sh = stage_avg["shared"] * 1e-3
-        res["shared_stage"] = {"ms": round(stage_avg["shared"], 5),
-                               "algorithmic_flops": sf, "algorithmic_bytes": sb,
+        res["shared_stage"] = {"ms": round(stage_avg["shared"], 5), "algorithmic_flops": sf,
                                "tflops": round(sf / t_sh / 1e12, 2) if t_sh > 0 else None,
                                "mfma_frac": round(sf / t_sh / (mfma_peak * 1e12), 4)
                                if t_sh > 0 else None}
-    if not args.no_cpu_baseline:
+    del d_all, x, out, ws, cw, layer, overlap
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu:
         log("bench: timing the fp64 CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(spec, w_np, x_np, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(spec, w_np, x_np, cpu_budget)
+        if wl.regime == "tiny":
+            res["cpu_baseline_1core"] = cpu_baseline(spec, w_np, x_np, cpu_budget / 2, threads=1)
+    return res
+
+
+CONFIG_KEYS = ("value", "unit", "ms_per_step", "dtype", "config", "stage_ms", "latency_ms",
+               "roofline", "layer_roofline", "experts", "cpu_baseline", "cpu_baseline_1core")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="suite",
+                    help="'suite' (default: the five layer configurations, headline %s) or one "
+                         "workload name" % HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work per configuration")
+    ap.add_argument("--overlap", choices=("on", "off"), default="on",
+                    help="shared experts on a side stream (on) or first on the launch stream")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per call (default: the workload's batch; single workloads only)")
+    ap.add_argument("--expert-kernel", choices=("auto", "tiled", "stream", "fused"),
+                    default="auto", help="force one expert-FFN kernel (default: the library's choice)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (known HBM traffic: "
+                         "1 GiB read + 1 GiB written per launch) to scale rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE readings")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": 1 << 30,
+                          "bytes_written_per_launch": 1 << 30, "launches": 5}))
+        return
+
+    cpu = not args.no_cpu_baseline
+    if args.workload != "suite":
+        print(json.dumps(measure(args.workload, args, args.tokens, cpu, args.cpu_budget)),
+              flush=True)
+        return
+    res = measure(HEADLINE, args, 0, cpu, args.cpu_budget)
+    res["configs"] = {HEADLINE: {k: res[k] for k in CONFIG_KEYS if k in res}}
+    for name in SUITE:
+        if name == HEADLINE:
+            continue
+        r = measure(name, args, 0, cpu, args.cpu_budget)
+        res["configs"][name] = {k: r[k] for k in CONFIG_KEYS if k in r}
     print(json.dumps(res), flush=True)
 
 

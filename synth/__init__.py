@@ -32,10 +32,13 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile synth.c into libsynth.so (gcc, OpenMP)."""
+    """Compile synth.c into libsynth.so (gcc, OpenMP).  sin and cos stay
+    separate library calls (no merged sincos), so every value is the same
+    whether its Box-Muller partner is computed in the same pass or not."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-Wall",
+        subprocess.check_call(["gcc", "-O2", "-fno-builtin-sin", "-fno-builtin-cos", "-fopenmp",
+                               "-shared", "-fPIC", "-Wall",
                                _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -55,7 +58,7 @@ def _load():
                 f.argtypes = [u64, u32, u64, i64, dbl, vp]
                 f.restype = None
             lib.synth_normal_fp8_rows.argtypes = [u64, u32, u64, i64, i64, dbl, vp, vp]
-            lib.synth_normal_fp8_rows.restype = None
+            lib.synth_normal_fp8_rows.restype = ctypes.c_int
             lib.synth_zipf_bias.argtypes = [u64, u32, i64, dbl, vp]
             lib.synth_zipf_bias.restype = ctypes.c_int
             lib.synth_permutation.argtypes = [u64, u32, i64, vp]
@@ -100,7 +103,8 @@ def normal_fp8_rows(seed: int, tid: int, rows: int, cols: int, std: float, offse
     lib = _load()
     q = np.empty((rows, cols), np.uint8)
     s = np.empty((rows,), np.float32)
-    lib.synth_normal_fp8_rows(seed, tid, offset, rows, cols, std, _ptr(q), _ptr(s))
+    if lib.synth_normal_fp8_rows(seed, tid, offset, rows, cols, std, _ptr(q), _ptr(s)) != 0:
+        raise MemoryError("synth: row buffer allocation failed")
     return q, s
 
 

@@ -21,6 +21,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define SYNTH_GAMMA 0x9E3779B97F4A7C15ULL
@@ -45,27 +46,49 @@ uint64_t synth_raw_u64(uint64_t seed, uint32_t tid, uint64_t i) {
   return sm_mix(stream_base(seed, tid) + (i + 1) * SYNTH_GAMMA);
 }
 
-static inline double normal_at(uint64_t base, uint64_t i) {
-  uint64_t p = i >> 1;
-  double u1 = unit_draw(base, 2 * p);
-  double u2 = unit_draw(base, 2 * p + 1);
-  double r = sqrt(-2.0 * log(u1));
-  double a = 6.283185307179586476925286766559 * u2;
-  return (i & 1) ? r * sin(a) : r * cos(a);
+/* out[i] = std * (normal j0 + i) for i < n: each Box-Muller pair (elements
+ * 2p, 2p+1 of the stream) is evaluated once for both of its elements. */
+static void normals_range(uint64_t base, uint64_t j0, int64_t n, double std, double *out) {
+  int64_t i = 0;
+  while (i < n) {
+    const uint64_t j = j0 + (uint64_t)i, p = j >> 1;
+    const double u1 = unit_draw(base, 2 * p);
+    const double u2 = unit_draw(base, 2 * p + 1);
+    const double r = sqrt(-2.0 * log(u1));
+    const double a = 6.283185307179586476925286766559 * u2;
+    if (j & 1) {
+      out[i++] = std * (r * sin(a));
+    } else {
+      out[i++] = std * (r * cos(a));
+      if (i < n) out[i++] = std * (r * sin(a));
+    }
+  }
 }
+
+#define SYNTH_CHUNK 4096
 
 void synth_normal_f64(uint64_t seed, uint32_t tid, uint64_t offset, int64_t n,
                       double std, double *out) {
   uint64_t base = stream_base(seed, tid);
+  const int64_t nc = (n + SYNTH_CHUNK - 1) / SYNTH_CHUNK;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) out[i] = std * normal_at(base, offset + (uint64_t)i);
+  for (int64_t c = 0; c < nc; ++c) {
+    const int64_t i0 = c * SYNTH_CHUNK, len = n - i0 < SYNTH_CHUNK ? n - i0 : SYNTH_CHUNK;
+    normals_range(base, offset + (uint64_t)i0, len, std, out + i0);
+  }
 }
 
 void synth_normal_f32(uint64_t seed, uint32_t tid, uint64_t offset, int64_t n,
                       double std, float *out) {
   uint64_t base = stream_base(seed, tid);
+  const int64_t nc = (n + SYNTH_CHUNK - 1) / SYNTH_CHUNK;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) out[i] = (float)(std * normal_at(base, offset + (uint64_t)i));
+  for (int64_t c = 0; c < nc; ++c) {
+    double buf[SYNTH_CHUNK];
+    const int64_t i0 = c * SYNTH_CHUNK, len = n - i0 < SYNTH_CHUNK ? n - i0 : SYNTH_CHUNK;
+    normals_range(base, offset + (uint64_t)i0, len, std, buf);
+    for (int64_t i = 0; i < len; ++i) out[i0 + i] = (float)buf[i];
+  }
 }
 
 /* fp64 -> bf16 bits, round to nearest even, for finite inputs. */
@@ -90,9 +113,14 @@ uint16_t synth_f64_to_bf16(double v) { return f64_to_bf16_rne(v); }
 void synth_normal_bf16(uint64_t seed, uint32_t tid, uint64_t offset, int64_t n,
                        double std, uint16_t *out) {
   uint64_t base = stream_base(seed, tid);
+  const int64_t nc = (n + SYNTH_CHUNK - 1) / SYNTH_CHUNK;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i)
-    out[i] = f64_to_bf16_rne(std * normal_at(base, offset + (uint64_t)i));
+  for (int64_t c = 0; c < nc; ++c) {
+    double buf[SYNTH_CHUNK];
+    const int64_t i0 = c * SYNTH_CHUNK, len = n - i0 < SYNTH_CHUNK ? n - i0 : SYNTH_CHUNK;
+    normals_range(base, offset + (uint64_t)i0, len, std, buf);
+    for (int64_t i = 0; i < len; ++i) out[i0 + i] = f64_to_bf16_rne(buf[i]);
+  }
 }
 
 /* |a| (a >= 0, finite) -> E4M3 magnitude code (0..0x7E), RNE, saturating. */
@@ -118,24 +146,31 @@ uint8_t synth_f64_to_e4m3(double v) {
 }
 
 /* rows x cols normals (std) quantised per row to E4M3 with an fp32 scale. */
-void synth_normal_fp8_rows(uint64_t seed, uint32_t tid, uint64_t offset, int64_t rows,
+int synth_normal_fp8_rows(uint64_t seed, uint32_t tid, uint64_t offset, int64_t rows,
                            int64_t cols, double std, uint8_t *q, float *scale) {
   uint64_t base = stream_base(seed, tid);
-#pragma omp parallel for schedule(static)
-  for (int64_t r = 0; r < rows; ++r) {
-    double amax = 0.0;
-    uint64_t o = offset + (uint64_t)(r * cols);
-    for (int64_t c = 0; c < cols; ++c) {
-      double w = std * normal_at(base, o + (uint64_t)c);
-      if (fabs(w) > amax) amax = fabs(w);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *w = malloc(sizeof(double) * (size_t)(cols > 0 ? cols : 1));
+    if (!w) {
+#pragma omp atomic write
+      bad = 1;
     }
-    float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
-    scale[r] = s;
-    for (int64_t c = 0; c < cols; ++c) {
-      double w = std * normal_at(base, o + (uint64_t)c);
-      q[r * cols + c] = synth_f64_to_e4m3(w / (double)s);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (!w) continue;
+      normals_range(base, offset + (uint64_t)(r * cols), cols, std, w);
+      double amax = 0.0;
+      for (int64_t c = 0; c < cols; ++c)
+        if (fabs(w[c]) > amax) amax = fabs(w[c]);
+      float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+      scale[r] = s;
+      for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = synth_f64_to_e4m3(w[c] / (double)s);
     }
+    free(w);
   }
+  return bad ? -1 : 0;
 }
 
 /* Uniform integer in [0, n) from draw i (Lemire's multiply-shift; the tiny
