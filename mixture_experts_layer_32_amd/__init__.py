@@ -16,9 +16,7 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# LATENTMOE_LIB selects another build of the same library (e.g. a variant
-# compiled with different tile constants); default: the in-tree build.
-LIB_PATH = os.environ.get("LATENTMOE_LIB") or os.path.join(HERE, "liblatentmoe.so")
+LIB_PATH = os.path.join(HERE, "liblatentmoe.so")   # the in-tree build
 
 LMOE_F32, LMOE_BF16, LMOE_FP8_E4M3_ROWSCALE, LMOE_MXFP4_E2M1 = 0, 1, 2, 3
 ROUTER_ON_X, ROUTER_ON_LATENT = 0, 1
@@ -307,27 +305,23 @@ class LatentMoELayer:
         act = torch.float32 if s.act_dtype == "f32" else torch.bfloat16
         T = int(x.shape[0])
         xp = self._expect("x", x, (T, s.d), (act,))
-        if out is None:
-            out = torch.empty((T, s.d), dtype=act, device=x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        # tensors made here are allocated on the launch stream, so that the
+        # caching allocator does not hand their memory to other work on
+        # another stream while the call's kernels still use it
+        with torch.cuda.stream(stream):
+            if out is None:
+                out = torch.empty((T, s.d), dtype=act, device=x.device)
+            need = self.workspace_size(T)
+            if workspace is None:
+                workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
         op = self._expect("out", out, (T, s.d), (act,))
-        need = self.workspace_size(T)
-        if workspace is None:
-            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
         if workspace.numel() < need:
             raise ValueError("workspace has %d bytes, needs %d" % (workspace.numel(), need))
         cw = cweights if cweights is not None else self.weights_struct(weights)
-        dbg = LmoeDebug()
-        dbg_p = None
-        if debug or timer is not None:
-            for k, v in (debug or {}).items():
-                if not hasattr(dbg, k):
-                    raise ValueError("unknown debug output %r" % k)
-                setattr(dbg, k, v.data_ptr())
-            if timer is not None:
-                dbg.timer = timer._h
-            dbg_p = ctypes.byref(dbg)
-        if stream is None:
-            stream = torch.cuda.current_stream(x.device)
+        dbg = self._debug(debug, timer)
+        dbg_p = ctypes.byref(dbg) if dbg is not None else None
         st = ctypes.c_void_p(stream.cuda_stream)
         if overlap is not None:
             _check(lib().latentmoe_forward_overlap(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
@@ -337,6 +331,20 @@ class LatentMoELayer:
             _check(lib().latentmoe_forward(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
                                            workspace.data_ptr(), workspace.numel(), st))
         return out
+
+    @staticmethod
+    def _debug(debug, timer):
+        """lmoe_debug_out of the optional device outputs and timer, or None."""
+        if not debug and timer is None:
+            return None
+        dbg = LmoeDebug()
+        for k, v in (debug or {}).items():
+            if not hasattr(dbg, k):
+                raise ValueError("unknown debug output %r" % k)
+            setattr(dbg, k, v.data_ptr())
+        if timer is not None:
+            dbg.timer = timer._h
+        return dbg
 
 
 def debug_buffers(spec, T: int, device="cuda") -> dict:

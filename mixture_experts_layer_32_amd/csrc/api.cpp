@@ -295,7 +295,7 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.tiles = take(size_t(c.n_experts + 1) * 4);
   p.slot = take(size_t(p.copies) * 4);
   p.token = take(size_t(p.copies) * 4);
-  p.H = take(size_t(p.copies) * c.m * ab);
+  p.H = take(p.fused ? 0 : size_t(p.copies) * c.m * ab);  // the fused kernel keeps H on chip
   p.Y = take(size_t(p.copies) * c.l * ab);
   p.v = take(c.has_projections ? size_t(T) * c.l * ab : 0);
   p.partial = take(partial);
