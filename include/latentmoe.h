@@ -226,6 +226,26 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle *h, const lmoe_weights *
                                       void *workspace, size_t workspace_bytes, void *stream,
                                       lmoe_overlap *ov);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * latentmoe_forward with the workspace taken from a scratch array the
+ * library holds in device memory, LMOE_STATIC_SCRATCH_BYTES per device (each
+ * GPU the library runs on holds its copy until the process ends).  The call
+ * allocates nothing; the caller still passes x, out and the weights.  The
+ * shared experts run on `stream` (no side stream).  `stream` must belong to
+ * the current device (NULL = its null stream).  Returns LMOE_ERR_WORKSPACE,
+ * enqueuing nothing, when latentmoe_workspace_size(T) exceeds
+ * LMOE_STATIC_SCRATCH_BYTES (64 MiB: the decode layers up to T = 512 fit,
+ * e.g. d 4096, l 1024, m 1536, N 512, K 32; the prefill batches do not).
+ * Every call on one device shares that device's scratch and leaves the last
+ * call's contents in it (nothing in it needs to start at zero): calls that
+ * overlap on one device -- on two streams, or from two threads without
+ * stream order -- race on it and give undefined results. */
+#define LMOE_STATIC_SCRATCH_BYTES (64u << 20)
+lmoe_status latentmoe_forward_static(const lmoe_handle *h, const lmoe_weights *w, const void *x,
+                                     int64_t T, void *out, const lmoe_debug_out *dbg,
+                                     void *stream);
+
 lmoe_status latentmoe_destroy(lmoe_handle *h);
 
 /* Stage timer: create/destroy, and read the accumulated milliseconds per

@@ -39,7 +39,7 @@ EXPORTED = ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
             "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
             "latentmoe_timer_destroy", "latentmoe_status_string", "latentmoe_last_error",
             "latentmoe_expert_regime", "latentmoe_overlap_create", "latentmoe_overlap_destroy",
-            "latentmoe_forward_overlap")
+            "latentmoe_forward_overlap", "latentmoe_forward_static")
 
 
 class LmoeConfig(ctypes.Structure):
@@ -102,6 +102,8 @@ def lib():
             L.latentmoe_forward_overlap.argtypes = [vp, ctypes.POINTER(LmoeWeights), vp, i64, vp,
                                                     ctypes.POINTER(LmoeDebug), vp,
                                                     ctypes.c_size_t, vp, vp]
+            L.latentmoe_forward_static.argtypes = [vp, ctypes.POINTER(LmoeWeights), vp, i64, vp,
+                                                   ctypes.POINTER(LmoeDebug), vp]
             L.latentmoe_overlap_create.argtypes = [vp, ctypes.POINTER(vp)]
             L.latentmoe_overlap_destroy.argtypes = [vp]
             L.latentmoe_destroy.argtypes = [vp]
@@ -118,6 +120,7 @@ def lib():
             for f in ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
                       "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
                       "latentmoe_timer_destroy", "latentmoe_forward_overlap",
+                      "latentmoe_forward_static",
                       "latentmoe_overlap_create", "latentmoe_overlap_destroy"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -345,6 +348,27 @@ class LatentMoELayer:
         if timer is not None:
             dbg.timer = timer._h
         return dbg
+
+    def forward_static(self, x, weights, out, debug: dict | None = None,
+                       timer: StageTimer | None = None, stream=None,
+                       cweights: LmoeWeights | None = None):
+        """latentmoe_forward_static: the layer with the library's own device
+        scratch as workspace (no allocation in the call).  `out` is required
+        (T x d, act dtype); the shared experts run on the launch stream."""
+        torch = _torch()
+        s = self.spec
+        act = torch.float32 if s.act_dtype == "f32" else torch.bfloat16
+        T = int(x.shape[0])
+        xp = self._expect("x", x, (T, s.d), (act,))
+        op = self._expect("out", out, (T, s.d), (act,))
+        cw = cweights if cweights is not None else self.weights_struct(weights)
+        dbg = self._debug(debug, timer)
+        dbg_p = ctypes.byref(dbg) if dbg is not None else None
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        _check(lib().latentmoe_forward_static(self._h, ctypes.byref(cw), xp, T, op, dbg_p,
+                                              ctypes.c_void_p(stream.cuda_stream)))
+        return out
 
 
 def debug_buffers(spec, T: int, device="cuda") -> dict:

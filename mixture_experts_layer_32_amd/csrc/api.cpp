@@ -22,6 +22,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -95,6 +96,17 @@ constexpr double kFusedMaxRowsPerExpert = 36.0;
 constexpr double kSparseMaxRowsPerExpert = LMOE_SPARSE_MAX_ROWS;
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Scratch of latentmoe_forward_static, for callers that cannot allocate:
+// one copy per device (each GPU the library runs on holds it until the
+// process ends).  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[LMOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 lmoe::Dt act_dt(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? lmoe::Dt::F32 : lmoe::Dt::BF16; }
 lmoe::Dt exp_dt(const lmoe_config& c) {
@@ -776,6 +788,54 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
 #undef LMOE_END
 #undef LMOE_TRY
   return LMOE_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+lmoe_status latentmoe_forward_static(const lmoe_handle* h, const lmoe_weights* w, const void* x,
+                                     int64_t T, void* out, const lmoe_debug_out* dbg,
+                                     void* stream) {
+  if (!h || !w) return fail(LMOE_ERR_INVALID_ARG, "forward_static: NULL handle or weights");
+  if (T < 0) return fail(LMOE_ERR_INVALID_ARG, "forward_static: T < 0");
+  if (T == 0) return LMOE_OK;
+  if (T * h->cfg.top_k > kMaxCopies)
+    return fail(LMOE_ERR_UNSUPPORTED, "forward_static: T*K too large");
+  const size_t need = make_plan(h->cfg, T).total;
+  if (need > size_t(LMOE_STATIC_SCRATCH_BYTES))
+    return fail(LMOE_ERR_WORKSPACE,
+                "forward_static: %lld tokens need %zu bytes of scratch, more than the %zu the "
+                "library holds per device; use latentmoe_forward with a workspace",
+                (long long)T, need, size_t(LMOE_STATIC_SCRATCH_BYTES));
+  // the device of the call: the stream's, which must be the current one
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "forward_static: hipGetDevice");
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return hip_fail(e, "forward_static: hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(LMOE_ERR_INVALID_ARG, "forward_static: the stream belongs to device %d, "
+                  "the current device is %d", sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LMOE_ERR_UNSUPPORTED, "forward_static: device %d beyond %d", dev, kMaxDevices);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "forward_static: hipGetSymbolAddress(scratch)");
+      if (!p) return fail(LMOE_ERR_HIP, "forward_static: no device address for the scratch");
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return latentmoe_forward_overlap(h, w, x, T, out, dbg, ws, size_t(LMOE_STATIC_SCRATCH_BYTES),
+                                   stream, nullptr);
 }
 
 }  // extern "C"

@@ -205,3 +205,25 @@ def test_workspace_size_for_zero_and_one_token():
         lay = pkg.LatentMoELayer(__import__("synth").workload(name).spec)
         assert lay.workspace_size(0) >= 0
         assert lay.workspace_size(1) > 0
+
+
+def test_forward_static_limits_need_no_gpu():
+    """The allocation-free entry point refuses, before any HIP call, a batch
+    whose workspace exceeds the library's static scratch, and accepts T == 0;
+    the decode layers at T = 512 fit the scratch."""
+    lib = pkg.lib()
+    limit = 64 << 20
+    st, h = _create(pkg.make_config(workload("latent_prefill_zipf").spec))
+    assert st == 0
+    w = pkg.LmoeWeights()
+    w.w_router = w.w1 = w.w2 = w.w_down = w.w_up = 4096
+    assert lib.latentmoe_forward_static(h, ctypes.byref(w), None, 0, None, None, None) == 0
+    assert lib.latentmoe_forward_static(h, ctypes.byref(w), None, -1, None, None, None) == -1
+    assert lib.latentmoe_forward_static(None, ctypes.byref(w), None, 4, None, None, None) == -1
+    assert lib.latentmoe_forward_static(h, ctypes.byref(w), ctypes.c_void_p(4096), 16384,
+                                        ctypes.c_void_p(4096), None, None) == -3
+    assert b"scratch" in lib.latentmoe_last_error()
+    lib.latentmoe_destroy(h)
+    for name in ("std_decode", "latent_decode"):
+        lay = pkg.LatentMoELayer(workload(name).spec)
+        assert lay.workspace_size(512) <= limit, name
