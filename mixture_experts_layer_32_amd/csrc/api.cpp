@@ -193,6 +193,7 @@ struct Plan {
   bool stream = true;   // expert GEMMs: weight-streaming kernel
   bool sparse = false;  // streaming kernel over the list of experts with copies only
   bool fused = false;   // FC1 + FC2 in the fused weight-streaming kernel
+  bool grouped = false; // expert GEMMs in the persistent grouped kernel (prefill)
   int mb_max = 4;       // streaming kernel rows per pass / 16
   int expert_tile = 0;  // tiled kernel tile config
   int tile_m = 128;
@@ -241,6 +242,15 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.expert_tile = c.act_dtype == LMOE_BF16 ? (mean >= LMOE_EXPERT_TILE_BIG_ROWS ? 2 : LMOE_EXPERT_TILE)
                                            : 1;  // fp32: the 64 x 64 tile
   p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
+  {
+    // many rows per expert, bf16: the persistent grouped kernel (mixed tile
+    // heights, so skewed loads pad little) for both expert GEMMs
+    const int n1 = static_cast<int>(c.activation == LMOE_ACT_SWIGLU ? 2 * c.m : c.m);
+    p.grouped = !p.stream && bf16 && mean >= LMOE_EXPERT_TILE_BIG_ROWS &&
+                lmoe::gemm_grouped_fits(n1, static_cast<int>(c.l), static_cast<int>(c.n_experts)) &&
+                lmoe::gemm_grouped_fits(static_cast<int>(c.l), static_cast<int>(c.m),
+                                        static_cast<int>(c.n_experts));
+  }
   const size_t ab = act_bytes(c);
   const int64_t r_in = c.router_input == LMOE_ROUTER_ON_LATENT ? c.l : c.d;
   size_t partial = 0;
@@ -724,6 +734,7 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.act = act1;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC1 (tiled, fp8)");
+    else if (p.grouped) LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC1 (grouped)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");
   }
   LMOE_MARK(4);
@@ -744,6 +755,7 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.act = lmoe::kActNone;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC2 (stream)");
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC2 (tiled, fp8)");
+    else if (p.grouped) LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC2 (grouped)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");
   }
   LMOE_MARK(5);

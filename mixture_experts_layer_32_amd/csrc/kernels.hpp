@@ -67,6 +67,13 @@ int tiled_block_m(int tile);
 hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s);
 int tiled_block_m_fp8w();
 
+// Grouped GEMM for experts with many rows (prefill), bf16 operands and
+// output: a persistent grid walks (expert, row tile, 256-column tile) items;
+// an expert's last row tile is 256, 128 or 64 rows high.  Needs N a multiple
+// of 256, K of 32, at most 2048 groups; g_tiles is not read.
+bool gemm_grouped_fits(int N, int K, int G);
+hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);
+
 // Compute units of the current device (queried once per device; 256 on
 // MI355X), for persistent grids.
 int device_compute_units();

@@ -38,6 +38,7 @@ ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide what the expert kernels read and write
 KERNEL_SOURCES = ("csrc/gemm_stream.hip", "csrc/ffn_stream.hip", "csrc/gemm_tiled.hip",
+                  "csrc/gemm_grouped.hip", "csrc/routing.hip",
                   "csrc/common.hpp", "csrc/kernels.hpp", "csrc/api.cpp")
 COPY_BYTES = 1 << 30  # bench.py --copy-calibration: 1 GiB read + 1 GiB written per launch
 

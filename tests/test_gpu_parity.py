@@ -275,7 +275,40 @@ def test_crafted_ties_go_to_the_lower_expert_id(N, K, gating):
     check_against_oracle(spec, w, x, g)
 
 
-# Sizes that select the large GEMM tiles (256 x 256 dense, 128 x 256 grouped,
+# The persistent grouped kernel (experts with 256 rows or more on average):
+# skewed loads give every tile height (256, 128, 64 rows), experts with no
+# rows and experts of many full tiles in one launch; SwiGLU, the standard
+# MoE and a single expert.
+GROUPED = {
+    "grouped_zipf": (LayerSpec(d=512, l=256, m=512, n_experts=8, top_k=2, gating="softmax_all",
+                               has_router_bias=True), 1500),
+    "grouped_swiglu": (LayerSpec(d=256, l=256, m=256, n_experts=4, top_k=2, gating="softmax_topk",
+                                 activation="swiglu"), 700),
+    "grouped_std_moe": (LayerSpec(d=512, l=512, m=256, n_experts=4, top_k=1, gating="softmax_all",
+                                  has_projections=False), 1200),
+    "grouped_one_expert": (LayerSpec(d=256, l=256, m=512, n_experts=1, top_k=1), 300),
+    "grouped_many_experts_zipf": (LayerSpec(d=256, l=256, m=256, n_experts=64, top_k=8,
+                                            gating="softmax_all", has_router_bias=True), 2100),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUPED))
+def test_grouped_kernel_matches_oracle(name):
+    import mixture_experts_layer_32_amd as pkg
+    spec, T = GROUPED[name]
+    layer = pkg.LatentMoELayer(spec)
+    assert layer.expert_regime(T) == "tiled"
+    w, x = _case(spec, T, seed=4)
+    g, _ = run_gpu(spec, w, x, layer=layer)
+    counts = g["expert_counts"]
+    print(name, "rows per expert", counts.tolist(), flush=True)
+    check_routing_structure(spec, g, T)
+    tok = None if T * spec.top_k * spec.m * spec.l <= 2e9 else _sample_tokens(T, n=200, seed=7)
+    st = check_against_oracle(spec, w, x, g, tokens=tok)
+    print(name, st, flush=True)
+
+
+# Sizes that select (256 x 256 dense, 128 x 256 grouped,
 # 128 x 128 dense) with ragged row and column tails, on sampled tokens.
 MID = {
     "ragged_large_tiles": (LayerSpec(d=2064, l=1040, m=528, n_experts=64, top_k=4,
