@@ -66,7 +66,8 @@ typedef enum {
   LMOE_FP8_E4M3_ROWSCALE = 2, /* OCP E4M3 bytes + one fp32 scale per matrix row: w = q * s */
   LMOE_MXFP4_E2M1 = 3         /* OCP MX FP4: E2M1 elements, two per byte (element 2j in the low
                                  nibble of byte j), + one E8M0 scale byte 2^(e-127) per 32
-                                 consecutive elements of a row; expert weights only, bf16
+                                 consecutive elements of a row (byte 0 is 2^-127, byte 0xFF
+                                 is NaN and makes the block NaN); expert weights only, bf16
                                  activations, l and m multiples of 32, streaming or fused
                                  kernel */
 } lmoe_dtype;

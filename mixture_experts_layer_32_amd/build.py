@@ -26,17 +26,14 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD,
-          defines: tuple = ()) -> str:
-    """Compile every source (always) and link liblatentmoe.so (or `out`).
-
-    defines: extra -D flags for variant builds (tile constants)."""
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source (always) and link liblatentmoe.so (or `out`)."""
     os.makedirs(build_dir, exist_ok=True)
     hipcc = _hipcc()
 
     def compile_one(src):
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc] + FLAGS + ["-D" + d for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -75,25 +75,17 @@ constexpr int64_t kMaxCopies = int64_t(1) << 30;  // T * K (int32 row indices)
 constexpr double kStreamMaxRowsPerExpert = 40.0;
 // fp8 weights: the tiled kernel (one weight tile per expert and 256 columns,
 // token rows staged once per tile) from this many rows per expert on
-#ifndef LMOE_FP8_STREAM_MAX_ROWS
-#define LMOE_FP8_STREAM_MAX_ROWS 40.0
-#endif
-constexpr double kFp8StreamMaxRowsPerExpert = LMOE_FP8_STREAM_MAX_ROWS;
+constexpr double kFp8StreamMaxRowsPerExpert = 40.0;
 // streaming kernel: passes of 64 rows (4 MFMA row blocks, 128 columns per
 // unit) up to this mean row count per expert, of 128 rows (64 columns) above
-#ifndef LMOE_STREAM_MB4_MAX_ROWS
-#define LMOE_STREAM_MB4_MAX_ROWS 40.0
-#endif
+constexpr double kStreamMb4MaxRowsPerExpert = 40.0;
 // fused expert FFN (bf16): up to this many copies per expert on average, so
 // that few experts exceed the kernel's 48-row pass
 constexpr double kFusedMaxRowsPerExpert = 36.0;
 // below this mean row count per expert the streaming kernel works from the
 // list of experts with copies (empty experts would otherwise cost a unit
 // each: measured 1.7 TB/s at 0.2 rows per expert, 1024 experts)
-#ifndef LMOE_SPARSE_MAX_ROWS
-#define LMOE_SPARSE_MAX_ROWS 2.0
-#endif
-constexpr double kSparseMaxRowsPerExpert = LMOE_SPARSE_MAX_ROWS;
+constexpr double kSparseMaxRowsPerExpert = 2.0;
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -168,24 +160,18 @@ DensePlan plan_dense_128(int64_t M, int64_t N, int64_t K, size_t elem_bytes, int
   return d;
 }
 
-// Shared-expert GEMMs: 0 = plan_dense, 1 / 2 = 128 x 128 tiles split to 1 / 2
-// workgroups per compute unit
-#ifndef LMOE_SHARED_PLAN
-#define LMOE_SHARED_PLAN 1
-#endif
+// Shared-expert GEMMs: 128 x 128 tiles, one workgroup per compute unit
+// (plan_dense_128's mode 1)
+constexpr int kSharedPlan = 1;
 
 // Tile of the grouped expert GEMMs when experts receive many tokens: 128 rows
 // keeps the padding of each expert's last tile small, 256 columns halve the
 // operand bytes per flop against 128 x 128.
-#ifndef LMOE_EXPERT_TILE
-#define LMOE_EXPERT_TILE 3
-#endif
-// experts with many rows (prefill): the 256 x 256 tile of eight waves from
-// this mean row count per expert on (measured at 704 rows per expert: 4.33
-// against 4.44 ms per layer call; at 48 rows its padding would waste work)
-#ifndef LMOE_EXPERT_TILE_BIG_ROWS
-#define LMOE_EXPERT_TILE_BIG_ROWS 256.0
-#endif
+constexpr int kExpertTile = 3;
+// experts with many rows (prefill): 256 x 256 tiles (the persistent grouped
+// kernel for bf16 layers) from this mean row count per expert on (at 48 rows
+// their padding would waste work)
+constexpr double kBigTileRowsPerExpert = 256.0;
 
 struct Plan {
   int64_t T = 0, copies = 0;
@@ -235,18 +221,18 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
                 c.n_experts >= kComputeUnits;
   }
   if (fp4 && !p.stream) p.stream = true;  // MXFP4 weights: no tiled kernel
-  p.mb_max = mean <= LMOE_STREAM_MB4_MAX_ROWS ? 4 : 8;
+  p.mb_max = mean <= kStreamMb4MaxRowsPerExpert ? 4 : 8;
   // most experts empty (expected share e^-mean > 1/8): the streaming kernel
   // visits only the experts with copies, listed by the dispatch stage
   p.sparse = p.stream && !p.fused && mean < kSparseMaxRowsPerExpert;
-  p.expert_tile = c.act_dtype == LMOE_BF16 ? (mean >= LMOE_EXPERT_TILE_BIG_ROWS ? 2 : LMOE_EXPERT_TILE)
+  p.expert_tile = c.act_dtype == LMOE_BF16 ? (mean >= kBigTileRowsPerExpert ? 2 : kExpertTile)
                                            : 1;  // fp32: the 64 x 64 tile
   p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
   {
     // many rows per expert, bf16: the persistent grouped kernel (mixed tile
     // heights, so skewed loads pad little) for both expert GEMMs
     const int n1 = static_cast<int>(c.activation == LMOE_ACT_SWIGLU ? 2 * c.m : c.m);
-    p.grouped = !p.stream && bf16 && mean >= LMOE_EXPERT_TILE_BIG_ROWS &&
+    p.grouped = !p.stream && bf16 && mean >= kBigTileRowsPerExpert &&
                 lmoe::gemm_grouped_fits(n1, static_cast<int>(c.l), static_cast<int>(c.n_experts)) &&
                 lmoe::gemm_grouped_fits(static_cast<int>(c.l), static_cast<int>(c.m),
                                         static_cast<int>(c.n_experts));
@@ -292,12 +278,12 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   // SwiGLU: the shared FC1 computes 2 * hs columns (up, gate pairs)
   const int64_t hs1 = c.activation == LMOE_ACT_SWIGLU ? 2 * hs : hs;
   if (hs > 0) {
-    if (LMOE_SHARED_PLAN == 0 || ab != 2) {
+    if (ab != 2) {
       p.sh1 = plan_dense(T, hs1, c.d, ab, ab == 2);
       p.sh2 = plan_dense(T, c.d, hs, ab, false);
     } else {
-      p.sh1 = plan_dense_128(T, hs1, c.d, ab, LMOE_SHARED_PLAN);
-      p.sh2 = plan_dense_128(T, c.d, hs, ab, LMOE_SHARED_PLAN);
+      p.sh1 = plan_dense_128(T, hs1, c.d, ab, kSharedPlan);
+      p.sh2 = plan_dense_128(T, c.d, hs, ab, kSharedPlan);
       const int64_t t256 = ((T + 255) / 256) * ((hs1 + 255) / 256);
       if (t256 >= kComputeUnits) p.sh1 = plan_dense(T, hs1, c.d, ab, true);
     }

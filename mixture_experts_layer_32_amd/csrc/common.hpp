@@ -129,9 +129,12 @@ struct fp4x2_t {
   uint8_t v;
 };
 
-// E8M0 scale byte -> fp32 2^(e - 127) (e = 0, the one subnormal scale, reads
-// as 0; the generator never writes it for a block holding a non-zero value)
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+// E8M0 scale byte -> fp32 2^(e - 127) as the OCP MX format defines it: e = 0
+// is the subnormal 2^-127 (fp32 bits 0x00400000) and e = 0xFF is NaN
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  const uint32_t b = e == 0u ? 0x00400000u : (e == 0xFFu ? 0x7fc00000u : e << 23);
+  return __uint_as_float(b);
+}
 
 // Eight E2M1 elements (one dword) times the block scale -> eight bf16 (one
 // 16-byte MFMA operand), with the gfx950 scaled conversion

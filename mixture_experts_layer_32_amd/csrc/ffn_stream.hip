@@ -49,22 +49,16 @@
 namespace lmoe {
 namespace {
 
-#ifndef LMOE_FFN_NWB
-#define LMOE_FFN_NWB 4
-#endif
-#ifndef LMOE_FFN_WD
-#define LMOE_FFN_WD 3
-#endif
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMB = 3;                         // 16-row blocks of token rows per pass
 constexpr int kRows = 16 * kMB;                // token rows per pass
-constexpr int kNWB = LMOE_FFN_NWB;             // 16-row weight blocks per wave
+constexpr int kNWB = 4;             // 16-row weight blocks per wave
 constexpr int kTileN = kWaves * kNWB * 16;     // output columns per tile
 constexpr int kKE = 64;                        // reduction elements per stage
 constexpr int kNS = kKE / 32;                  // MFMA k-steps per stage
 constexpr int kNLD = kNS;                      // 16-byte weight loads per n-block per stage
-constexpr int kWD = LMOE_FFN_WD;               // weight stages in flight ahead
+constexpr int kWD = 3;               // weight stages in flight ahead
 // registers rotate: weights modulo kWD + 1 stages, staged token rows modulo 2
 constexpr int kP = (kWD + 1) % 2 == 0 ? kWD + 1 : 2 * (kWD + 1);
 constexpr int kMaxM = 1536;                    // hidden width that fits in LDS

@@ -77,21 +77,8 @@ template <> struct StreamTraits<float, float> {        // fp32 tokens and weight
   __device__ __forceinline__ static int elem_of(int s, int q) { return 16 * s + 4 * q; }
 };
 
-#ifndef LMOE_W_CPOL
-#define LMOE_W_CPOL kCpolDefault
-#endif
 
 constexpr int kStageChunks = 16;  // 16-byte chunks of A per row per K stage (256 bytes)
-
-// K stages of weights requested ahead of the one being multiplied.  An fp8
-// stage is half the bytes of a bf16 one and its registers a quarter (one
-// n-block), so fp8 looks further ahead.
-#ifndef LMOE_W_DEPTH
-#define LMOE_W_DEPTH 1
-#endif
-#ifndef LMOE_W_DEPTH_FP8
-#define LMOE_W_DEPTH_FP8 3
-#endif
 
 // Stage geometry of one (token type, weight type) pair.
 template <typename TA, typename TW>
@@ -106,7 +93,10 @@ struct StreamShape {
   static constexpr int NLD = FP8 ? NS / 2 : FP4 ? NS / 4 : NS;
   static constexpr uint32_t W_STAGE_BYTES = FP4 ? KE / 2 : KE * sizeof(TW);
   static constexpr uint32_t A_STAGE_BYTES = KE * sizeof(TA);
-  static constexpr int WD = (FP8 || FP4) ? LMOE_W_DEPTH_FP8 : LMOE_W_DEPTH;
+  // K stages of weights requested ahead of the one being multiplied.  An fp8
+  // stage is half the bytes of a bf16 one and its registers a quarter (one
+  // n-block), so fp8 (and fp4) look further ahead.
+  static constexpr int WD = (FP8 || FP4) ? 3 : 1;
   // Register sets rotate: weights modulo WD + 1 stages, token rows modulo 2.
   // Units are padded to a multiple of this period, so every unit starts at
   // rotation phase 0 and the rotation stays in compile-time indices.
@@ -148,10 +138,7 @@ struct Unit {
   }
 };
 
-#ifndef LMOE_STREAM_OCC
-#define LMOE_STREAM_OCC 2
-#endif
-constexpr int kStreamOcc = LMOE_STREAM_OCC;  // resident workgroups per compute unit
+constexpr int kStreamOcc = 2;  // resident workgroups per compute unit
 
 // MB_MAX m-blocks of 16 rows per pass, NWB n-blocks of 16 weight rows per
 // wave, 4 waves.
@@ -265,7 +252,7 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
       const uint32_t vo = live ? u.w_off[nb] + so : kOutOfRange;
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
-        br[nb][j] = buffer_load_chunk<LMOE_W_CPOL>(u.w_rsrc, vo + 64u * j, 0u);
+        br[nb][j] = buffer_load_chunk<kCpolDefault>(u.w_rsrc, vo + 64u * j, 0u);
       if constexpr (S::FP4)
         bs[nb] = buffer_load_byte(u.s_rsrc, live ? u.s_off[nb] + 4u * s : kOutOfRange);
     }
@@ -432,30 +419,12 @@ __global__ __launch_bounds__(256, kStreamOcc) void gemm_stream_kernel(GemmArgs p
   }
 }
 
-// n-blocks of 16 weight rows per wave: two with up to 64 rows per pass, one
-// with 128 (the accumulators of the larger pass then leave room for two
-// workgroups per compute unit)
-#ifndef LMOE_STREAM_NWB
-#define LMOE_STREAM_NWB 2
-#endif
-#ifndef LMOE_STREAM_NWB_MB8
-#define LMOE_STREAM_NWB_MB8 1
-#endif
-
-// MXFP4 weights: a stage is half the bytes of an fp8 one and one register
-// chunk per n-block, so units can be wider against the staged token rows
-#ifndef LMOE_STREAM_NWB_FP4
-#define LMOE_STREAM_NWB_FP4 2
-#endif
-#ifndef LMOE_STREAM_NWB_FP4_MB8
-#define LMOE_STREAM_NWB_FP4_MB8 1
-#endif
-
 template <typename Mma, typename TA, typename TW, typename TOut, int MB>
 hipError_t launch_s(const GemmArgs& a, hipStream_t s) {
-  constexpr bool fp4 = std::is_same_v<TW, fp4x2_t>;
-  constexpr int NWB = fp4 ? (MB >= 8 ? LMOE_STREAM_NWB_FP4_MB8 : LMOE_STREAM_NWB_FP4)
-                          : (MB >= 8 ? LMOE_STREAM_NWB_MB8 : LMOE_STREAM_NWB);
+  // n-blocks of 16 weight rows per wave: two with up to 64 rows per pass,
+  // one with 128 (the accumulators of the larger pass then leave room for
+  // two workgroups per compute unit); the same for every weight type
+  constexpr int NWB = MB >= 8 ? 1 : 2;
   constexpr int NT = 4 * NWB * 16;
   if (a.g_off == nullptr || a.G < 1 || (a.g_active && !a.g_tiles)) return hipErrorInvalidValue;
   const int64_t n_tiles = (a.N + NT - 1) / NT;

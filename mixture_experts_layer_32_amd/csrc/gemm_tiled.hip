@@ -53,28 +53,10 @@ struct TileCfg {
   static constexpr int NSTAGE = NSTAGE_;
 };
 // tile configurations (index = the `tile` argument of launch_gemm_tiled)
-#ifndef LMOE_T0_BKC
-#define LMOE_T0_BKC 8
-#endif
-#ifndef LMOE_T0_STAGES
-#define LMOE_T0_STAGES 2
-#endif
-#ifndef LMOE_T0_OCC
-#define LMOE_T0_OCC 2
-#endif
-#ifndef LMOE_T3_STAGES
-#define LMOE_T3_STAGES 3
-#endif
-#ifndef LMOE_T3_BKC
-#define LMOE_T3_BKC 4
-#endif
-#ifndef LMOE_T3_OCC
-#define LMOE_T3_OCC 2
-#endif
-using Tile128 = TileCfg<128, 128, 2, 2, LMOE_T0_BKC, LMOE_T0_STAGES, LMOE_T0_OCC>;  // 0: 4 waves of 64x64
+using Tile128 = TileCfg<128, 128, 2, 2, 8, 2, 2>;  // 0: 4 waves of 64x64
 using Tile64 = TileCfg<64, 64, 2, 2, 8, 4>;                 // 1: 4 waves of 32x32
 using Tile256 = TileCfg<256, 256, 2, 4, 4, 4>;              // 2: 8 waves of 128x64 (bf16 output only)
-using Tile128x256 = TileCfg<128, 256, 2, 2, LMOE_T3_BKC, LMOE_T3_STAGES, LMOE_T3_OCC>;  // 3: 4 waves of 64x128
+using Tile128x256 = TileCfg<128, 256, 2, 2, 4, 3, 2>;  // 3: 4 waves of 64x128
 
 template <int BKC>
 __device__ __forceinline__ int lds_swz(int r) {
@@ -543,22 +525,7 @@ hipError_t launch_tile(const GemmArgs& a, Dt a_dt, Dt out_dt, int splits, float*
 // each weight tile is read once; 4 waves side by side along N (96 x 64 each);
 // stage rows of 64 bf16 (A) / 64 fp8 (B); two stages and two workgroups per
 // compute unit.
-#ifndef LMOE_F8_BN
-#define LMOE_F8_BN 256
-#endif
-#ifndef LMOE_F8_STAGES
-#define LMOE_F8_STAGES 2
-#endif
-#ifndef LMOE_F8_OCC
-#define LMOE_F8_OCC 2
-#endif
-#ifndef LMOE_F8_BM
-#define LMOE_F8_BM 96
-#endif
-#ifndef LMOE_F8_WGM
-#define LMOE_F8_WGM 1
-#endif
-using TileFp8 = TileCfg<LMOE_F8_BM, LMOE_F8_BN, LMOE_F8_WGM, 4 / LMOE_F8_WGM, 8, LMOE_F8_STAGES, LMOE_F8_OCC>;
+using TileFp8 = TileCfg<96, 256, 1, 4, 8, 2, 2>;
 
 }  // namespace
 

@@ -58,6 +58,23 @@ def test_mxfp4_case_matches_oracle(name):
     print(name, st, flush=True)
 
 
+def test_mxfp4_scale_byte_zero_matches_oracle():
+    """E8M0 byte 0 is the subnormal scale 2^-127 (OCP MX): blocks whose scale
+    byte is 0, in both expert matrices, decode as in the oracle (their
+    elements contribute about 1e-38) and leave the rest of the layer exact."""
+    spec, T = CASES["mb4"]
+    w, x = _case(spec, T, seed=11)
+    for k in ("w1_mx", "w2_mx"):
+        sc = w[k].copy()
+        sc[:, ::3, 0] = 0          # every third row's first block, every expert
+        sc[1::5, :, -1] = 0        # every row's last block of every fifth expert
+        w[k] = sc
+    g, _ = run_gpu(spec, w, x)
+    check_routing_structure(spec, g, T)
+    st = check_against_oracle(spec, w, x, g)
+    print("scale_byte_zero", st, flush=True)
+
+
 def test_mxfp4_equals_bf16_layer_with_decoded_weights():
     """The GPU's MXFP4 layer against its bf16 layer holding the decoded
     weights (exact in bf16): the same routing, outputs within bf16 rounding."""
