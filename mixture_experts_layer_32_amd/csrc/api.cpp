@@ -418,7 +418,7 @@ lmoe_status latentmoe_workspace_size(const lmoe_handle* h, int64_t T, size_t* by
 const char* latentmoe_expert_regime(const lmoe_handle* h, int64_t T) {
   if (!h || T < 0) return "invalid";
   const Plan p = make_plan(h->cfg, T);
-  return p.fused ? "fused" : p.stream ? "stream" : "tiled";
+  return p.fused ? "fused" : p.stream ? "stream" : p.grouped ? "grouped" : "tiled";
 }
 
 lmoe_status latentmoe_timer_create(lmoe_timer** out) {

@@ -65,14 +65,30 @@ __device__ __forceinline__ u32x4 buffer_load_chunk(BufRsrc r, uint32_t voff, uin
 }
 
 // One 16-byte chunk per lane straight from global memory into LDS: lane i of
-// the wave writes bytes [16 i, 16 i + 16) after `lds` (a wave-uniform
-// address); an out-of-range offset writes zeros.  The load counts in vmcnt
-// like any vector load, and nothing orders later LDS reads after it except
-// an explicit wait (wait_vmcnt_lgkm0) and, across waves, a barrier.
+// the wave writes bytes [16 i, 16 i + 16) after the wave-uniform LDS byte
+// address `lds`; an out-of-range offset writes zeros.  The load counts in
+// vmcnt like any vector load, and nothing orders later LDS reads after it
+// except an explicit wait (wait_vmcnt_lgkm0) and, across waves, a barrier.
+// Written as inline asm: the compiler's own form of this load makes it wait
+// for every LDS-mode load in flight before any later LDS read it cannot
+// prove disjoint, which collapses a ring of stage buffers to one stage.  The
+// memory clobber keeps the load in program order against LDS reads; M0
+// carries the LDS address (an operand: the compiler sets it).
+__device__ __forceinline__ void dma16_to_lds(BufRsrc r, uint32_t lds, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "{m0}"(lds)
+               : "memory");
+}
+
+// LDS byte address of a shared-memory pointer, as a wave-uniform value
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p)));
+}
+
 __device__ __forceinline__ void buffer_load_chunk_lds(BufRsrc r, u32x4* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)(lds), 16,
-      static_cast<int>(voff), 0, 0, 0);
+  dma16_to_lds(r, lds_addr(lds), voff);
 }
 
 // LDS-only barrier: this wave's LDS operations are complete and every wave

@@ -151,9 +151,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
       const int mid = (lo + hi + 1) >> 1;
       if (p.g_tiles[mid] <= mg) lo = mid; else hi = mid - 1;
     }
-    g = lo;
-    const int gs = p.g_off[g], ge = p.g_off[g + 1];
-    row0 = gs + (mg - p.g_tiles[g]) * BM;
+    // wave-uniform values (the buffer resources built from them must sit in
+    // scalar registers)
+    g = __builtin_amdgcn_readfirstlane(lo);
+    const int gs = __builtin_amdgcn_readfirstlane(p.g_off[g]);
+    const int ge = __builtin_amdgcn_readfirstlane(p.g_off[g + 1]);
+    row0 = gs + (mg - __builtin_amdgcn_readfirstlane(p.g_tiles[g])) * BM;
     rows = min(BM, ge - row0);
   }
   // K range of this split, in whole stages

@@ -58,11 +58,14 @@ def short_name(name: str) -> str:
 
 def expert_kernel_kind(name: str) -> str | None:
     """Which expert-FFN kernel a profiled kernel name is: "ffn_stream" (fused
-    FC1 + FC2), "gemm_stream" (weight streaming) or "gemm_tiled" (grouped
+    FC1 + FC2), "gemm_stream" (weight streaming), "gemm_grouped" (the
+    persistent 256 x 256 grouped kernel) or "gemm_tiled" (grouped
     LDS-tiled: the 128 x 256 tile, or fp8 weights), else None (dense GEMMs
     and routing kernels)."""
     if "ffn_stream_kernel" in name:
         return "ffn_stream"
+    if "gemm_grouped_kernel<" in name:
+        return "gemm_grouped"
     if "gemm_stream_kernel<" in name:
         return "gemm_stream"
     if "gemm_tiled_kernel<" in name and ("TileCfg<128, 256" in name or "unsigned char" in name
@@ -198,17 +201,18 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
         f.write("\n".join(lines) + "\n")
 
 
-REGIME_KERNEL = {"fused": "ffn_stream", "stream": "gemm_stream", "tiled": "gemm_tiled"}
+REGIME_KERNEL = {"fused": "ffn_stream", "stream": "gemm_stream", "tiled": "gemm_tiled",
+                 "grouped": "gemm_grouped"}
 
 
 def hbm_file(workload: str, kind: str) -> str:
-    """kind: "ffn_stream", "gemm_stream" or "gemm_tiled"."""
+    """kind: "ffn_stream", "gemm_stream", "gemm_tiled" or "gemm_grouped"."""
     return os.path.join(PROFILES, "%s_%s_hbm.txt" % (kind, workload))
 
 
 def read_hbm(workload: str, stage: str, regime: str):
     """HBM bytes per launch of the FC1/FC2 (or fused, stage "ffn") kernel of
-    the expert regime ("fused", "stream", "tiled") from the committed
+    the expert regime ("fused", "stream", "tiled", "grouped") from the committed
     summary, or None when there is none or the kernel sources changed since."""
     path = hbm_file(workload, REGIME_KERNEL[regime])
     if not os.path.exists(path):

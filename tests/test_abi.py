@@ -52,7 +52,7 @@ def test_regime_choice():
     assert lay.expert_regime(512) == "fused"     # 32 rows per expert, 512 experts, m 1536
     assert lay.expert_regime(640) == "stream"    # 40 rows per expert
     assert lay.expert_regime(1024) == "tiled"    # 64 rows per expert
-    assert lay.expert_regime(16384) == "tiled"
+    assert lay.expert_regime(16384) == "grouped"  # 1024 rows per expert: 256 x 256 tiles
     std = pkg.LatentMoELayer(workload("std_decode").spec)
     assert std.expert_regime(512) == "stream"    # 128 experts: fewer than compute units
     assert std.expert_regime(768) == "tiled"     # 48 rows per expert

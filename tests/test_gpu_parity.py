@@ -297,7 +297,7 @@ def test_grouped_kernel_matches_oracle(name):
     import mixture_experts_layer_32_amd as pkg
     spec, T = GROUPED[name]
     layer = pkg.LatentMoELayer(spec)
-    assert layer.expert_regime(T) == "tiled"
+    assert layer.expert_regime(T) == "grouped"
     w, x = _case(spec, T, seed=4)
     g, _ = run_gpu(spec, w, x, layer=layer)
     counts = g["expert_counts"]

@@ -48,6 +48,12 @@ NAMES = {
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 1, false>"
     "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc1"),
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<1, true>(lmoe::GemmArgs)":
+        ("gemm_grouped", "fc1"),
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<2, true>(lmoe::GemmArgs)":
+        ("gemm_grouped", "fc1"),
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<0, false>(lmoe::GemmArgs)":
+        ("gemm_grouped", "fc2"),
     # the same tile without activation is shared with the dense projections
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 0, false>"
