@@ -10,8 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblatentmoe.so")
-SOURCES = ["api.cpp", "gemm_tiled.hip", "gemm_grouped.hip", "gemm_stream.hip", "ffn_stream.hip",
-           "routing.hip"]
+SOURCES = ["api.cpp", "gemm_tiled.hip", "gemm_grouped.hip", "gemm_fp8w.hip", "gemm_stream.hip",
+           "ffn_stream.hip", "routing.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions stay off: hipcc must not form v_pk_{add,mul,fma}_f32.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall",

@@ -227,7 +227,7 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   p.sparse = p.stream && !p.fused && mean < kSparseMaxRowsPerExpert;
   p.expert_tile = c.act_dtype == LMOE_BF16 ? (mean >= kBigTileRowsPerExpert ? 2 : kExpertTile)
                                            : 1;  // fp32: the 64 x 64 tile
-  p.tile_m = fp8 ? lmoe::tiled_block_m_fp8w() : lmoe::tiled_block_m(p.expert_tile);
+  p.tile_m = fp8 ? lmoe::fp8w_block_m() : lmoe::tiled_block_m(p.expert_tile);
   {
     // many rows per expert, bf16: the persistent grouped kernel (mixed tile
     // heights, so skewed loads pad little) for both expert GEMMs
@@ -719,7 +719,7 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.g_active = active;
     a.act = act1;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
-    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC1 (tiled, fp8)");
+    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC1 (grouped, fp8)");
     else if (p.grouped) LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC1 (grouped)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");
   }
@@ -740,7 +740,7 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.g_active = active;
     a.act = lmoe::kActNone;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC2 (stream)");
-    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_tiled_fp8w(a, s), "FC2 (tiled, fp8)");
+    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC2 (grouped, fp8)");
     else if (p.grouped) LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC2 (grouped)");
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");
   }

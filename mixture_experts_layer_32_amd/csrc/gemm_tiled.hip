@@ -1,6 +1,6 @@
 // LDS-tiled MFMA GEMM, dense or grouped by expert, for gfx950.
 //
-// C[r][n] = act(scale[n] * sum_k A[arow(r)][k] * B[g][n][k])  (+ R[r][n], dense)
+// C[r][n] = act(sum_k A[arow(r)][k] * B[g][n][k])  (+ R[r][n], dense)
 //
 // Used for the two projections (W_down: u = x W_down^T, W_up: out = v W_up^T),
 // the router logits (fp32 output) and, when experts receive many tokens, the
@@ -33,7 +33,7 @@
 //
 // Dense problems with too few tiles to fill the device split K: every split
 // writes an fp32 partial tile and a reduction kernel adds the partials in a
-// fixed order (deterministic), then scales, activates and converts.
+// fixed order (deterministic), then activates and converts.
 #include <type_traits>
 
 #include "common.hpp"
@@ -91,19 +91,14 @@ __device__ __forceinline__ void store2<float>(float* p, float a, float b) {
   *reinterpret_cast<float2*>(p) = float2{a, b};
 }
 
-// TB: element type of B (TA, or uint8_t for OCP E4M3 weights with one fp32
-// scale per row of B, applied in the epilogue; fp8 fragments are widened to
-// bf16 right after their LDS read).
-template <typename Mma, typename TA, typename TB, typename TOut, typename Cfg, int ACT, bool SCALE>
+template <typename Mma, typename TA, typename TOut, typename Cfg, int ACT>
 __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs p, int splits, float* partial) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BKC = Cfg::BKC, NSTAGE = Cfg::NSTAGE;
   constexpr int EPC = 16 / sizeof(TA);       // A elements per 16-byte chunk
   constexpr int BKE = BKC * EPC;             // elements of K per stage
-  constexpr bool FP8B = sizeof(TB) == 1 && sizeof(TA) == 2;
-  constexpr int EPCB = 16 / sizeof(TB);      // B elements per chunk
-  constexpr int BKCB = BKE / EPCB;           // B chunks per row per stage
-  static_assert(sizeof(TB) == sizeof(TA) || FP8B, "B is the A type or fp8 with bf16 A");
-  static_assert(BKCB == 4 || BKCB == 8, "B stage row = 64 or 128 bytes");
+  using TB = TA;                             // B is the A type
+  constexpr int EPCB = EPC;                  // B elements per chunk
+  constexpr int BKCB = BKC;                  // B chunks per row per stage
   constexpr int KS = BKC / Mma::CPS;         // MFMA k-steps per stage
   constexpr int WM = BM / Cfg::WGM, WN = BN / Cfg::WGN;
   constexpr int BLK = Mma::BLK, NV = Mma::NV;
@@ -249,16 +244,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < NI; ++j) {                                    \
       const int r_ = wn * WN + j * BLK + frow;                                          \
-      if constexpr (FP8B) {                                                             \
-        /* 8 fp8 values = K elements 8 c_ .. 8 c_ + 7: half (c_ & 1) of chunk c_ / 2 */ \
-        const int cb_ = c_ >> 1;                                                        \
-        const uint2 q8_ = reinterpret_cast<const uint2*>(                               \
-            s_ + ACH + r_ * BKCB + (cb_ ^ lds_swz<BKCB>(r_)))[c_ & 1];                  \
-        const uint2 lo_ = fp8x4_to_bf16x4(q8_.x), hi_ = fp8x4_to_bf16x4(q8_.y);         \
-        fb[f][j] = u32x4{lo_.x, lo_.y, hi_.x, hi_.y};                                   \
-      } else {                                                                          \
-        fb[f][j] = s_[ACH + r_ * BKCB + (c_ ^ lds_swz<BKCB>(r_))];                      \
-      }                                                                                 \
+      fb[f][j] = s_[ACH + r_ * BKCB + (c_ ^ lds_swz<BKCB>(r_))];                        \
     }                                                                                   \
   } while (0)
 #define LMOE_MMA(f)                                                                     \
@@ -318,7 +304,6 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   __syncthreads();
 
   // ---- epilogue through LDS: direct output (scale, act, convert) or fp32 partial
-  const float* sc = SCALE ? p.b_scale + (int64_t)g * p.s_gstride : nullptr;
   if (partial == nullptr) {
     // SwiGLU: column pairs (up, gate) become one output column, the tile is
     // BN / 2 wide
@@ -336,19 +321,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
 #pragma unroll
       for (int g4 = 0; g4 < NV / 4; ++g4) {
         const int colt = wn * WN + j * BLK + Mma::t_col(lane, g4);
-        float s4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s4[e] = (SCALE && col0 + colt + e < p.N) ? sc[col0 + colt + e] : 1.f;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           float val[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            val[e] = acc[i][j][4 * g4 + e];
-            if (SCALE) val[e] *= s4[e];
-            val[e] = apply_act<ACT>(val[e]);
-          }
+          for (int e = 0; e < 4; ++e) val[e] = apply_act<ACT>(acc[i][j][4 * g4 + e]);
           if constexpr (GLU) {
             store2<TOut>(Ct + (wm * WM + i * BLK + trow) * LDT + colt / 2, swiglu(val[0], val[1]),
                          swiglu(val[2], val[3]));
@@ -414,10 +391,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::OCC) void gemm_tiled_kernel(GemmArgs 
   }
 }
 
-// C[r][c] = act(scale[c] * sum_s P[s][r][c]) (+ R[r][c]), splits added in order.
-template <typename TOut, int ACT, bool SCALE>
+// C[r][c] = act(sum_s P[s][r][c]) (+ R[r][c]), splits added in order.
+template <typename TOut, int ACT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int splits,
-                                                            int M, int N, const float* __restrict__ scale,
+                                                            int M, int N,
                                                             const float* __restrict__ R, int64_t ldr,
                                                             TOut* __restrict__ C, int64_t ldc) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 columns per thread
@@ -429,27 +406,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   f32x4_t s = *reinterpret_cast<const f32x4_t*>(P + (int64_t)r * N + c);
   for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4_t*>(P + z * mn + (int64_t)r * N + c);
   if constexpr (ACT == kActSwiGlu) {  // columns (c, c+1), (c+2, c+3) -> c/2, c/2 + 1
-    float v4[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) v4[v] = SCALE ? s[v] * scale[c + v] : s[v];
-    store_elem<TOut>(C + (int64_t)r * ldc + c / 2, swiglu(v4[0], v4[1]));
-    store_elem<TOut>(C + (int64_t)r * ldc + c / 2 + 1, swiglu(v4[2], v4[3]));
+    store_elem<TOut>(C + (int64_t)r * ldc + c / 2, swiglu(s[0], s[1]));
+    store_elem<TOut>(C + (int64_t)r * ldc + c / 2 + 1, swiglu(s[2], s[3]));
     return;
   }
   f32x4_t res = {0.f, 0.f, 0.f, 0.f};
   if (R != nullptr) res = *reinterpret_cast<const f32x4_t*>(R + (int64_t)r * ldr + c);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    float val = s[v];
-    if (SCALE) val *= scale[c + v];
-    val = apply_act<ACT>(val);
+    float val = apply_act<ACT>(s[v]);
     if (R != nullptr) val += res[v];
     store_elem<TOut>(C + (int64_t)r * ldc + c + v, val);
   }
 }
 
-template <typename Mma, typename TA, typename TB, typename TOut, typename Cfg>
+template <typename Mma, typename TA, typename TOut, typename Cfg>
 hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, hipStream_t s) {
+  using TB = TA;
   constexpr int BM = Cfg::BM, BN = Cfg::BN;
   const int n_tiles = (a.N + BN - 1) / BN;
   int64_t m_tiles;
@@ -462,7 +435,7 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
   const uint64_t a_rows = a.g_off ? (uint64_t)a.a_nrows : (uint64_t)a.M;
   if (a_rows * a.lda * sizeof(TA) >= (1ull << 31) || (uint64_t)a.N * a.ldb * sizeof(TB) >= (1ull << 31))
     return hipErrorInvalidValue;
-  const bool scale = a.b_scale != nullptr;
+  if (a.b_scale) return hipErrorInvalidValue;  // fp8 weights: launch_gemm_fp8w
   float* part = splits > 1 ? partial : nullptr;
   if (part && BM * BN > 128 * 128) return hipErrorInvalidValue;  // partial tile must fit LDS
   // two weight matrices: dense, whole column tiles each, partials only
@@ -475,31 +448,23 @@ hipError_t launch_t(const GemmArgs& a, int splits, float* partial, bool reduce, 
     return hipErrorInvalidValue;
   // SwiGLU: whole column pairs, output N / 2 wide
   if (a.act == kActSwiGlu && (a.N % 4 || a.ldc < a.N / 2 || a.B2)) return hipErrorInvalidValue;
-  if (a.act == kActSqRelu) {
-    if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSqRelu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-  } else if (a.act == kActSwiGlu) {
-    if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSwiGlu, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActSwiGlu, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-  } else {
-    if (scale) gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, true><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-    else gemm_tiled_kernel<Mma, TA, TB, TOut, Cfg, kActNone, false><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
-  }
+  if (a.act == kActSqRelu)
+    gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActSqRelu><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+  else if (a.act == kActSwiGlu)
+    gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActSwiGlu><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
+  else
+    gemm_tiled_kernel<Mma, TA, TOut, Cfg, kActNone><<<dim3(grid), dim3(Cfg::NT), 0, s>>>(a, splits, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part || !reduce) return e;
   const int64_t n4 = (int64_t)a.M * (a.N / 4);
   const dim3 rg((n4 + 255) / 256);
   TOut* C = static_cast<TOut*>(a.C);
-  if (a.act == kActSqRelu) {
-    if (scale) splitk_reduce_kernel<TOut, kActSqRelu, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
-    else splitk_reduce_kernel<TOut, kActSqRelu, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
-  } else if (a.act == kActSwiGlu) {
-    if (scale) splitk_reduce_kernel<TOut, kActSwiGlu, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
-    else splitk_reduce_kernel<TOut, kActSwiGlu, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
-  } else {
-    if (scale) splitk_reduce_kernel<TOut, kActNone, true><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.b_scale, a.R, a.ldr, C, a.ldc);
-    else splitk_reduce_kernel<TOut, kActNone, false><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, nullptr, a.R, a.ldr, C, a.ldc);
-  }
+  if (a.act == kActSqRelu)
+    splitk_reduce_kernel<TOut, kActSqRelu><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.R, a.ldr, C, a.ldc);
+  else if (a.act == kActSwiGlu)
+    splitk_reduce_kernel<TOut, kActSwiGlu><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.R, a.ldr, C, a.ldc);
+  else
+    splitk_reduce_kernel<TOut, kActNone><<<rg, 256, 0, s>>>(part, splits, a.M, a.N, a.R, a.ldr, C, a.ldc);
   return hipGetLastError();
 }
 
@@ -512,32 +477,17 @@ hipError_t launch_tile(const GemmArgs& a, Dt a_dt, Dt out_dt, int splits, float*
   using MmaB = std::conditional_t<(Cfg::BM / Cfg::WGM >= 64 && Cfg::BN / Cfg::WGN >= 64),
                                   MmaBf16x32, MmaBf16>;
   if (a_dt == Dt::BF16) {
-    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, uint16_t, Cfg>(a, splits, partial, reduce, s);
+    if (out_dt == Dt::BF16) return launch_t<MmaB, uint16_t, uint16_t, Cfg>(a, splits, partial, reduce, s);
     if constexpr (Cfg::BM * Cfg::BN <= 128 * 256)
-      return launch_t<MmaB, uint16_t, uint16_t, float, Cfg>(a, splits, partial, reduce, s);
+      return launch_t<MmaB, uint16_t, float, Cfg>(a, splits, partial, reduce, s);
     return hipErrorInvalidValue;
   }
   if constexpr (Cfg::BM * Cfg::BN <= 64 * 64)
-    return launch_t<MmaF32, float, float, float, Cfg>(a, splits, partial, reduce, s);
+    return launch_t<MmaF32, float, float, Cfg>(a, splits, partial, reduce, s);
   return hipErrorInvalidValue;
 }
 
-// fp8 (OCP E4M3) B with per-row scales, bf16 A and output: grouped expert
-// GEMMs over fp8 expert weights when experts receive several dozen rows.
-// 96 rows (3 MFMA blocks of 32) cover such an expert with little padding, so
-// each weight tile is read once; 4 waves side by side along N (96 x 64 each);
-// stage rows of 64 bf16 (A) / 64 fp8 (B); two stages and two workgroups per
-// compute unit.
-using TileFp8 = TileCfg<96, 256, 1, 4, 8, 2, 2>;
-
 }  // namespace
-
-hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s) {
-  if (a.b_scale == nullptr) return hipErrorInvalidValue;
-  return launch_t<MmaBf16x32, uint16_t, uint8_t, uint16_t, TileFp8>(a, 1, nullptr, false, s);
-}
-
-int tiled_block_m_fp8w() { return TileFp8::BM; }
 
 int tiled_block_m(int tile) {
   switch (tile) {  // (fp32 layers run every tile index as Tile64)
@@ -550,7 +500,7 @@ int tiled_block_m(int tile) {
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hipStream_t s,
                              int splits, float* partial, bool reduce) {
-  if (a_dt == Dt::FP8) return hipErrorInvalidValue;  // fp8 weights go through the streaming kernel
+  if (a_dt == Dt::FP8) return hipErrorInvalidValue;  // fp8 weights: launch_gemm_fp8w, gemm_stream
   if (a_dt == Dt::F32 && out_dt != Dt::F32) return hipErrorInvalidValue;
   if (splits < 1 || (splits > 1 && (a.g_off != nullptr || partial == nullptr || a.N % 4)))
     return hipErrorInvalidValue;

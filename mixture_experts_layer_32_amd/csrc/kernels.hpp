@@ -63,9 +63,12 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, Dt a_dt, Dt out_dt, int tile, hi
                              int splits = 1, float* partial = nullptr, bool reduce = true);
 int tiled_block_m(int tile);
 // Grouped GEMM with OCP E4M3 weights (b_scale: one fp32 scale per weight
-// row), bf16 activations and output, LDS-tiled.
-hipError_t launch_gemm_tiled_fp8w(const GemmArgs& a, hipStream_t s);
-int tiled_block_m_fp8w();
+// row), bf16 activations and output: 96-row tiles (g_tiles counts them),
+// weights streamed into registers.  Needs N and K multiples of 16, at most
+// 2048 groups.
+bool gemm_fp8w_fits(int N, int K, int G);
+hipError_t launch_gemm_fp8w(const GemmArgs& a, hipStream_t s);
+int fp8w_block_m();
 
 // Grouped GEMM for experts with many rows (prefill), bf16 operands and
 // output: a persistent grid walks (expert, row tile, 256-column tile) items;
