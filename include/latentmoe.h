@@ -264,9 +264,10 @@ const char *latentmoe_last_error(void);
 /* Name of the expert-kernel regime the handle picks for T tokens:
  * "stream" (weight-streaming grouped GEMMs, tokens per expert few),
  * "fused" (FC1 and FC2 in one weight-streaming kernel), "tiled"
- * (LDS-tiled MFMA grouped GEMMs) or "grouped" (the persistent 256 x 256
- * MFMA grouped GEMMs of bf16 layers with many tokens per expert).  For
- * reports only. */
+ * (LDS-tiled MFMA grouped GEMMs), "grouped" (the persistent 256 x 256
+ * MFMA grouped GEMMs of bf16 layers with many tokens per expert) or "fp8w"
+ * (the grouped GEMMs over fp8 weights streamed into registers, which the
+ * TILED choice selects for fp8 experts).  For reports only. */
 const char *latentmoe_expert_regime(const lmoe_handle *h, int64_t T);
 
 #ifdef __cplusplus

@@ -418,7 +418,9 @@ lmoe_status latentmoe_workspace_size(const lmoe_handle* h, int64_t T, size_t* by
 const char* latentmoe_expert_regime(const lmoe_handle* h, int64_t T) {
   if (!h || T < 0) return "invalid";
   const Plan p = make_plan(h->cfg, T);
-  return p.fused ? "fused" : p.stream ? "stream" : p.grouped ? "grouped" : "tiled";
+  if (p.fused || p.stream) return p.fused ? "fused" : "stream";
+  if (p.grouped) return "grouped";
+  return h->cfg.expert_dtype == LMOE_FP8_E4M3_ROWSCALE ? "fp8w" : "tiled";
 }
 
 lmoe_status latentmoe_timer_create(lmoe_timer** out) {

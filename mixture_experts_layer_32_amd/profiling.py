@@ -59,17 +59,18 @@ def short_name(name: str) -> str:
 def expert_kernel_kind(name: str) -> str | None:
     """Which expert-FFN kernel a profiled kernel name is: "ffn_stream" (fused
     FC1 + FC2), "gemm_stream" (weight streaming), "gemm_grouped" (the
-    persistent 256 x 256 grouped kernel) or "gemm_tiled" (grouped
-    LDS-tiled: the 128 x 256 tile, or fp8 weights), else None (dense GEMMs
-    and routing kernels)."""
+    persistent 256 x 256 grouped kernel), "gemm_fp8w" (fp8 weights streamed
+    into registers) or "gemm_tiled" (grouped LDS-tiled: the 128 x 256
+    tile), else None (dense GEMMs and routing kernels)."""
     if "ffn_stream_kernel" in name:
         return "ffn_stream"
     if "gemm_grouped_kernel<" in name:
         return "gemm_grouped"
+    if "gemm_fp8w_kernel<" in name:
+        return "gemm_fp8w"
     if "gemm_stream_kernel<" in name:
         return "gemm_stream"
-    if "gemm_tiled_kernel<" in name and ("TileCfg<128, 256" in name or "unsigned char" in name
-                                         or ", u8," in name):
+    if "gemm_tiled_kernel<" in name and "TileCfg<128, 256" in name:
         return "gemm_tiled"
     # the 256 x 256 tile serves the dense projections too: only an instance
     # with an activation (the experts' FC1; the dense GEMMs have none, the
@@ -80,14 +81,21 @@ def expert_kernel_kind(name: str) -> str | None:
 
 
 def _act_arg(name: str) -> str:
-    """ACT, the second to last template argument of a GEMM kernel name."""
-    return [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")][-2]
+    """The ACT template argument of an expert GEMM kernel name: the first of
+    the grouped and fp8 kernels, the last of the LDS-tiled kernel, the second
+    to last of the streaming kernel."""
+    args = [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")]
+    if "gemm_grouped_kernel<" in name or "gemm_fp8w_kernel<" in name:
+        return args[0]
+    if "gemm_tiled_kernel<" in name:
+        return args[-1]
+    return args[-2]
 
 
 def expert_stage(name: str) -> str | None:
     """The stage an expert kernel runs: "ffn" for the fused kernel, else
-    "fc1" when its activation template argument (ACT, second to last) is
-    not 0 (squared ReLU 1, SwiGLU 2), "fc2" when it is."""
+    "fc1" when its activation template argument (ACT) is not 0 (squared ReLU
+    1, SwiGLU 2), "fc2" when it is."""
     kind = expert_kernel_kind(name)
     if kind is None:
         return None
@@ -202,17 +210,17 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
 
 
 REGIME_KERNEL = {"fused": "ffn_stream", "stream": "gemm_stream", "tiled": "gemm_tiled",
-                 "grouped": "gemm_grouped"}
+                 "grouped": "gemm_grouped", "fp8w": "gemm_fp8w"}
 
 
 def hbm_file(workload: str, kind: str) -> str:
-    """kind: "ffn_stream", "gemm_stream", "gemm_tiled" or "gemm_grouped"."""
+    """kind: "ffn_stream", "gemm_stream", "gemm_tiled", "gemm_grouped" or "gemm_fp8w"."""
     return os.path.join(PROFILES, "%s_%s_hbm.txt" % (kind, workload))
 
 
 def read_hbm(workload: str, stage: str, regime: str):
     """HBM bytes per launch of the FC1/FC2 (or fused, stage "ffn") kernel of
-    the expert regime ("fused", "stream", "tiled", "grouped") from the committed
+    the expert regime ("fused", "stream", "tiled", "grouped", "fp8w") from the committed
     summary, or None when there is none or the kernel sources changed since."""
     path = hbm_file(workload, REGIME_KERNEL[regime])
     if not os.path.exists(path):

@@ -60,7 +60,7 @@ def test_regime_choice():
     assert sw.expert_regime(512) == "tiled"      # 48 rows per expert
     assert sw.expert_regime(256) == "fused"      # 24 rows, 256 experts
     fp8 = pkg.LatentMoELayer(workload("latent_fp8_sparse").spec)
-    assert fp8.expert_regime(4096) == "tiled"    # 73 rows per expert
+    assert fp8.expert_regime(4096) == "fp8w"     # 73 rows per expert
     assert fp8.expert_regime(512) == "stream"    # 9 rows per expert
     for kind in ("tiled", "stream", "fused"):
         forced = pkg.LatentMoELayer(workload("latent_decode").spec, expert_kernel=kind)

@@ -40,13 +40,14 @@ NAMES = {
     "void lmoe::(anonymous namespace)::gemm_stream_kernel<lmoe::MmaBf16, unsigned short, "
     "unsigned char, unsigned short, 8, 1, 0, true>(lmoe::GemmArgs)": ("gemm_stream", "fc2"),
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
-    "unsigned short, unsigned short, lmoe::TileCfg<128, 256, 2, 2, 4, 3, 2>, 2, false>"
+    "unsigned short, lmoe::TileCfg<128, 256, 2, 2, 4, 3, 2>, 2>"
     "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc1"),
+    "void lmoe::(anonymous namespace)::gemm_fp8w_kernel<0, true>(lmoe::GemmArgs)":
+        ("gemm_fp8w", "fc2"),
+    "void lmoe::(anonymous namespace)::gemm_fp8w_kernel<1, true>(lmoe::GemmArgs)":
+        ("gemm_fp8w", "fc1"),
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
-    "unsigned char, unsigned short, lmoe::TileCfg<96, 256, 1, 4, 8, 2, 2>, 0, true>"
-    "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc2"),
-    "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
-    "unsigned short, unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 1, false>"
+    "unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 1>"
     "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc1"),
     "void lmoe::(anonymous namespace)::gemm_grouped_kernel<1, true>(lmoe::GemmArgs)":
         ("gemm_grouped", "fc1"),
@@ -56,11 +57,11 @@ NAMES = {
         ("gemm_grouped", "fc2"),
     # the same tile without activation is shared with the dense projections
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
-    "unsigned short, unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 0, false>"
+    "unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 0>"
     "(lmoe::GemmArgs, int, float*)": (None, None),
     # dense GEMMs (projections, router, shared experts) and routing are not expert kernels
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
-    "unsigned short, float, lmoe::TileCfg<128, 128, 2, 2, 8, 2, 2>, 1, false>"
+    "float, lmoe::TileCfg<128, 128, 2, 2, 8, 2, 2>, 1>"
     "(lmoe::GemmArgs, int, float*)": (None, None),
     "void lmoe::(anonymous namespace)::combine_kernel<unsigned short, 32>(...)": (None, None),
 }
