@@ -237,6 +237,94 @@ def read_hbm(workload: str, stage: str, regime: str):
     return float(v) if v is not None else None
 
 
+COUNTER_PASSES = (
+    "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_MFMA",
+    "GRBM_GUI_ACTIVE SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_LDS_DATA_FIFO_FULL "
+    "SQ_LDS_CMD_FIFO_FULL SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL SQ_INST_LEVEL_VMEM",
+    "GRBM_GUI_ACTIVE TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum TCP_PENDING_STALL_CYCLES_sum "
+    "TCP_TCC_READ_REQ_sum TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum "
+    "TCC_TAG_STALL_sum",
+)
+N_XCD, N_SIMD, N_CU = 8, 1024, 256
+MFMA_PEAK_BF16 = 2.5e15      # dense bf16 MFMA, flop/s at the 2.4 GHz peak clock
+
+
+def counter_means(pmc_dirs):
+    """kernel name -> counter -> mean value per dispatch, over the passes."""
+    out = defaultdict(dict)
+    for d in pmc_dirs:
+        acc = defaultdict(lambda: defaultdict(list))
+        with open(_one(d, "counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k, cs in acc.items():
+            for c, v in cs.items():
+                if c != "GRBM_GUI_ACTIVE" or c not in out[k]:
+                    out[k][c] = sum(v) / len(v)
+    return out
+
+
+def write_counters_md(workload: str, pmc_dirs, trace_dir: str | None, out: str):
+    """Per expert GEMM kernel: MFMA utilisation from the SQ counters, the
+    wave-state split, LDS and vector-memory stalls and the L2 hit rate."""
+    avg_us = {}
+    if trace_dir:
+        avg_us = {r["name"]: r["avg_us"] for r in kernel_stats(trace_dir)}
+    m = counter_means(pmc_dirs)
+    lines = ["# Hardware counters of the expert GEMM kernels, workload %s" % workload, "",
+             "Commands (from a scratch directory, TMPDIR=/tmp), one pass per counter group:", ""]
+    for p in COUNTER_PASSES:
+        lines.append("    rocprofv3 --pmc %s -d <dir> -o pmc --output-format csv -- "
+                     "python3 bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline"
+                     % (p, workload))
+    lines += ["", "Reading the counters: GRBM_GUI_ACTIVE adds the 8 XCDs' busy cycles (per-XCD "
+              "cycles = value / 8; over the kernel's traced duration this gives the clock); "
+              "SQ_VALU_MFMA_BUSY_CYCLES adds the 1024 SIMDs' MFMA-busy cycles (busy fraction = "
+              "value / (1024 x per-XCD cycles); a 32x32x16 bf16 MFMA counts 32 busy cycles, "
+              "a 16x16x32 one 16); one SQ_INSTS_VALU_MFMA_MOPS_BF16 unit is 512 flop.  The "
+              "wave-state counters are given as fractions of SQ_WAVE_CYCLES.", ""]
+    for name, c in sorted(m.items()):
+        st = expert_stage(name)
+        if not st or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc)
+        flop = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        lines.append("## %s: `%s`" % (st.upper(), short_name(name)[:140]))
+        lines.append("")
+        lines.append("- per-XCD busy cycles %.4g" % cyc)
+        if name in avg_us:
+            us = avg_us[name]
+            lines.append("- traced average duration %.2f us: clock %.2f GHz" % (us, cyc / us / 1e3))
+            lines.append("- MFMA work %.4g flop: %.1f TFLOP/s, %.3f of the %.0f TFLOP/s bf16 peak"
+                         % (flop, flop / us / 1e6, flop / us / 1e6 / (MFMA_PEAK_BF16 / 1e12),
+                            MFMA_PEAK_BF16 / 1e12))
+        lines.append("- MFMA busy %.1f%% of SIMD cycles (%.4g MFMA instructions, %.1f busy "
+                     "cycles each)" % (100 * busy, c.get("SQ_INSTS_MFMA", 0.0),
+                                       c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(c.get("SQ_INSTS_MFMA", 1.0), 1.0)))
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        if wc:
+            lines.append("- wave cycles: issuing %.1f%%, waiting to issue %.1f%%, waiting on "
+                         "s_waitcnt %.1f%%" % tuple(100 * c.get(k, 0.0) / wc for k in (
+                             "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY")))
+        if "SQ_LDS_IDX_ACTIVE" in c:
+            lines.append("- LDS bank-conflict cycles %.1f%% of LDS-active cycles; VMEM TA "
+                         "address / command FIFO full %.4g / %.4g cycles"
+                         % (100 * c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0),
+                            c["SQ_VMEM_TA_ADDR_FIFO_FULL"], c["SQ_VMEM_TA_CMD_FIFO_FULL"]))
+        if "TCC_HIT_sum" in c:
+            h, mi = c["TCC_HIT_sum"], c["TCC_MISS_sum"]
+            lines.append("- L2 hit rate %.1f%% (%.4g requests from the CUs); TA busy %.1f%%, "
+                         "TCP pending-stall %.1f%% of per-CU cycles"
+                         % (100 * h / max(h + mi, 1.0), c.get("TCP_TCC_READ_REQ_sum", 0.0),
+                            100 * c["TA_TA_BUSY_sum"] / (N_CU * cyc),
+                            100 * c["TCP_PENDING_STALL_CYCLES_sum"] / (N_CU * cyc)))
+        lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def _read_kv(path):
     kv = {}
     with open(path) as f:
@@ -293,6 +381,8 @@ def main():
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--bench-json")
+    ap.add_argument("--counters", action="append", default=[],
+                    help="rocprofv3 --pmc output directory of one counter pass (repeatable)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="batch of a run at a non-default T (names the HBM file ..._T<T>)")
     ap.add_argument("--sweep-summary", help="write the alpha-sweep summary (markdown) here")
@@ -307,6 +397,10 @@ def main():
     if a.trace:
         out = os.path.join(PROFILES, "%s_kernels_trace.md" % a.workload)
         write_trace_md(a.workload, a.trace, a.bench_json, out)
+        print(out)
+    if a.counters:
+        out = os.path.join(PROFILES, "%s_expert_counters.md" % a.workload)
+        write_counters_md(a.workload, a.counters, a.trace, out)
         print(out)
     if a.fetch and a.write and a.copy_fetch and a.copy_write:
         kinds = {expert_kernel_kind(n) for n in counter_per_dispatch(a.fetch, "FETCH_SIZE")}
