@@ -160,17 +160,23 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   // stage kt -> ring buffer kt % kGgNS; stages past the end load zeros
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)gg_ring)));
-  auto issue = [&](int kt) {
+  auto issue_part = [&](int kt, int j0, int j1) {
     const uint32_t s_ = ring_lds + static_cast<uint32_t>((kt % kGgNS) * kGgStage * 16);
     const uint32_t kb = static_cast<uint32_t>(kt) * (kGgBK * 2);
     const bool live = kt < nk;
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
+    for (int j = j0; j < j1; ++j) {
       const bool is_a = (kGgNW * j + wave) * 64 < ACH;  // wave-uniform
       gg_dma(is_a ? a_rsrc : b_rsrc, s_ + static_cast<uint32_t>((kGgNW * j + wave) * 64 * 16),
              live ? d_off[j] + kb : kOutOfRange);
     }
   };
+  auto issue = [&](int kt) { issue_part(kt, 0, NDMA); };
+  // the loads of stage kt + 2: NA of them in k-step 0, NB in k-step 1.  FC1
+  // (gathered rows, K = l) measured 3 % faster with the loads split over
+  // both k-steps, FC2 (K = m) 3 % slower; so only the gathering instance
+  // splits them.
+  constexpr int NA = GATHER ? (NDMA + 1) / 2 : NDMA, NB = NDMA - NA;
 
   // fragments of k-step ks (two chunks of K per 32x32x16 MFMA) of stage kt
   const int frow = lane & 31, fchk = lane >> 5;
@@ -197,15 +203,15 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
           acc[i][j], 0, 0, 0);                                                   \
   } while (0)
   // a k-step: its MFMAs with the next k-step's fragment reads in front
-  // (one read, one MFMA), then the stage's loads (k-step 0 only)
-#define GG_SCHED(with_loads)                                                     \
+  // (one read, one MFMA), then its share of the next stage's loads
+#define GG_SCHED(loads)                                                          \
   do {                                                                           \
     _Pragma("unroll") for (int q_ = 0; q_ < MI + 4; ++q_) {                      \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         \
     }                                                                            \
-    if (with_loads) {                                                            \
-      _Pragma("unroll") for (int q_ = 0; q_ < NDMA; ++q_) {                      \
+    if ((loads) > 0) {                                                           \
+      _Pragma("unroll") for (int q_ = 0; q_ < (loads); ++q_) {                   \
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                       \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       \
       }                                                                          \
@@ -224,22 +230,30 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   __builtin_amdgcn_sched_barrier(0);
   GG_FRAGS(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    // k-step 0: fragments of k-step 1 in front, then the loads of stage
-    // kt + 3 into the buffer stage kt - 1 used (every wave finished reading
-    // it before the last barrier)
+    // k-step 0: fragments of k-step 1 in front, then the first NA loads of
+    // stage kt + 2 into the buffer stage kt - 1 used (every wave finished
+    // reading it before the last barrier)
     GG_FRAGS(kt, 1, 1);
-    issue(kt + kGgNS - 1);
+    issue_part(kt + kGgNS - 1, 0, NA);
     GG_MMA(0);
-    GG_SCHED(true);
-    // stage kt + 1 landed (this thread's loads; the barrier makes it
+    GG_SCHED(NA);
+    // k-step 0's MFMAs stay in front of the wait (the scheduler would move
+    // some of them past the barrier, and the wave would wait with the MFMA
+    // pipe idle)
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt + 1 landed (this thread's loads, all issued before the NA
+    // of stage kt + 2 still allowed in flight; the barrier makes it
     // everyone's), this wave's fragment reads done
-    wait_vmcnt_lgkm0<(kGgNS - 2) * NDMA>();
+    wait_vmcnt_lgkm0<(kGgNS - 3) * NDMA + NA>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // k-step 1: stage kt + 1's first fragments in front
+    // k-step 1: stage kt + 1's first fragments in front, then the rest of
+    // stage kt + 2's loads (into the same buffer, read by no wave since the
+    // last barrier)
     GG_FRAGS(kt + 1, 0, 0);
+    issue_part(kt + kGgNS - 1, NA, NDMA);
     GG_MMA(1);
-    GG_SCHED(false);
+    GG_SCHED(NB);
   }
 #undef GG_SCHED
 #undef GG_MMA
