@@ -10,34 +10,34 @@
 // cut into tiles of 256; its last tile is 256, 128 or 64 rows high, the
 // smallest that holds what is left, so that skewed loads (many experts with
 // a few dozen rows, a few with thousands) spend little MFMA work on padding
-// rows.  Every tile is computed by 2 x 2 waves: 128 x 128 each (64 x 128 or
-// 32 x 128 in the shorter tiles) in 32x32x16 bf16 MFMA blocks, with the
-// 16 accumulator blocks of a wave in AGPRs.  One workgroup of four waves
-// (one per SIMD) runs per compute unit and walks its items (a persistent
-// grid); each XCD takes a contiguous range of items, so the column tiles of
-// a row tile (which share its A rows) and the row tiles of an expert (which
-// share its weights) run on the same L2 at about the same time.  The
-// expert offsets sit in LDS, and a tile fetches the next tile's gathered
-// row indices into LDS behind its own first loads, so that a tile starts
-// without a dependent global load.
+// rows.  Every tile is computed by 2 x 4 waves: 128 x 64 each (64 x 64 or
+// 32 x 64 in the shorter tiles) in 32x32x16 bf16 MFMA blocks.  One
+// workgroup of eight waves (two per SIMD, so that one wave's MFMAs run while
+// the other waits on a load, a barrier or its epilogue) runs per compute
+// unit and walks its items (a persistent grid); each XCD takes a contiguous
+// range of items, so the column tiles of a row tile (which share its A
+// rows) and the row tiles of an expert (which share its weights) run on the
+// same L2 at about the same time.  The expert offsets sit in LDS, and a
+// tile fetches the next tile's gathered row indices into LDS behind its own
+// first loads, so that a tile starts without a dependent global load.
 //
-// K advances in stages of 32 elements through an LDS ring of three stage
+// K advances in stages of 32 elements through an LDS ring of four stage
 // buffers filled by buffer loads in LDS mode (each lane 16 bytes, no
-// register staging): two stages are in flight while one is multiplied.
-// Every thread issues the same number of loads per stage, so "the next
-// stage has landed" is an exact vmcnt wait, then one barrier per stage.
-// Fragment reads of the next k-step are issued at the front of each
-// k-step, so they are complete when the stage ends.  LDS rows are 64 bytes
-// (4 chunks); chunk c of row r sits at c ^ ((r >> 2) & 3), so the 32 lanes
-// reading one fragment column touch distinct bank groups.
+// register staging): three stages are in flight while one is multiplied.
+// Every thread issues the same number of loads per stage (A rows past a
+// short tile read zeros without a memory request), so "the next stage has
+// landed" is an exact vmcnt wait, then one barrier per stage.  Fragment
+// reads of the next k-step are issued at the front of each k-step, so they
+// are complete when the stage ends.  LDS rows are 64 bytes (4 chunks);
+// chunk c of row r sits at c ^ ((r >> 2) & 3), so the 32 lanes reading one
+// fragment column touch distinct bank groups.
 //
 // Each lane ends with 4 consecutive output columns per block row (the
 // MFMA computes the block transposed); one 32-row block row of the wave's
 // columns at a time is activated, rounded to bf16, staged in LDS and
-// stored as 256-byte row segments (stores straight from the accumulators,
+// stored as 128-byte row segments (stores straight from the accumulators,
 // 16 bytes to each of 32 rows per instruction, took several times longer).
-// One wave per SIMD leaves nothing to overlap the epilogue's vector work
-// with, so it is kept short: buffer stores whose range ends at the tile's
+// The epilogue is kept short: buffer stores whose range ends at the tile's
 // last row (no per-row test) and a one-instruction ReLU.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,13 +45,16 @@
 namespace lmoe {
 namespace {
 
-constexpr int kGgNT = 256;                           // 4 waves, one per SIMD
+constexpr int kGgNT = 512;                           // 8 waves, two per SIMD
 constexpr int kGgNW = kGgNT / 64;
+constexpr int kGgWN = 4;                             // waves along N (2 along M)
+constexpr int kGgWCols = 256 / kGgWN;                // columns of a wave (64)
+constexpr int kGgNJ = kGgWCols / 32;                 // 32-column blocks of a wave (2)
 constexpr int kGgBN = 256;                           // columns per tile
 constexpr int kGgBM = 256;                           // rows of a full tile
 constexpr int kGgBKC = 4;                            // 16-byte chunks of K per row per stage
 constexpr int kGgBK = kGgBKC * 8;                    // K elements per stage
-constexpr int kGgNS = 3;                             // stage buffers in the ring
+constexpr int kGgNS = 4;                             // stage buffers in the ring
 constexpr int kGgStage = (kGgBM + kGgBN) * kGgBKC;   // chunks per stage buffer (32 KB)
 constexpr int kGgMaxG = 2048;
 
@@ -64,14 +67,19 @@ struct GgTile {
   int col0;    // first output column
 };
 
-typedef f32x16_t GgAcc[4][4];
+typedef f32x16_t GgAcc[4][kGgNJ];
 
-__shared__ u32x4 gg_ring[kGgNS * kGgStage];   // the LDS ring, 96 KB
 // Epilogue staging, one area per wave: a 32-row block row of the wave's
-// 128 output columns in bf16 (rows padded by 16 bytes against bank
-// conflicts), so that stores leave as 256-byte row segments.
-constexpr int kGgOutLd = 128 + 8;                   // bf16 elements per staged row
-__shared__ uint16_t gg_out[kGgNW][32 * kGgOutLd];   // 4 x 8.5 KB
+// 64 output columns in bf16 (rows padded by 16 bytes against bank
+// conflicts), so that stores leave as 128-byte row segments.  The areas
+// (8 x 4.5 KB) sit in the ring's last stage buffer and 4 KB past it: the
+// next tile's first loads fill the other buffers, and the last buffer is
+// next written after the barrier that every wave reaches only once its
+// epilogue is done.
+constexpr int kGgOutLd = kGgWCols + 8;              // bf16 elements per staged row
+constexpr int kGgOutChunks = kGgNW * 32 * kGgOutLd * 2 / 16;
+constexpr int kGgRingTail = kGgOutChunks > kGgStage ? kGgOutChunks - kGgStage : 0;
+__shared__ u32x4 gg_ring[kGgNS * kGgStage + kGgRingTail];   // the LDS ring, 128 + 4 KB
 // Source rows of a tile's A rows (FC1 gathers them through a_rows), double
 // buffered: a tile reads its own and prefetches the next tile's.
 __shared__ int gg_rows[2][kGgBM];
@@ -126,11 +134,14 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   constexpr int BM = 64 * MI;
   constexpr int WM = BM / 2;                     // rows per wave
-  constexpr int ACH = BM * kGgBKC;               // A chunks per stage
+  // A rows loaded per stage: at least 128, so that every thread issues a
+  // whole number of loads (rows past the tile read zeros, no memory request)
+  constexpr int BMLD = BM < 128 ? 128 : BM;
+  constexpr int ACH = BMLD * kGgBKC;             // A chunks per stage
   constexpr int NCH = ACH + kGgBN * kGgBKC;      // chunks loaded per stage
   constexpr int NDMA = NCH / kGgNT;              // loads per thread per stage
   static_assert(NCH % kGgNT == 0 && ACH % 64 == 0, "stage splits into wave loads");
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kGgWN, wn = wave % kGgWN;
   const int nk = p.K / kGgBK;
 
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
@@ -172,7 +183,7 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
     }
   };
   auto issue = [&](int kt) { issue_part(kt, 0, NDMA); };
-  // the loads of stage kt + 2: NA of them in k-step 0, NB in k-step 1.  FC1
+  // the loads of stage kt + 3: NA of them in k-step 0, NB in k-step 1.  FC1
   // (gathered rows, K = l) measured 3 % faster with the loads split over
   // both k-steps, FC2 (K = m) 3 % slower; so only the gathering instance
   // splits them.
@@ -180,7 +191,7 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
 
   // fragments of k-step ks (two chunks of K per 32x32x16 MFMA) of stage kt
   const int frow = lane & 31, fchk = lane >> 5;
-  u32x4 fa[2][MI], fb[2][4];
+  u32x4 fa[2][MI], fb[2][kGgNJ];
 #define GG_FRAGS(kt, ks, f)                                                      \
   do {                                                                           \
     const u32x4* s_ = gg_ring + ((kt) % kGgNS) * kGgStage;                       \
@@ -189,15 +200,15 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
       const int r_ = wm * WM + i * 32 + frow;                                    \
       fa[f][i] = s_[r_ * kGgBKC + (c_ ^ gg_swz(r_))];                            \
     }                                                                            \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                              \
-      const int n_ = wn * 128 + j * 32 + frow;                                   \
+    _Pragma("unroll") for (int j = 0; j < kGgNJ; ++j) {                          \
+      const int n_ = wn * kGgWCols + j * 32 + frow;                              \
       fb[f][j] = s_[ACH + n_ * kGgBKC + (c_ ^ gg_swz(n_))];                      \
     }                                                                            \
   } while (0)
 #define GG_MMA(f)                                                                \
   do {                                                                           \
     _Pragma("unroll") for (int i = 0; i < MI; ++i)                               \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                \
+    _Pragma("unroll") for (int j = 0; j < kGgNJ; ++j)                            \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                       \
           __builtin_bit_cast(bf16x8_t, fb[f][j]), __builtin_bit_cast(bf16x8_t, fa[f][i]), \
           acc[i][j], 0, 0, 0);                                                   \
@@ -206,7 +217,7 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   // (one read, one MFMA), then its share of the next stage's loads
 #define GG_SCHED(loads)                                                          \
   do {                                                                           \
-    _Pragma("unroll") for (int q_ = 0; q_ < MI + 4; ++q_) {                      \
+    _Pragma("unroll") for (int q_ = 0; q_ < MI + kGgNJ; ++q_) {                  \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         \
     }                                                                            \
@@ -216,7 +227,7 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       \
       }                                                                          \
     }                                                                            \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI, 0);                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, kGgNJ * MI, 0);                  \
   } while (0)
 
 #pragma unroll
@@ -224,14 +235,15 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   // the next tile's source rows, behind this tile's first stages: the waits
   // below then also cover them (one load more than a stage may stay in
   // flight at the first wait), and they have landed after k-step 0
-  if (GATHER && next_row0 >= 0) gg_fetch_rows(p, total_rows, next_row0, buf ^ 1, wave, lane);
+  if (GATHER && next_row0 >= 0 && wave < kGgBM / 64)
+    gg_fetch_rows(p, total_rows, next_row0, buf ^ 1, wave, lane);
   wait_vmcnt_lgkm0<(kGgNS - 2) * NDMA>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   GG_FRAGS(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     // k-step 0: fragments of k-step 1 in front, then the first NA loads of
-    // stage kt + 2 into the buffer stage kt - 1 used (every wave finished
+    // stage kt + 3 into the buffer stage kt - 1 used (every wave finished
     // reading it before the last barrier)
     GG_FRAGS(kt, 1, 1);
     issue_part(kt + kGgNS - 1, 0, NA);
@@ -241,14 +253,14 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
     // some of them past the barrier, and the wave would wait with the MFMA
     // pipe idle)
     __builtin_amdgcn_sched_barrier(0);
-    // stage kt + 1 landed (this thread's loads, all issued before the NA
-    // of stage kt + 2 still allowed in flight; the barrier makes it
-    // everyone's), this wave's fragment reads done
+    // stage kt + 1 landed (this thread's loads, issued before stage kt + 2's
+    // and the first NA of stage kt + 3, which may stay in flight; the
+    // barrier makes it everyone's), this wave's fragment reads done
     wait_vmcnt_lgkm0<(kGgNS - 3) * NDMA + NA>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // k-step 1: stage kt + 1's first fragments in front, then the rest of
-    // stage kt + 2's loads (into the same buffer, read by no wave since the
+    // stage kt + 3's loads (into the same buffer, read by no wave since the
     // last barrier)
     GG_FRAGS(kt + 1, 0, 0);
     issue_part(kt + kGgNS - 1, NA, NDMA);
@@ -266,15 +278,15 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   // ---- epilogue, one 32-row block row at a time: lane holds row frow of
   // each block, columns 8 g + 4 (lane / 32) + 0..3 in accumulator elements
   // 4 g .. 4 g + 3; they go to the wave's staging area (activated, in bf16)
-  // and leave as 16-byte chunks, 16 lanes per 256-byte row segment (128
+  // and leave as 16-byte chunks, 8 lanes per 128-byte row segment (64
   // bytes with SwiGLU, whose output is half as wide).  LDS operations of one
   // wave complete in order, so the reads see the writes.  The stores are
   // buffer stores whose range ends at the tile's last row: those of rows
   // past it are dropped by the range check, without a per-store test.
-  constexpr int OW = ACT == kActSwiGlu ? 64 : 128;   // output columns of a wave
+  constexpr int OW = ACT == kActSwiGlu ? kGgWCols / 2 : kGgWCols;  // output columns of a wave
   constexpr int CPR = OW / 8;                        // 16-byte chunks per staged row
   constexpr int RPS = 64 / CPR;                      // rows per wave store
-  uint16_t* stg = gg_out[wave];
+  uint16_t* stg = reinterpret_cast<uint16_t*>(gg_ring + (kGgNS - 1) * kGgStage) + wave * 32 * kGgOutLd;
   const int ocol0 = (ACT == kActSwiGlu ? t.col0 / 2 : t.col0) + wn * OW;
   const uint32_t ldc2 = static_cast<uint32_t>(p.ldc) * 2;
   const BufRsrc c_rsrc = make_rsrc(p.C, static_cast<uint64_t>(t.row0 + t.rows) * ldc2);
@@ -284,10 +296,10 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kGgNJ; ++j)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int c = j * 32 + 8 * g4 + 4 * fchk;   // column within the wave's 128
+        const int c = j * 32 + 8 * g4 + 4 * fchk;   // column within the wave's 64
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = apply_act<ACT>(acc[i][j][4 * g4 + e]);
@@ -390,7 +402,7 @@ __global__ __launch_bounds__(kGgNT, 1) void gemm_grouped_kernel(GemmArgs p) {
     if (g + step < G && s_pre[g + step] <= item) g += step;
   g = __builtin_amdgcn_readfirstlane(g);
   if (GATHER) {  // the first tile's source rows
-    gg_fetch_rows(p, total_rows, tile_of(g, item).row0, 0, wave, lane);
+    if (wave < kGgBM / 64) gg_fetch_rows(p, total_rows, tile_of(g, item).row0, 0, wave, lane);
     wait_vmcnt_lgkm0<0>();
     __syncthreads();
   }
@@ -403,7 +415,7 @@ __global__ __launch_bounds__(kGgNT, 1) void gemm_grouped_kernel(GemmArgs p) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < kGgNJ; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
     if (t.rows > 128) gg_tile<4, ACT, GATHER>(p, t, wave, lane, acc, buf, next_row0, total_rows);
