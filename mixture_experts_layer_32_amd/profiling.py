@@ -16,7 +16,8 @@ and writes profiles/<workload>_kernels_trace.md (per-kernel durations) and
 profiles/<kernel>_<workload>_hbm.txt (HBM bytes per launch of the expert
 kernels, scaled by what the same counters read for a 1 GiB device copy;
 <kernel> is ffn_stream for the fused FC1 + FC2 kernel, gemm_stream for the
-weight-streaming GEMMs and gemm_tiled for the grouped LDS-tiled ones; with
+weight-streaming GEMMs, gemm_grouped for the persistent bf16 grouped GEMM,
+gemm_fp8w for the fp8-weight one and gemm_tiled for the LDS-tiled one; with
 --tokens T the workload is named <workload>_T<T>).  --sweep-summary writes
 the table of a sweep over workloads and batches from their bench lines and
 HBM files.
@@ -38,7 +39,7 @@ ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide what the expert kernels read and write
 KERNEL_SOURCES = ("csrc/gemm_stream.hip", "csrc/ffn_stream.hip", "csrc/gemm_tiled.hip",
-                  "csrc/gemm_grouped.hip", "csrc/routing.hip",
+                  "csrc/gemm_grouped.hip", "csrc/gemm_fp8w.hip", "csrc/routing.hip",
                   "csrc/common.hpp", "csrc/kernels.hpp", "csrc/api.cpp")
 COPY_BYTES = 1 << 30  # bench.py --copy-calibration: 1 GiB read + 1 GiB written per launch
 
