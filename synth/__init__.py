@@ -108,11 +108,15 @@ def normal_fp8_rows(seed: int, tid: int, rows: int, cols: int, std: float, offse
     return q, s
 
 
-# OCP MX FP4 (E2M1) magnitudes of codes 0..7; codes 8..15 are their negatives
-_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+# Thresholds between neighbouring E2M1 magnitudes (0, 0.5, 1, 1.5, 2, 3, 4,
+# 6: codes 0..7, codes 8..15 their negatives).  A magnitude exactly at a
+# midpoint takes the even code: upwards at 0.75, 1.75 and 3.5 (codes 2, 4,
+# 6), downwards at 0.25, 1.25, 2.5 and 5 (codes 0, 2, 4, 6).
+_E2M1_UP = (0.75, 1.75, 3.5)
+_E2M1_DOWN = (0.25, 1.25, 2.5, 5.0)
 
 
-def mxfp4_quantize(v: np.ndarray):
+def mxfp4_quantize(v: np.ndarray, chunk_rows: int = 4096):
     """OCP MX quantisation of v [rows][cols] (cols a multiple of 32) to FP4
     E2M1 with one E8M0 scale per 32 consecutive elements of a row.
 
@@ -121,28 +125,31 @@ def mxfp4_quantize(v: np.ndarray):
     v / 2^X rounded to the nearest E2M1 value, ties to the even code,
     magnitudes above 6 saturated to 6.  Returns (packed [rows][cols/2]
     uint8, element 2j in the low nibble of byte j; scales [rows][cols/32]
-    uint8, the biased exponent X + 127).
+    uint8, the biased exponent X + 127).  Rows are processed in chunks.
     """
     v = np.asarray(v, np.float64)
     rows, cols = v.shape
     if cols % 32:
         raise ValueError("MXFP4 rows must hold whole blocks of 32")
-    blk = v.reshape(rows, cols // 32, 32)
-    amax = np.abs(blk).max(axis=2)
-    with np.errstate(divide="ignore"):
-        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
-    X = np.clip(X, -127, 127)
-    y = blk / np.ldexp(1.0, X.astype(np.int64))[..., None]
-    a = np.minimum(np.abs(y), 6.0)
-    dist = np.abs(a[..., None] - _E2M1)
-    k = np.argmin(dist, axis=-1)                     # lower code on a tie
-    km = np.minimum(k + 1, 7)
-    d_k = np.take_along_axis(dist, k[..., None], -1)[..., 0]
-    d_n = np.take_along_axis(dist, km[..., None], -1)[..., 0]
-    k = np.where((k % 2 == 1) & (km != k) & (d_n == d_k), km, k)   # ties to the even code
-    code = (k + 8 * (y < 0) * (k > 0)).astype(np.uint8).reshape(rows, cols)
-    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    return packed, (X + 127).astype(np.uint8)
+    packed = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    for r0 in range(0, rows, chunk_rows):
+        blk = v[r0:r0 + chunk_rows].reshape(-1, cols // 32, 32)
+        amax = np.abs(blk).max(axis=2)
+        with np.errstate(divide="ignore"):
+            X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+        X = np.clip(X, -127, 127)
+        y = blk / np.ldexp(1.0, X.astype(np.int64))[..., None]
+        a = np.abs(y)
+        k = np.zeros(a.shape, np.uint8)      # nearest code; past 6 it stays 7
+        for t in _E2M1_UP:
+            k += a >= t
+        for t in _E2M1_DOWN:
+            k += a > t
+        code = (k + 8 * ((y < 0) & (k > 0))).astype(np.uint8).reshape(-1, cols)
+        packed[r0:r0 + chunk_rows] = code[:, 0::2] | (code[:, 1::2] << 4)
+        scales[r0:r0 + chunk_rows] = (X + 127).astype(np.uint8)
+    return packed, scales
 
 
 def normal_mxfp4_rows(seed: int, tid: int, rows: int, cols: int, std: float, offset: int = 0):
