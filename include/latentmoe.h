@@ -95,12 +95,14 @@ typedef enum {
  *   STREAM - weight-streaming grouped GEMMs, FC1 then FC2 (few rows per
  *            expert: the decode regime, bound by reading the expert weights);
  *   FUSED  - FC1 and FC2 in one kernel, the activated rows kept on chip
- *            (decode regime, bf16, m <= 1536, at least one expert per compute
- *            unit; an expert with more than 48 rows takes several passes);
+ *            (decode regime, bf16 tokens, bf16 or MXFP4 experts, m <= 1536,
+ *            at least one expert per compute unit; an expert with more than
+ *            48 rows takes several passes);
  *   TILED  - LDS-tiled MFMA grouped GEMMs (many rows per expert: prefill).
  * Every choice computes the same function; forcing one is for tests and
- * measurements.  FUSED needs bf16 activations, bf16 or MXFP4 experts and
- * m <= 1536; MXFP4 experts never run TILED (AUTO streams them). */
+ * measurements.  FUSED needs bf16 activations, bf16 or MXFP4 experts,
+ * m <= 1536, and each expert weight array (all N experts) below 2 GiB;
+ * MXFP4 experts never run TILED (AUTO streams them, or runs FUSED). */
 typedef enum {
   LMOE_EXPERTS_AUTO = 0,
   LMOE_EXPERTS_TILED = 1,

@@ -213,11 +213,13 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
     default:
       p.stream = fp8 ? mean <= kFp8StreamMaxRowsPerExpert : mean <= kStreamMaxRowsPerExpert;
       // one expert per resident workgroup: the fused kernel fills the chip
-      // only with at least one expert per compute unit
-      // (bf16 weights: with MXFP4 the fused kernel is issue-bound and no
-      // faster than the streaming one, measured 371 against 371 us)
-      p.fused = p.stream && bf16 && mean <= kFusedMaxRowsPerExpert &&
-                lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m)) &&
+      // only with at least one expert per compute unit (bf16 or MXFP4
+      // weights, bf16 tokens)
+      p.fused = p.stream && (bf16 || (fp4 && c.act_dtype == LMOE_BF16)) &&
+                mean <= kFusedMaxRowsPerExpert &&
+                lmoe::ffn_stream_fits(static_cast<int>(c.n_experts), static_cast<int>(c.l),
+                                      static_cast<int>(c.m), c.activation == LMOE_ACT_SWIGLU,
+                                      fp4) &&
                 c.n_experts >= kComputeUnits;
   }
   if (fp4 && !p.stream) p.stream = true;  // MXFP4 weights: no tiled kernel
@@ -391,10 +393,12 @@ lmoe_status latentmoe_create(const lmoe_config* cfg, lmoe_handle** out) {
   if (c.expert_kernel == LMOE_EXPERTS_FUSED &&
       !(c.act_dtype == LMOE_BF16 &&
         (c.expert_dtype == LMOE_BF16 || c.expert_dtype == LMOE_MXFP4_E2M1) &&
-        lmoe::ffn_stream_fits(static_cast<int>(c.l), static_cast<int>(c.m))))
+        lmoe::ffn_stream_fits(static_cast<int>(c.n_experts), static_cast<int>(c.l),
+                              static_cast<int>(c.m), c.activation == LMOE_ACT_SWIGLU,
+                              c.expert_dtype == LMOE_MXFP4_E2M1)))
     return fail(LMOE_ERR_UNSUPPORTED,
-                "create: the fused expert kernel needs bf16 activations, bf16 or MXFP4 experts "
-                "and m <= 1536");
+                "create: the fused expert kernel needs bf16 activations, bf16 or MXFP4 experts, "
+                "m <= 1536 and each expert weight array below 2 GiB");
   lmoe_handle* h = new (std::nothrow) lmoe_handle;
   if (!h) return fail(LMOE_ERR_ALLOC, "create: out of host memory");
   h->cfg = c;

@@ -7,10 +7,12 @@
 // the latent width l, with the squared-ReLU activation of Table 2).  With
 // SwiGLU experts W1 holds 2m rows, up-projection and gate rows interleaved,
 // and H[i] = up_i * SiLU(gate_i): FC1 streams twice the rows.  With MXFP4
-// weights (E2M1 pairs, an E8M0 scale per 32 elements) a lane takes 16
-// consecutive elements of a row per stage (one 8-byte load and its block's
-// scale byte) and widens them to two bf16 MFMA operands; the token and H
-// fragments then take the matching reduction indices.
+// weights (E2M1 pairs, an E8M0 scale per 32 elements) a lane loads 32
+// consecutive elements of a row (16 bytes, one scale block, and that
+// block's scale byte) for two stages, a double stage of 128 elements, and
+// widens 16 of them per stage to two bf16 MFMA operands; the staged token
+// chunks and the H fragments take the matching reduction indices.  (One
+// 8-byte piece per stage, half as many bytes per request, ran 1.4x slower.)
 //
 // With a few dozen token rows per expert both GEMMs are bound by streaming
 // the expert weights from HBM.  Writing H out and reading it back, as two
@@ -23,7 +25,11 @@
 //    fills the LDS); experts blockIdx.x, blockIdx.x + gridDim.x, ...
 //  - A stage is 64 reduction elements.  Each wave streams 16 * NWB weight
 //    rows into registers in the MFMA operand layout, 4 lanes side by side on
-//    64 contiguous bytes of a row, WD stages ahead of the one multiplied.
+//    64 contiguous bytes of a row, WD stages ahead of the one multiplied
+//    (MXFP4: two double stages ahead).
+//  - One buffer resource per weight array (all experts) and 32-bit offsets:
+//    per-expert resources for the current and the next unit overflowed the
+//    scalar registers into lanes of a vector register.
 //  - FC1's token rows are gathered through token_of and staged through LDS
 //    two stages ahead (double-buffered, one barrier per FC1 stage).  FC2's
 //    operand is H itself: the waves run through FC2 without barriers until
@@ -61,6 +67,11 @@ constexpr int kNLD = kNS;                      // 16-byte weight loads per n-blo
 constexpr int kWD = 3;               // weight stages in flight ahead
 // registers rotate: weights modulo kWD + 1 stages, staged token rows modulo 2
 constexpr int kP = (kWD + 1) % 2 == 0 ? kWD + 1 : 2 * (kWD + 1);
+// MXFP4: a lane's 16-byte weight piece is 32 elements (one scale block) and
+// serves two stages (a double stage); weights run two double stages ahead
+// in four register sets
+constexpr int kWD4 = 4;
+constexpr int kP4 = 8;
 constexpr int kMaxM = 1536;                    // hidden width that fits in LDS
 constexpr int kAChunks = kRows * (kKE / 8);    // staged token chunks per stage (384)
 
@@ -69,9 +80,7 @@ struct FfnUnit {
   int valid;         // 0: past the last expert
   int gs, cnt;       // first grouped row of the expert and its row count
   int p0, rows;      // this pass's first row (within the expert) and its rows
-  BufRsrc w1, w2;    // the expert's weight matrices
-  BufRsrc s1, s2;    // MXFP4: their block scales
-  uint32_t a_off;       // this thread's staged token chunk, or out of range
+  uint32_t a_off;    // this thread's staged token chunk, or out of range
 
   __device__ __forceinline__ void assign(const FfnUnit& o) {
     e = o.e;
@@ -80,27 +89,26 @@ struct FfnUnit {
     cnt = o.cnt;
     p0 = o.p0;
     rows = o.rows;
-    w1 = o.w1;
-    w2 = o.w2;
-    s1 = o.s1;
-    s2 = o.s2;
     a_off = o.a_off;
   }
 };
 
 // Weight registers of one stage: bf16 rows (kNLD 16-byte chunks per n-block),
-// or MXFP4 rows (one 8-byte piece and its scale byte per n-block)
+// or of one MXFP4 double stage (a 16-byte piece and its scale byte per n-block)
 struct WStageBf16 {
   u32x4 b[kNWB][kNLD];
 };
 struct WStageFp4 {
-  u32x2 b[kNWB];
+  u32x4 b[kNWB];
   uint32_t s[kNWB];
 };
 
 template <bool GLU, bool FP4>
 __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   using WS = std::conditional_t<FP4, WStageFp4, WStageBf16>;
+  constexpr int KWD = FP4 ? kWD4 : kWD;      // weight stages in flight ahead
+  constexpr int KP = FP4 ? kP4 : kP;         // unrolled stages (register rotation period)
+  constexpr int NSLOT = FP4 ? 4 : kWD + 1;   // weight register sets
   __shared__ u32x4 Hs[kRows * kMaxM / 8];  // H, 16-byte chunk c of row r at c ^ (r & 7)
   __shared__ u32x4 As[2][kAChunks];        // FC1 token stages, chunk c of row r at c ^ ((r >> 1) & 7)
 
@@ -110,12 +118,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   const int fr = lane & 15, fq = lane >> 4;
   const int L = p.l, M = p.m;
   const int N1 = GLU ? 2 * M : M;            // FC1 weight rows (H columns x 2 with SwiGLU)
-  const int mh = (M + kKE - 1) / kKE * kKE;  // H row length: m rounded up to a stage
+  // H row length: m rounded up to a stage (MXFP4: to a double stage)
+  constexpr int kRound = FP4 ? 2 * kKE : kKE;
+  const int mh = (M + kRound - 1) / kRound * kRound;
   const int hcpr = mh / 8;                   // 16-byte chunks per H row
-  const int s1 = (L + kKE - 1) / kKE;        // FC1 stages (reduction over l)
+  const int s1 = (L + kRound - 1) / kRound * (kRound / kKE);  // FC1 stages (reduction over l)
   const int s2 = mh / kKE;                   // FC2 stages (reduction over m)
-  const int s1p = (s1 + kP - 1) / kP * kP;
-  const int s2p = (s2 + kP - 1) / kP * kP;
+  const int s1p = (s1 + KP - 1) / KP * KP;
+  const int s2p = (s2 + KP - 1) / KP * KP;
   const int t1 = (N1 + kTileN - 1) / kTileN; // FC1 tiles (of W1 rows)
   const int t2 = (L + kTileN - 1) / kTileN;  // FC2 tiles (Y columns)
   const uint32_t rb1 = FP4 ? static_cast<uint32_t>(L) / 2u : static_cast<uint32_t>(L) * 2u;  // W1 row bytes
@@ -125,8 +135,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   const uint32_t a_row_bytes = static_cast<uint32_t>(p.lda) * 2u;
   const BufRsrc a_rsrc = make_rsrc(p.A, (uint64_t)p.a_nrows * p.lda * 2u);
   const BufRsrc goff_rsrc = make_rsrc(p.g_off, (uint64_t)(p.G + 1) * sizeof(int32_t));
-  const uint8_t* const w1g = static_cast<const uint8_t*>(p.W1);
-  const uint8_t* const w2g = static_cast<const uint8_t*>(p.W2);
+  // one resource per weight (and scale) array, all experts; an expert's
+  // matrix starts at e times its size (the launch keeps every array below
+  // 2 GiB, so offsets stay 32-bit and below kOutOfRange)
+  const uint32_t wm1 = static_cast<uint32_t>(N1) * rb1;   // bytes of one W1 matrix
+  const uint32_t wm2 = static_cast<uint32_t>(L) * rb2;
+  const uint32_t sm1 = static_cast<uint32_t>(N1) * sb1;   // MXFP4: bytes of its scales
+  const uint32_t sm2 = static_cast<uint32_t>(L) * sb2;
+  const BufRsrc w1r = make_rsrc(p.W1, (uint64_t)p.G * wm1);
+  const BufRsrc w2r = make_rsrc(p.W2, (uint64_t)p.G * wm2);
+  const BufRsrc s1r = make_rsrc(p.W1_mx, FP4 ? (uint64_t)p.G * sm1 : 0u);
+  const BufRsrc s2r = make_rsrc(p.W2_mx, FP4 ? (uint64_t)p.G * sm2 : 0u);
   uint16_t* const Y = static_cast<uint16_t*>(p.Y);
   const int nl = wave * (kNWB * 16) + fr;    // weight row of n-block 0 within a tile
   const int ar = tid >> 3, ac = tid & 7;     // staged token chunk of this thread
@@ -136,13 +155,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   auto set_expert = [&](FfnUnit& u, int e) {
     u.e = e;
     u.valid = e < p.G;
-    const int64_t ee = u.valid ? e : 0;
-    u.w1 = make_rsrc(w1g + ee * N1 * rb1, (uint64_t)N1 * rb1);
-    u.w2 = make_rsrc(w2g + ee * L * rb2, (uint64_t)L * rb2);
-    if constexpr (FP4) {
-      u.s1 = make_rsrc(p.W1_mx + ee * N1 * sb1, (uint64_t)N1 * sb1);
-      u.s2 = make_rsrc(p.W2_mx + ee * L * sb2, (uint64_t)L * sb2);
-    }
     u.gs = 0;
     u.cnt = 0;
     u.p0 = 0;
@@ -175,8 +187,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   auto issue_rows = [&](const FfnUnit& u) {
     tok = (a_thread && ar < u.rows) ? p.a_rows[u.gs + u.p0 + ar] : 0;
   };
+  // a thread's staged chunk ac of a stage: chunk ac of its 64 elements, or
+  // with MXFP4 (a double stage covers 128 elements, lane fq of an n-block
+  // holds elements 32 fq .. 32 fq + 31 of it, 16 per stage) chunk
+  // 4 (ac / 2) + ac % 2 of the double stage, plus 2 in its second stage
+  const uint32_t a_chunk = FP4 ? 4u * (ac >> 1) + (ac & 1) : static_cast<uint32_t>(ac);
   auto take_rows = [&](FfnUnit& u) {
-    u.a_off = (a_thread && ar < u.rows) ? static_cast<uint32_t>(tok) * a_row_bytes + 16u * ac
+    u.a_off = (a_thread && ar < u.rows) ? static_cast<uint32_t>(tok) * a_row_bytes + 16u * a_chunk
                                         : kOutOfRange;
   };
 
@@ -200,48 +217,58 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
     return false;
   };
 
-  // weight chunks of stage ks of tile t of GEMM ph
+  // weight chunks of stage ks of tile t of GEMM ph (MXFP4: of the double
+  // stage that starts at the even stage ks)
   auto load_w = [&](const FfnUnit& u, int ph, int t, int ks, bool live, WS& ws) {
     const int N = ph == 0 ? N1 : L;
     const uint32_t rb = ph == 0 ? rb1 : rb2;
-    const bool lv = live && ks < (ph == 0 ? s1 : s2);
+    const bool lv = live && u.valid && ks < (ph == 0 ? s1 : s2);
+    const uint32_t ue = u.valid ? static_cast<uint32_t>(u.e) : 0u;
     if constexpr (FP4) {
-      // elements 16 fq .. 16 fq + 15 of the stage: 8 bytes, one scale block
+      // elements 32 fq .. 32 fq + 31 of the double stage: 16 bytes, scale
+      // block 4 j + fq of the row
+      const uint32_t j = static_cast<uint32_t>(ks) >> 1;
       const uint32_t sb = ph == 0 ? sb1 : sb2;
-      const uint32_t so = static_cast<uint32_t>(ks) * (kKE / 2) + 8u * fq;
-      const uint32_t ss = static_cast<uint32_t>(ks) * (kKE / 32) + (fq >> 1);
+      const uint32_t wbase = ue * (ph == 0 ? wm1 : wm2) + 64u * j + 16u * fq;
+      const uint32_t sbase = ue * (ph == 0 ? sm1 : sm2) + 4u * j + fq;
+      const bool in_k = 128u * j + 32u * fq < static_cast<uint32_t>(ph == 0 ? L : M);
 #pragma unroll
       for (int nb = 0; nb < kNWB; ++nb) {
         const int n = t * kTileN + nl + nb * 16;
-        const bool in = lv && n < N;
-        const uint32_t vo = in ? static_cast<uint32_t>(n) * rb + so : kOutOfRange;
-        const uint32_t vs = in ? static_cast<uint32_t>(n) * sb + ss : kOutOfRange;
-        ws.b[nb] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(ph == 0 ? u.w1 : u.w2,
-                                                        static_cast<int>(vo), 0, 0));
-        ws.s[nb] = buffer_load_byte(ph == 0 ? u.s1 : u.s2, vs);
+        const bool in = lv && in_k && n < N;
+        const uint32_t vo = in ? wbase + static_cast<uint32_t>(n) * rb : kOutOfRange;
+        const uint32_t vs = in ? sbase + static_cast<uint32_t>(n) * sb : kOutOfRange;
+        ws.b[nb] = buffer_load_chunk(ph == 0 ? w1r : w2r, vo, 0u);
+        ws.s[nb] = buffer_load_byte(ph == 0 ? s1r : s2r, vs);
       }
     } else {
-      const uint32_t so = static_cast<uint32_t>(ks) * (kKE * 2) + 16u * fq;
+      const uint32_t so = ue * (ph == 0 ? wm1 : wm2) + static_cast<uint32_t>(ks) * (kKE * 2) + 16u * fq;
 #pragma unroll
       for (int nb = 0; nb < kNWB; ++nb) {
         const int n = t * kTileN + nl + nb * 16;
         const uint32_t vo = (lv && n < N) ? static_cast<uint32_t>(n) * rb + so : kOutOfRange;
         if (ph == 0) {
 #pragma unroll
-          for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(u.w1, vo + 64u * j, 0u);
+          for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(w1r, vo + 64u * j, 0u);
         } else {
 #pragma unroll
-          for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(u.w2, vo + 64u * j, 0u);
+          for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(w2r, vo + 64u * j, 0u);
         }
       }
     }
   };
   // this thread's token chunk of FC1 stage ks (FC2 stages stage nothing)
   auto load_a = [&](const FfnUnit& u, int ph, int ks) -> u32x4 {
-    const bool in_k = ph == 0 && ks * kKE + ac * 8 < L;
-    return buffer_load_chunk(
-        a_rsrc, in_k ? u.a_off + static_cast<uint32_t>(ks) * (kKE * 2) : kOutOfRange, 0u);
+    uint32_t so, el;  // byte offset of the stage in a token row, element of the chunk
+    if constexpr (FP4) {
+      so = 256u * (static_cast<uint32_t>(ks) >> 1) + 32u * (ks & 1);
+      el = so / 2u + 8u * a_chunk;
+    } else {
+      so = static_cast<uint32_t>(ks) * (kKE * 2);
+      el = so / 2u + 8u * ac;
+    }
+    const bool in_k = ph == 0 && el < static_cast<uint32_t>(L);
+    return buffer_load_chunk(a_rsrc, in_k ? u.a_off + so : kOutOfRange, 0u);
   };
   auto store_a = [&](int buf, const u32x4& v) {
     if (a_thread) As[buf][ar * 8 + (ac ^ ((ar >> 1) & 7))] = v;
@@ -255,23 +282,32 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
 
   // one stage: weights first (rows n), token rows second, so that a lane
   // ends with D[n = 4 fq + v][row = fr] of each 16 x 16 block
-  auto compute = [&](int ph, int ks, int buf, const WS& ws) {
+  auto compute = [&](int ph, int ks, int buf, WS& ws) {
+    if constexpr (FP4) {
+      // the first stage of a double stage turns its scale bytes into floats
+      if ((ks & 1) == 0) {
+#pragma unroll
+        for (int nb = 0; nb < kNWB; ++nb) ws.s[nb] = __float_as_uint(e8m0_to_f32(ws.s[nb]));
+      }
+    }
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
       // chunk of the stage: reduction elements 32 s + 8 fq .. (bf16 weights),
-      // 16 fq + 8 s .. (MXFP4: a lane's 16 consecutive elements)
+      // or (MXFP4) elements 32 fq + 16 (ks % 2) + 8 s .. of the double stage:
+      // staged chunk 2 fq + s, H chunk hc of the row
       const int c = FP4 ? 2 * fq + s : 4 * s + fq;
+      const int hc = FP4 ? 16 * (ks >> 1) + 4 * fq + 2 * (ks & 1) + s : ks * 8 + c;
       u32x4 bfr[kNWB];
 #pragma unroll
       for (int nb = 0; nb < kNWB; ++nb) {
-        if constexpr (FP4) bfr[nb] = fp4x8_to_bf16x8(ws.b[nb][s], e8m0_to_f32(ws.s[nb]));
+        if constexpr (FP4) bfr[nb] = fp4x8_to_bf16x8(ws.b[nb][2 * (ks & 1) + s], __uint_as_float(ws.s[nb]));
         else bfr[nb] = ws.b[nb][s];
       }
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const int r = mb * 16 + fr;
         const u32x4 a = ph == 0 ? As[buf][r * 8 + (c ^ ((r >> 1) & 7))]
-                                : Hs[r * hcpr + ((ks * 8 + c) ^ (r & 7))];
+                                : Hs[r * hcpr + (hc ^ (r & 7))];
 #pragma unroll
         for (int nb = 0; nb < kNWB; ++nb) MmaBf16::mma(acc[mb][nb], bfr[nb], a);
       }
@@ -282,18 +318,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   FfnUnit cur, nxt;
   set_expert(cur, blockIdx.x);
   if (!cur.valid) return;
-  WS bw[kWD + 1];
+  WS bw[NSLOT];
   u32x4 ra[2];
   // its first weight stages depend on the expert alone
+  constexpr int kStep = FP4 ? 2 : 1;
 #pragma unroll
-  for (int i = 0; i < kWD; ++i) load_w(cur, 0, 0, i, true, bw[i]);
+  for (int i = 0; i < KWD; i += kStep) load_w(cur, 0, 0, i, true, bw[i / kStep]);
   issue_bounds(cur);
   take_bounds(cur);
   if (cur.cnt <= 0) {  // no rows: the first expert with rows takes the prefetch
     find_rows(cur);
     if (!cur.valid) return;
 #pragma unroll
-    for (int i = 0; i < kWD; ++i) load_w(cur, 0, 0, i, true, bw[i]);
+    for (int i = 0; i < KWD; i += kStep) load_w(cur, 0, 0, i, true, bw[i / kStep]);
   }
   issue_rows(cur);
   take_rows(cur);
@@ -319,9 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
       const int nt = ph == 0 ? t1 : t2;
       const int sp = ph == 0 ? s1p : s2p;
       for (int t = 0; t < nt; ++t) {
-        for (int ks0 = 0; ks0 < sp; ks0 += kP) {
+        for (int ks0 = 0; ks0 < sp; ks0 += KP) {
 #pragma unroll
-          for (int u = 0; u < kP; ++u) {
+          for (int u = 0; u < KP; ++u) {
             const int ks = ks0 + u;
             // the next unit, read during the first three stages of this one
             // (its loads start in this unit's last kWD stages)
@@ -346,12 +383,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
               }
             }
             ++q;
-            // weights of the stage kWD ahead, token rows of the stage 2 ahead
-            {
+            // weights of the stage KWD ahead (MXFP4: at even stages, the
+            // double stage KWD ahead), token rows of the stage 2 ahead
+            if (u % kStep == 0) {
               int ph2, tt2, ks2;
-              const bool nx = advance(ph, t, ks, kWD, ph2, tt2, ks2);
-              if (nx) load_w(nxt, ph2, tt2, ks2, nxt.rows > 0, bw[(u + kWD) % (kWD + 1)]);
-              else load_w(cur, ph2, tt2, ks2, cur.rows > 0, bw[(u + kWD) % (kWD + 1)]);
+              const bool nx = advance(ph, t, ks, KWD, ph2, tt2, ks2);
+              WS& dst = bw[(u + KWD) / kStep % NSLOT];
+              if (nx) load_w(nxt, ph2, tt2, ks2, nxt.rows > 0, dst);
+              else load_w(cur, ph2, tt2, ks2, cur.rows > 0, dst);
             }
             {
               int ph2, tt2, ks2;
@@ -359,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
               ra[u % 2] = nx ? load_a(nxt, ph2, ks2) : load_a(cur, ph2, ks2);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (ks < (ph == 0 ? s1 : s2)) compute(ph, ks, u % 2, bw[u % (kWD + 1)]);
+            if (ks < (ph == 0 ? s1 : s2)) compute(ph, ks, u % 2, bw[u / kStep % NSLOT]);
             store_a((u + 1) % 2, ra[(u + 1) % 2]);
             // FC1 stages read the staged token rows; FC2 stages read only H,
             // so the waves run through FC2 unsynchronised until its last
@@ -405,24 +444,27 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
 
 }  // namespace
 
-bool ffn_stream_fits(int l, int m) {
-  return l > 0 && m > 0 && m <= kMaxM && l % 16 == 0 && m % 16 == 0;
+bool ffn_stream_fits(int G, int l, int m, bool glu, bool fp4) {
+  if (G < 1 || l <= 0 || m <= 0 || m > kMaxM || l % 16 || m % 16) return false;
+  if (fp4 && (l % 32 || m % 32)) return false;  // whole MX scale blocks per row
+  // each weight array (all experts) below 2 GiB: 32-bit offsets from one
+  // buffer resource per array
+  const uint64_t n1 = glu ? 2ull * m : uint64_t(m);
+  const uint64_t rb1 = fp4 ? uint64_t(l) / 2 : 2ull * l, rb2 = fp4 ? uint64_t(m) / 2 : 2ull * m;
+  return uint64_t(G) * n1 * rb1 < (1ull << 31) && uint64_t(G) * uint64_t(l) * rb2 < (1ull << 31);
 }
 
 int ffn_stream_rows() { return kRows; }
 
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s) {
-  if (!ffn_stream_fits(a.l, a.m) || a.G < 1 || !a.g_off || !a.a_rows || a.ldy % 4 ||
-      a.lda < a.l || (a.act != kActSqRelu && a.act != kActSwiGlu))
-    return hipErrorInvalidValue;
+  if (a.act != kActSqRelu && a.act != kActSwiGlu) return hipErrorInvalidValue;
   const bool glu = a.act == kActSwiGlu;
   const bool fp4 = a.W1_mx != nullptr;
-  // MXFP4: both scale arrays, whole scale blocks per row
-  if (fp4 && (!a.W2_mx || a.l % 32 || a.m % 32)) return hipErrorInvalidValue;
-  // 32-bit buffer offsets: token rows and one expert matrix stay below 2 GiB
-  if ((uint64_t)a.a_nrows * a.lda * 2u >= (1ull << 31) ||
-      (uint64_t)(glu ? 2 : 1) * a.m * a.l * 2u >= (1ull << 31))
+  if (!ffn_stream_fits(a.G, a.l, a.m, glu, fp4) || !a.g_off || !a.a_rows || a.ldy % 4 ||
+      a.lda < a.l || (fp4 && !a.W2_mx))
     return hipErrorInvalidValue;
+  // 32-bit buffer offsets: token rows stay below 2 GiB
+  if ((uint64_t)a.a_nrows * a.lda * 2u >= (1ull << 31)) return hipErrorInvalidValue;
   const int grid = std::min(a.G, device_compute_units());
   if (fp4) {
     if (glu) ffn_stream_kernel<true, true><<<dim3(grid), dim3(kThreads), 0, s>>>(a);

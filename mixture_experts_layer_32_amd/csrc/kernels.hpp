@@ -111,8 +111,9 @@ struct FfnArgs {
   const uint8_t* W1_mx = nullptr;
   const uint8_t* W2_mx = nullptr;
 };
-// Whether the fused kernel takes this shape (the hidden rows fit in LDS).
-bool ffn_stream_fits(int l, int m);
+// Whether the fused kernel takes this shape: the hidden rows fit in LDS,
+// and each weight array of all G experts stays below 2 GiB.
+bool ffn_stream_fits(int G, int l, int m, bool glu, bool fp4);
 int ffn_stream_rows();
 hipError_t launch_ffn_stream(const FfnArgs& a, hipStream_t s);
 

@@ -1,13 +1,14 @@
 """GPU parity of MXFP4 expert weights (OCP MX: E2M1 elements, E8M0 scale per
 32) against the fp64 oracle, through the C ABI.
 
-The streaming expert kernel widens each 16-byte chunk (32 elements, one
-scale block) to bf16 with the gfx950 scaled conversion, the fused decode
-FFN each 8-byte piece (16 elements); the oracle decodes the same codes
+Both expert kernels widen each 16-byte chunk (32 elements, one scale
+block) to bf16 with the gfx950 scaled conversion (the fused decode FFN
+spreads a chunk over two of its stages); the oracle decodes the same codes
 exactly.  Small cases: ragged shapes, 64- and 128-row passes,
 multi-pass experts under a skewed router, K not a multiple of the 128-element
 stage, SwiGLU with shared experts, the standard MoE, one token.  Full size:
-the iso-cost LatentMoE decode layer with MXFP4 experts on sampled tokens.
+the iso-cost LatentMoE decode layer with MXFP4 experts on sampled tokens,
+in the fused kernel (AUTO) and the streaming kernel.
 """
 import numpy as np
 import pytest
@@ -99,21 +100,32 @@ def _sample_tokens(T, n=48, seed=5):
     return np.array(sorted(s), np.int64)
 
 
-def test_full_size_mxfp4_decode():
+_FULL = {}
+
+
+@pytest.mark.parametrize("kernel", ["auto", "stream"])
+def test_full_size_mxfp4_decode(kernel):
+    """AUTO runs the fused kernel at this size; the streaming kernel forced."""
     wl = workload("latent_mxfp4_decode")
     spec, T = wl.spec, wl.T
-    w, x = _case(spec, T, seed=0)
-    g, layer = run_gpu(spec, w, x)
+    if not _FULL:
+        _FULL["wx"] = _case(spec, T, seed=0)
+    w, x = _FULL["wx"]
+    layer = pkg.LatentMoELayer(spec, expert_kernel=kernel)
+    assert layer.expert_regime(T) == ("fused" if kernel == "auto" else "stream")
+    g, layer = run_gpu(spec, w, x, layer=layer)
     print(wl.name, "regime", layer.expert_regime(T), flush=True)
     check_routing_structure(spec, g, T)
     st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T))
     print(wl.name, st, flush=True)
+    if kernel == "stream":
+        _FULL.clear()
 
 
 # the fused FC1 + FC2 kernel with MXFP4 weights, forced on shapes the
-# automatic choice would not give it: ragged l and m (last 64-element stage
-# partly past K), multi-pass experts with SwiGLU, the widest hidden layer,
-# a skewed router with empty experts
+# automatic choice would not give it: ragged l and m (the last 128-element
+# double stage partly past K), multi-pass experts with SwiGLU, the widest
+# hidden layer, a skewed router with empty experts
 FUSED = {
     "fused_ragged": (_mx(LayerSpec(d=1056, l=1056, m=544, n_experts=24, top_k=4,
                                    gating="sigmoid_topk_norm")), 200),
