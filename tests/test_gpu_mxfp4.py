@@ -106,6 +106,7 @@ _FULL = {}
 @pytest.mark.parametrize("kernel", ["auto", "stream"])
 def test_full_size_mxfp4_decode(kernel):
     """AUTO runs the fused kernel at this size; the streaming kernel forced."""
+    import mixture_experts_layer_32_amd as pkg
     wl = workload("latent_mxfp4_decode")
     spec, T = wl.spec, wl.T
     if not _FULL:
