@@ -282,7 +282,31 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
 
   // one stage: weights first (rows n), token rows second, so that a lane
   // ends with D[n = 4 fq + v][row = fr] of each 16 x 16 block
-  auto compute = [&](int ph, int ks, int buf, WS& ws) {
+  // nmb: 16-row token blocks of the pass that hold rows (the MFMAs of the
+  // empty ones are skipped; their accumulators stay zero)
+  auto compute = [&](int ph, int ks, int buf, WS& ws, int nmb) {
+    // token (FC1) or H (FC2) fragments: chunk of the stage for k-step s is
+    // reduction elements 32 s + 8 fq .. (bf16 weights), or (MXFP4) elements
+    // 32 fq + 16 (ks % 2) + 8 s .. of the double stage: staged chunk
+    // 2 fq + s, H chunk hc of the row
+    auto frag = [&](int s, int mb) -> u32x4 {
+      const int c = FP4 ? 2 * fq + s : 4 * s + fq;
+      const int hc = FP4 ? 16 * (ks >> 1) + 4 * fq + 2 * (ks & 1) + s : ks * 8 + c;
+      const int r = mb * 16 + fr;
+      return ph == 0 ? As[buf][r * 8 + (c ^ ((r >> 1) & 7))] : Hs[r * hcpr + (hc ^ (r & 7))];
+    };
+    // The fragments are read ahead of the MFMAs that use them, behind a
+    // scheduling fence: left alone, the scheduler sinks each read to its
+    // first use and waits for it there, six LDS round trips in a row per
+    // stage.  MXFP4 reads the whole stage at once; bf16 (whose weight
+    // registers leave less room) one k-step at a time.
+    constexpr int kAhead = FP4 ? kNS : 1;
+    u32x4 af[kNS][kMB];
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) af[s][mb] = frag(s, mb);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (FP4) {
       // the first stage of a double stage turns its scale bytes into floats
       if ((ks & 1) == 0) {
@@ -292,11 +316,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
     }
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
-      // chunk of the stage: reduction elements 32 s + 8 fq .. (bf16 weights),
-      // or (MXFP4) elements 32 fq + 16 (ks % 2) + 8 s .. of the double stage:
-      // staged chunk 2 fq + s, H chunk hc of the row
-      const int c = FP4 ? 2 * fq + s : 4 * s + fq;
-      const int hc = FP4 ? 16 * (ks >> 1) + 4 * fq + 2 * (ks & 1) + s : ks * 8 + c;
+      if (s >= kAhead) {
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) af[s][mb] = frag(s, mb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       u32x4 bfr[kNWB];
 #pragma unroll
       for (int nb = 0; nb < kNWB; ++nb) {
@@ -305,11 +329,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
       }
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
-        const int r = mb * 16 + fr;
-        const u32x4 a = ph == 0 ? As[buf][r * 8 + (c ^ ((r >> 1) & 7))]
-                                : Hs[r * hcpr + (hc ^ (r & 7))];
+        if (mb > 0 && mb >= nmb) break;
 #pragma unroll
-        for (int nb = 0; nb < kNWB; ++nb) MmaBf16::mma(acc[mb][nb], bfr[nb], a);
+        for (int nb = 0; nb < kNWB; ++nb) MmaBf16::mma(acc[mb][nb], bfr[nb], af[s][mb]);
       }
     }
   };
@@ -352,6 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
 
   for (;;) {
     int q = 0;  // stage of this unit (a unit has at least 4 stages)
+#pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
       const int nt = ph == 0 ? t1 : t2;
       const int sp = ph == 0 ? s1p : s2p;
@@ -398,7 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
               ra[u % 2] = nx ? load_a(nxt, ph2, ks2) : load_a(cur, ph2, ks2);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (ks < (ph == 0 ? s1 : s2)) compute(ph, ks, u % 2, bw[u / kStep % NSLOT]);
+            if (ks < (ph == 0 ? s1 : s2))
+              compute(ph, ks, u % 2, bw[u / kStep % NSLOT], (cur.rows + 15) >> 4);
             store_a((u + 1) % 2, ra[(u + 1) % 2]);
             // FC1 stages read the staged token rows; FC2 stages read only H,
             // so the waves run through FC2 unsynchronised until its last
