@@ -94,13 +94,13 @@ struct FfnUnit {
 };
 
 // Weight registers of one stage: bf16 rows (kNLD 16-byte chunks per n-block),
-// or of one MXFP4 double stage (a 16-byte piece and its scale byte per n-block)
+// or of one MXFP4 double stage (a 16-byte piece per n-block; the scales
+// come in groups of four double stages, see load_sg)
 struct WStageBf16 {
   u32x4 b[kNWB][kNLD];
 };
 struct WStageFp4 {
   u32x4 b[kNWB];
-  uint32_t s[kNWB];
 };
 
 template <bool GLU, bool FP4>
@@ -228,18 +228,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
       // elements 32 fq .. 32 fq + 31 of the double stage: 16 bytes, scale
       // block 4 j + fq of the row
       const uint32_t j = static_cast<uint32_t>(ks) >> 1;
-      const uint32_t sb = ph == 0 ? sb1 : sb2;
       const uint32_t wbase = ue * (ph == 0 ? wm1 : wm2) + 64u * j + 16u * fq;
-      const uint32_t sbase = ue * (ph == 0 ? sm1 : sm2) + 4u * j + fq;
       const bool in_k = 128u * j + 32u * fq < static_cast<uint32_t>(ph == 0 ? L : M);
 #pragma unroll
       for (int nb = 0; nb < kNWB; ++nb) {
         const int n = t * kTileN + nl + nb * 16;
         const bool in = lv && in_k && n < N;
         const uint32_t vo = in ? wbase + static_cast<uint32_t>(n) * rb : kOutOfRange;
-        const uint32_t vs = in ? sbase + static_cast<uint32_t>(n) * sb : kOutOfRange;
         ws.b[nb] = buffer_load_chunk(ph == 0 ? w1r : w2r, vo, 0u);
-        ws.s[nb] = buffer_load_byte(ph == 0 ? s1r : s2r, vs);
       }
     } else {
       const uint32_t so = ue * (ph == 0 ? wm1 : wm2) + static_cast<uint32_t>(ks) * (kKE * 2) + 16u * fq;
@@ -254,6 +250,41 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
 #pragma unroll
           for (int j = 0; j < kNLD; ++j) ws.b[nb][j] = buffer_load_chunk(w2r, vo + 64u * j, 0u);
         }
+      }
+    }
+  };
+  // MXFP4 block scales of a group of four double stages (eight stages, the
+  // first one ks) of tile t of GEMM ph.  Lane fq of row n needs byte
+  // 4 i + fq of the group's 16 (double stage 4 g + i) and keeps it in byte
+  // fq of dword i.  Where the group's bytes are 16-byte aligned (scale rows
+  // a multiple of 16 bytes, aligned array) every lane loads all 16 with one
+  // request per row: a byte load per lane and double stage cost as many
+  // requests as the weights themselves.  Otherwise four byte loads per lane.
+  // Bytes past the row's K / 32 blocks belong to weights that read as zero
+  // and are masked where the scales are decoded.
+  const bool sgv1 = sb1 % 16u == 0 && (reinterpret_cast<uintptr_t>(p.W1_mx) & 15u) == 0;
+  const bool sgv2 = sb2 % 16u == 0 && (reinterpret_cast<uintptr_t>(p.W2_mx) & 15u) == 0;
+  auto load_sg = [&](const FfnUnit& u, int ph, int t, int ks, bool live, u32x4* dst) {
+    const int N = ph == 0 ? N1 : L;
+    const uint32_t sb = ph == 0 ? sb1 : sb2;
+    const bool lv = live && u.valid && ks < (ph == 0 ? s1 : s2);
+    const uint32_t ue = u.valid ? static_cast<uint32_t>(u.e) : 0u;
+    const uint32_t base = ue * (ph == 0 ? sm1 : sm2) + 16u * (static_cast<uint32_t>(ks) >> 3);
+    const BufRsrc r = ph == 0 ? s1r : s2r;
+    if (ph == 0 ? sgv1 : sgv2) {
+#pragma unroll
+      for (int nb = 0; nb < kNWB; ++nb) {
+        const int n = t * kTileN + nl + nb * 16;
+        const uint32_t vo = (lv && n < N) ? base + static_cast<uint32_t>(n) * sb : kOutOfRange;
+        dst[nb] = buffer_load_chunk(r, vo, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < kNWB; ++nb) {
+        const int n = t * kTileN + nl + nb * 16;
+        const uint32_t vo = (lv && n < N) ? base + static_cast<uint32_t>(n) * sb + fq : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[nb][i] = buffer_load_byte(r, vo + 4u * i) << (8u * fq);
       }
     }
   };
@@ -284,7 +315,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   // ends with D[n = 4 fq + v][row = fr] of each 16 x 16 block
   // nmb: 16-row token blocks of the pass that hold rows (the MFMAs of the
   // empty ones are skipped; their accumulators stay zero)
-  auto compute = [&](int ph, int ks, int buf, WS& ws, int nmb) {
+  u32x4 sgc[kNWB], sgn[kNWB];  // MXFP4 scales: current and next group
+  float dsc[kNWB];              // MXFP4: scales of the current double stage
+  auto compute = [&](int ph, int ks, int u, int buf, WS& ws, int nmb) {
     // token (FC1) or H (FC2) fragments: chunk of the stage for k-step s is
     // reduction elements 32 s + 8 fq .. (bf16 weights), or (MXFP4) elements
     // 32 fq + 16 (ks % 2) + 8 s .. of the double stage: staged chunk
@@ -308,10 +341,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
       for (int mb = 0; mb < kMB; ++mb) af[s][mb] = frag(s, mb);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FP4) {
-      // the first stage of a double stage turns its scale bytes into floats
-      if ((ks & 1) == 0) {
+      // the first stage of a double stage decodes its scale bytes (u is the
+      // stage within the group, ks = u modulo 8); blocks past K scale by 0
+      if ((u & 1) == 0) {
+        const bool in_k = 128 * (ks >> 1) + 32 * fq < (ph == 0 ? L : M);
 #pragma unroll
-        for (int nb = 0; nb < kNWB; ++nb) ws.s[nb] = __float_as_uint(e8m0_to_f32(ws.s[nb]));
+        for (int nb = 0; nb < kNWB; ++nb) {
+          const uint32_t e = __builtin_amdgcn_ubfe(sgc[nb][(u >> 1) & 3], 8u * fq, 8u);
+          dsc[nb] = in_k ? e8m0_to_f32(e) : 0.f;
+        }
       }
     }
 #pragma unroll
@@ -324,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
       u32x4 bfr[kNWB];
 #pragma unroll
       for (int nb = 0; nb < kNWB; ++nb) {
-        if constexpr (FP4) bfr[nb] = fp4x8_to_bf16x8(ws.b[nb][2 * (ks & 1) + s], __uint_as_float(ws.s[nb]));
+        if constexpr (FP4) bfr[nb] = fp4x8_to_bf16x8(ws.b[nb][2 * (ks & 1) + s], dsc[nb]);
         else bfr[nb] = ws.b[nb][s];
       }
 #pragma unroll
@@ -346,6 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
   constexpr int kStep = FP4 ? 2 : 1;
 #pragma unroll
   for (int i = 0; i < KWD; i += kStep) load_w(cur, 0, 0, i, true, bw[i / kStep]);
+  if constexpr (FP4) load_sg(cur, 0, 0, 0, true, sgn);
   issue_bounds(cur);
   take_bounds(cur);
   if (cur.cnt <= 0) {  // no rows: the first expert with rows takes the prefetch
@@ -353,6 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
     if (!cur.valid) return;
 #pragma unroll
     for (int i = 0; i < KWD; i += kStep) load_w(cur, 0, 0, i, true, bw[i / kStep]);
+    if constexpr (FP4) load_sg(cur, 0, 0, 0, true, sgn);
   }
   issue_rows(cur);
   take_rows(cur);
@@ -406,6 +446,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
               }
             }
             ++q;
+            // MXFP4: a group of eight stages starts; its scales were loaded
+            // eight stages ago, the next group's are loaded now
+            if constexpr (FP4) {
+              static_assert(KP == 8, "a scale group is one unrolled iteration");
+              if (u == 0) {
+#pragma unroll
+                for (int nb = 0; nb < kNWB; ++nb) sgc[nb] = sgn[nb];
+                int ph2, tt2, ks2;
+                const bool nx = advance(ph, t, ks, KP, ph2, tt2, ks2);
+                if (nx) load_sg(nxt, ph2, tt2, ks2, nxt.rows > 0, sgn);
+                else load_sg(cur, ph2, tt2, ks2, cur.rows > 0, sgn);
+              }
+            }
             // weights of the stage KWD ahead (MXFP4: at even stages, the
             // double stage KWD ahead), token rows of the stage 2 ahead
             if (u % kStep == 0) {
@@ -422,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_stream_kernel(FfnArgs p) {
             }
             __builtin_amdgcn_sched_barrier(0);
             if (ks < (ph == 0 ? s1 : s2))
-              compute(ph, ks, u % 2, bw[u / kStep % NSLOT], (cur.rows + 15) >> 4);
+              compute(ph, ks, u, u % 2, bw[u / kStep % NSLOT], (cur.rows + 15) >> 4);
             store_a((u + 1) % 2, ra[(u + 1) % 2]);
             // FC1 stages read the staged token rows; FC2 stages read only H,
             // so the waves run through FC2 unsynchronised until its last
