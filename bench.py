@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HEADLINE = "latent_prefill_zipf"
-SUITE = ("latent_prefill_zipf", "tiny", "std_decode", "latent_decode", "latent_fp8_sparse")
+SUITE = ("latent_prefill_zipf", "tiny", "std_decode", "latent_decode", "latent_fp8_sparse",
+         "latent_mxfp4_decode")
 
 
 def log(msg):

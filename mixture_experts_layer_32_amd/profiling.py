@@ -21,8 +21,9 @@ gemm_fp8w for the fp8-weight one and gemm_tiled for the LDS-tiled one; with
 --tokens T the workload is named <workload>_T<T>).  --sweep-summary writes
 the table of a sweep over workloads and batches from their bench lines and
 HBM files.
-The HBM file records a hash of the kernel sources; bench.py reports its
-traffic only while the sources still hash the same.
+The HBM file records a hash of the sources its kernel depends on (its own
+file, the shared headers, the host planner and the routing); bench.py
+reports its traffic only while they still hash the same.
 """
 from __future__ import annotations
 
@@ -38,15 +39,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide what the expert kernels read and write
-KERNEL_SOURCES = ("csrc/gemm_stream.hip", "csrc/ffn_stream.hip", "csrc/gemm_tiled.hip",
-                  "csrc/gemm_grouped.hip", "csrc/gemm_fp8w.hip", "csrc/routing.hip",
-                  "csrc/common.hpp", "csrc/kernels.hpp", "csrc/api.cpp")
+# sources an expert kernel's HBM traffic depends on: its own file, the shared
+# headers, the host planner (tiles, grids) and the routing (row order)
+COMMON_SOURCES = ("csrc/common.hpp", "csrc/kernels.hpp", "csrc/api.cpp", "csrc/routing.hip")
+KIND_SOURCE = {"ffn_stream": "csrc/ffn_stream.hip", "gemm_stream": "csrc/gemm_stream.hip",
+               "gemm_tiled": "csrc/gemm_tiled.hip", "gemm_grouped": "csrc/gemm_grouped.hip",
+               "gemm_fp8w": "csrc/gemm_fp8w.hip"}
 COPY_BYTES = 1 << 30  # bench.py --copy-calibration: 1 GiB read + 1 GiB written per launch
 
 
-def sources_hash() -> str:
+def sources_hash(kind: str) -> str:
+    """Hash of the sources the traffic of expert kernel `kind` depends on."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in COMMON_SOURCES + (KIND_SOURCE[kind],):
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -162,8 +167,8 @@ def write_trace_md(workload: str, trace_dir: str, bench_json: str | None, out: s
         f.write("\n".join(lines) + "\n")
 
 
-def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cwrite: str,
-                  trace_dir: str | None, out: str, tokens: int = 0):
+def write_hbm_txt(workload: str, kind: str, fetch_dir: str, write_dir: str, cfetch: str,
+                  cwrite: str, trace_dir: str | None, out: str, tokens: int = 0):
     # factor: true KiB per counted KiB, from the copy's known 1 GiB each way
     cf, cw = copy_reading(cfetch, "FETCH_SIZE"), copy_reading(cwrite, "WRITE_SIZE")
     ff, fw = (COPY_BYTES / 1024) / cf, (COPY_BYTES / 1024) / cw
@@ -188,7 +193,7 @@ def write_hbm_txt(workload: str, fetch_dir: str, write_dir: str, cfetch: str, cw
              " %.1f KiB per dispatch: scale factors %.4f and %.4f" % (cf, cw, ff, fw),
              "workload=%s" % workload,
              "tokens=%d" % tokens,
-             "sources_sha256=%s" % sources_hash(),
+             "sources_sha256=%s" % sources_hash(kind),
              "fetch_scale=%.6f" % ff,
              "write_scale=%.6f" % fw]
     for name, (fv, n) in sorted(fetch.items()):
@@ -232,7 +237,7 @@ def read_hbm(workload: str, stage: str, regime: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.strip().split("=", 1)
                 kv[k] = v
-    if kv.get("sources_sha256") != sources_hash():
+    if kv.get("sources_sha256") != sources_hash(REGIME_KERNEL[regime]):
         return None
     v = kv.get("%s_hbm_bytes" % stage)
     return float(v) if v is not None else None
@@ -409,8 +414,9 @@ def main():
         if len(kinds) != 1:
             raise RuntimeError("expected one expert kernel kind, found %s" % sorted(kinds))
         wl = a.workload + ("_T%d" % a.tokens if a.tokens else "")
-        out = hbm_file(wl, kinds.pop())
-        write_hbm_txt(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out,
+        kind = kinds.pop()
+        out = hbm_file(wl, kind)
+        write_hbm_txt(a.workload, kind, a.fetch, a.write, a.copy_fetch, a.copy_write, a.trace, out,
                       a.tokens)
         print(out)
 
