@@ -726,7 +726,12 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.act = act1;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC1 (grouped, fp8)");
-    else if (p.grouped) LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC1 (grouped)");
+    else if (p.grouped) {
+      // H in 32-column blocks, so that FC2 loads each K stage of its rows as
+      // one contiguous block
+      a.c_kblock = static_cast<int>(p.copies);
+      LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC1 (grouped)");
+    }
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");
   }
   LMOE_MARK(4);
@@ -747,7 +752,10 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.act = lmoe::kActNone;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC2 (stream)");
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC2 (grouped, fp8)");
-    else if (p.grouped) LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC2 (grouped)");
+    else if (p.grouped) {
+      a.a_kblock = static_cast<int>(p.copies);   // H as FC1 wrote it
+      LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC2 (grouped)");
+    }
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");
   }
   LMOE_MARK(5);

@@ -147,7 +147,9 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* B = static_cast<const uint16_t*>(p.B) + (int64_t)t.g * p.b_gstride;
   const uint64_t a_rows_total = static_cast<uint64_t>(p.a_nrows);
-  const BufRsrc a_rsrc = make_rsrc(A, a_rows_total * p.lda * 2);
+  const BufRsrc a_rsrc = make_rsrc(A, !GATHER && p.a_kblock > 0
+                                         ? static_cast<uint64_t>(p.a_kblock) * p.K * 2
+                                         : a_rows_total * p.lda * 2);
   const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)p.N * p.ldb * 2);
 
   // this lane's chunk of each of its loads at K stage 0 (padding rows: an
@@ -161,7 +163,9 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
       const int c = (q % kGgBKC) ^ gg_swz(r);
       int64_t arow = -1;
       if (r < t.rows) arow = GATHER ? gg_rows[buf][r] : t.row0 + r;
-      d_off[j] = arow >= 0 ? static_cast<uint32_t>(arow * p.lda * 2) + c * 16u : kOutOfRange;
+      // row-major A: stage 0 of row arow; blocked A: the row's 64 bytes in block 0
+      const int64_t rb = GATHER || p.a_kblock == 0 ? p.lda * 2 : 64;
+      d_off[j] = arow >= 0 ? static_cast<uint32_t>(arow * rb) + c * 16u : kOutOfRange;
     } else {
       const int n = (q - ACH) / kGgBKC;
       const int c = ((q - ACH) % kGgBKC) ^ gg_swz(n);
@@ -171,15 +175,18 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   // stage kt -> ring buffer kt % kGgNS; stages past the end load zeros
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)gg_ring)));
+  // bytes between K stages: 32 elements of a row, or (blocked A) a block
+  const uint32_t a_step = GATHER || p.a_kblock == 0 ? kGgBK * 2u : static_cast<uint32_t>(p.a_kblock) * 64u;
   auto issue_part = [&](int kt, int j0, int j1) {
     const uint32_t s_ = ring_lds + static_cast<uint32_t>((kt % kGgNS) * kGgStage * 16);
     const uint32_t kb = static_cast<uint32_t>(kt) * (kGgBK * 2);
+    const uint32_t ka = static_cast<uint32_t>(kt) * a_step;
     const bool live = kt < nk;
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const bool is_a = (kGgNW * j + wave) * 64 < ACH;  // wave-uniform
       gg_dma(is_a ? a_rsrc : b_rsrc, s_ + static_cast<uint32_t>((kGgNW * j + wave) * 64 * 16),
-             live ? d_off[j] + kb : kOutOfRange);
+             live ? d_off[j] + (is_a ? ka : kb) : kOutOfRange);
     }
   };
   auto issue = [&](int kt) { issue_part(kt, 0, NDMA); };
@@ -288,11 +295,22 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   constexpr int RPS = 64 / CPR;                      // rows per wave store
   uint16_t* stg = reinterpret_cast<uint16_t*>(gg_ring + (kGgNS - 1) * kGgStage) + wave * 32 * kGgOutLd;
   const int ocol0 = (ACT == kActSwiGlu ? t.col0 / 2 : t.col0) + wn * OW;
-  const uint32_t ldc2 = static_cast<uint32_t>(p.ldc) * 2;
-  const BufRsrc c_rsrc = make_rsrc(p.C, static_cast<uint64_t>(t.row0 + t.rows) * ldc2);
   const int srow = lane / CPR, sch = lane % CPR;     // this lane's staged row / chunk
-  const uint32_t c_off = static_cast<uint32_t>(t.row0 + wm * WM + srow) * ldc2 +
-                         static_cast<uint32_t>(ocol0 + sch * 8) * 2;
+  // row-major C: a resource whose range ends at the tile's last row, rows
+  // past it dropped by the range check; blocked C (chunk in block
+  // (ocol0 + 8 sch) / 32): the whole array, rows past the tile offset out
+  // of range per lane
+  const bool cblk = p.c_kblock > 0;
+  const uint32_t ldc2 = cblk ? 64u : static_cast<uint32_t>(p.ldc) * 2;
+  const int out_cols = ACT == kActSwiGlu ? p.N / 2 : p.N;
+  const BufRsrc c_rsrc = make_rsrc(
+      p.C, cblk ? static_cast<uint64_t>(p.c_kblock) * out_cols * 2
+                : static_cast<uint64_t>(t.row0 + t.rows) * ldc2);
+  const int ccol = ocol0 + sch * 8;
+  const uint32_t c_off =
+      cblk ? static_cast<uint32_t>((ccol >> 5) * p.c_kblock + t.row0 + wm * WM + srow) * 64u +
+                 static_cast<uint32_t>(ccol & 31) * 2u
+           : static_cast<uint32_t>(t.row0 + wm * WM + srow) * ldc2 + static_cast<uint32_t>(ccol) * 2;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -315,8 +333,9 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
     for (int u = 0; u < 32 / RPS; ++u) {
       const u32x4 val =
           *reinterpret_cast<const u32x4*>(stg + (u * RPS + srow) * kGgOutLd + sch * 8);
-      __builtin_amdgcn_raw_buffer_store_b128(val, c_rsrc,
-                                             c_off + static_cast<uint32_t>(i * 32 + u * RPS) * ldc2,
+      const int r = wm * WM + i * 32 + u * RPS + srow;   // row within the tile
+      const uint32_t off = c_off + static_cast<uint32_t>(i * 32 + u * RPS) * ldc2;
+      __builtin_amdgcn_raw_buffer_store_b128(val, c_rsrc, !cblk || r < t.rows ? off : kOutOfRange,
                                              0, 0);
     }
   }
@@ -434,11 +453,17 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   if (a.g_off == nullptr || !gemm_grouped_fits(a.N, a.K, a.G) || a.b_scale || a.B2 || a.R ||
       a.b_mx || a.a_nrows <= 0 || a.max_rows <= 0)
     return hipErrorInvalidValue;
-  if (a.act == kActSwiGlu && a.ldc < a.N / 2) return hipErrorInvalidValue;
-  if (a.act != kActSwiGlu && a.ldc < a.N) return hipErrorInvalidValue;
+  const int out_cols = a.act == kActSwiGlu ? a.N / 2 : a.N;
+  if (a.c_kblock == 0 && a.ldc < out_cols) return hipErrorInvalidValue;
+  // blocked A: not gathered, every row of A in the blocks; blocked C: every
+  // row the launch writes in the blocks, whole 32-column blocks
+  if (a.a_kblock < 0 || a.c_kblock < 0 || (a.a_kblock > 0 && (a.a_rows || a.a_kblock < a.a_nrows)) ||
+      (a.c_kblock > 0 && (a.c_kblock < a.max_rows || out_cols % 32)))
+    return hipErrorInvalidValue;
   // 32-bit buffer offsets: A, one expert's B, C (max_rows bounds its rows)
-  if ((uint64_t)a.a_nrows * a.lda * 2 >= (1ull << 31) || (uint64_t)a.N * a.ldb * 2 >= (1ull << 31) ||
-      (uint64_t)a.max_rows * a.ldc * 2 >= (1ull << 31))
+  const uint64_t a_bytes = a.a_kblock ? (uint64_t)a.a_kblock * a.K * 2 : (uint64_t)a.a_nrows * a.lda * 2;
+  const uint64_t c_bytes = a.c_kblock ? (uint64_t)a.c_kblock * out_cols * 2 : (uint64_t)a.max_rows * a.ldc * 2;
+  if (a_bytes >= (1ull << 31) || (uint64_t)a.N * a.ldb * 2 >= (1ull << 31) || c_bytes >= (1ull << 31))
     return hipErrorInvalidValue;
   const int grid = (device_compute_units() + kNumXcd - 1) / kNumXcd * kNumXcd;
   const bool g = a.a_rows != nullptr;
