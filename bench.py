@@ -150,6 +150,12 @@ def measure(name, args, tokens=0, cpu=True, cpu_budget=10.0):
     log("bench: inputs on device in %.1f s" % (time.perf_counter() - t0))
 
     layer = pkg.LatentMoELayer(spec, expert_kernel=args.expert_kernel)
+    # the grouped expert kernel reads its weights from the banded copy, made
+    # once here like any weight preparation before serving (not timed)
+    packed = layer.expert_regime(T) == "grouped" and layer.packed_weights_size() > 0
+    if packed:
+        d_all["experts_packed"] = layer.pack_expert_weights(d_all)
+        torch.cuda.synchronize()
     cw = layer.weights_struct(d_all)
     x = d_all["x"]
     act = torch.float32 if spec.act_dtype == "f32" else torch.bfloat16
@@ -272,7 +278,8 @@ def measure(name, args, tokens=0, cpu=True, cpu_budget=10.0):
                    "n_shared": spec.n_shared, "m_shared": spec.m_shared,
                    "activation": spec.activation,
                    "shared_on_side_stream": overlap is not None,
-                   "expert_kernel": regime},
+                   "expert_kernel": regime,
+                   "expert_weights": "banded copy" if packed else "row-major"},
         "stage_ms": {k: round(v, 5) for k, v in stage_avg.items()},
         "latency_ms": {k: round(v, 5) for k, v in pct.items()},
         "roofline": roof,

@@ -39,7 +39,8 @@ EXPORTED = ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
             "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
             "latentmoe_timer_destroy", "latentmoe_status_string", "latentmoe_last_error",
             "latentmoe_expert_regime", "latentmoe_overlap_create", "latentmoe_overlap_destroy",
-            "latentmoe_forward_overlap", "latentmoe_forward_static")
+            "latentmoe_forward_overlap", "latentmoe_forward_static",
+            "latentmoe_packed_weights_size", "latentmoe_pack_expert_weights")
 
 
 class LmoeConfig(ctypes.Structure):
@@ -58,7 +59,8 @@ class LmoeWeights(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_shared1", ctypes.c_void_p), ("w_shared2", ctypes.c_void_p),
-                ("w1_mx", ctypes.c_void_p), ("w2_mx", ctypes.c_void_p)]
+                ("w1_mx", ctypes.c_void_p), ("w2_mx", ctypes.c_void_p),
+                ("experts_packed", ctypes.c_void_p)]
 
 
 class LmoeDebug(ctypes.Structure):
@@ -117,10 +119,14 @@ def lib():
             L.latentmoe_last_error.restype = ctypes.c_char_p
             L.latentmoe_expert_regime.argtypes = [vp, i64]
             L.latentmoe_expert_regime.restype = ctypes.c_char_p
+            L.latentmoe_packed_weights_size.argtypes = [vp]
+            L.latentmoe_packed_weights_size.restype = ctypes.c_size_t
+            L.latentmoe_pack_expert_weights.argtypes = [vp, ctypes.POINTER(LmoeWeights), vp,
+                                                        ctypes.c_size_t, vp]
             for f in ("latentmoe_create", "latentmoe_workspace_size", "latentmoe_forward",
                       "latentmoe_destroy", "latentmoe_timer_create", "latentmoe_timer_read",
                       "latentmoe_timer_destroy", "latentmoe_forward_overlap",
-                      "latentmoe_forward_static",
+                      "latentmoe_forward_static", "latentmoe_pack_expert_weights",
                       "latentmoe_overlap_create", "latentmoe_overlap_destroy"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -232,6 +238,28 @@ class LatentMoELayer:
     def expert_regime(self, T: int) -> str:
         return lib().latentmoe_expert_regime(self._h, T).decode()
 
+    def packed_weights_size(self) -> int:
+        """Bytes of the banded copy of W1 and W2 that the grouped expert
+        kernel reads (0: the layer's expert GEMMs never run there)."""
+        return int(lib().latentmoe_packed_weights_size(self._h))
+
+    def pack_expert_weights(self, weights: dict, stream=None):
+        """The banded copy of weights["w1"] and weights["w2"] as a device
+        uint8 tensor, written on the current (or given) stream.  Put it in
+        the weights dict as "experts_packed" for forward calls."""
+        torch = _torch()
+        n = self.packed_weights_size()
+        if n == 0:
+            raise LatentMoEError(-2, "this layer's expert GEMMs never run in the grouped kernel")
+        cw = self.weights_struct(weights)
+        dev = weights["w1"].device
+        buf = torch.empty((n,), dtype=torch.uint8, device=dev)
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        _check(lib().latentmoe_pack_expert_weights(self._h, ctypes.byref(cw),
+                                                   ctypes.c_void_p(buf.data_ptr()), n,
+                                                   ctypes.c_void_p(st.cuda_stream)))
+        return buf
+
     # ---- argument checks (shapes / dtypes of the device tensors)
     def _expect(self, name, t, shape, dtypes):
         torch = _torch()
@@ -285,6 +313,9 @@ class LatentMoELayer:
                                        (torch.float32,))
             cw.w2_scale = self._expect("w2_scale", w.get("w2_scale"), (s.n_experts, s.l),
                                        (torch.float32,))
+        if w.get("experts_packed") is not None:
+            cw.experts_packed = self._expect("experts_packed", w["experts_packed"],
+                                             (self.packed_weights_size(),), (torch.uint8,))
         S = getattr(s, "n_shared", 0)
         if S:
             hs = S * s.m_shared

@@ -419,6 +419,41 @@ lmoe_status latentmoe_workspace_size(const lmoe_handle* h, int64_t T, size_t* by
   return LMOE_OK;
 }
 
+size_t latentmoe_packed_weights_size(const lmoe_handle* h) {
+  if (!h) return 0;
+  const lmoe_config& c = h->cfg;
+  if (c.act_dtype != LMOE_BF16 || c.expert_dtype != LMOE_BF16) return 0;
+  const int64_t n1 = c.activation == LMOE_ACT_SWIGLU ? 2 * c.m : c.m;
+  if (!lmoe::gemm_grouped_fits(static_cast<int>(n1), static_cast<int>(c.l), static_cast<int>(c.n_experts)) ||
+      !lmoe::gemm_grouped_fits(static_cast<int>(c.l), static_cast<int>(c.m), static_cast<int>(c.n_experts)))
+    return 0;
+  return size_t(c.n_experts) * size_t(n1 * c.l + c.l * c.m) * 2;
+}
+
+lmoe_status latentmoe_pack_expert_weights(const lmoe_handle* h, const lmoe_weights* w, void* packed,
+                                          size_t packed_bytes, void* stream) {
+  if (!h || !w || !packed) return fail(LMOE_ERR_INVALID_ARG, "pack_expert_weights: NULL argument");
+  const size_t need = latentmoe_packed_weights_size(h);
+  if (need == 0)
+    return fail(LMOE_ERR_UNSUPPORTED, "pack_expert_weights: this layer's experts do not run in the "
+                "grouped kernel");
+  if (packed_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "pack_expert_weights: %zu bytes < required %zu", packed_bytes, need);
+  if (!w->w1 || !w->w2) return fail(LMOE_ERR_INVALID_ARG, "pack_expert_weights: NULL w1 or w2");
+  if (!aligned16(w->w1) || !aligned16(w->w2) || !aligned16(packed))
+    return fail(LMOE_ERR_INVALID_ARG, "pack_expert_weights: pointers must be 16-byte aligned");
+  const lmoe_config& c = h->cfg;
+  const int N = static_cast<int>(c.n_experts), l = static_cast<int>(c.l), m = static_cast<int>(c.m);
+  const int n1 = c.activation == LMOE_ACT_SWIGLU ? 2 * m : m;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* dst = static_cast<char*>(packed);
+  hipError_t e = lmoe::launch_pack_bands(w->w1, dst, N, n1, l, s);
+  if (e != hipSuccess) return hip_fail(e, "pack W1");
+  e = lmoe::launch_pack_bands(w->w2, dst + size_t(N) * n1 * l * 2, N, l, m, s);
+  if (e != hipSuccess) return hip_fail(e, "pack W2");
+  return LMOE_OK;
+}
+
 const char* latentmoe_expert_regime(const lmoe_handle* h, int64_t T) {
   if (!h || T < 0) return "invalid";
   const Plan p = make_plan(h->cfg, T);
@@ -535,7 +570,8 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
   if (ov && static_cast<hipStream_t>(stream) == ov->side)
     return fail(LMOE_ERR_INVALID_ARG, "forward: the side stream must differ from the call's stream");
   const void* ptrs[] = {x, out, w->w_router, w->w1, w->w2, w->w_down, w->w_up,
-                        shared ? w->w_shared1 : nullptr, shared ? w->w_shared2 : nullptr};
+                        shared ? w->w_shared1 : nullptr, shared ? w->w_shared2 : nullptr,
+                        w->experts_packed};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(LMOE_ERR_INVALID_ARG, "forward: pointers must be 16-byte aligned");
   const Plan p = make_plan(c, T);
@@ -728,8 +764,9 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC1 (grouped, fp8)");
     else if (p.grouped) {
       // H in 32-column blocks, so that FC2 loads each K stage of its rows as
-      // one contiguous block
+      // one contiguous block; W1 in 256-row bands when a packed copy is given
       a.c_kblock = static_cast<int>(p.copies);
+      if (w->experts_packed) { a.B = w->experts_packed; a.b_bands = 1; }
       LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC1 (grouped)");
     }
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC1 (tiled)");
@@ -754,6 +791,11 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC2 (grouped, fp8)");
     else if (p.grouped) {
       a.a_kblock = static_cast<int>(p.copies);   // H as FC1 wrote it
+      if (w->experts_packed) {                   // W2 follows W1 in the packed copy
+        const int n1 = glu ? 2 * m : m;
+        a.B = static_cast<const char*>(w->experts_packed) + size_t(N) * n1 * l * 2;
+        a.b_bands = 1;
+      }
       LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "FC2 (grouped)");
     }
     else LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.expert_tile, s), "FC2 (tiled)");

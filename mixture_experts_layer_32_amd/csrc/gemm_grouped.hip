@@ -32,6 +32,15 @@
 // chunk c of row r sits at c ^ ((r >> 2) & 3), so the 32 lanes reading one
 // fragment column touch distinct bank groups.
 //
+// A load instruction covers 16 rows x 64 bytes of a stage.  The load path
+// pays per row (cache line) touched more than per byte, so two operand
+// layouts put a stage's rows next to each other: B may come as the banded
+// copy of the weights (b_bands: 256-row bands stored as 32-column blocks,
+// so a weight tile's K stage is one contiguous 16 KB block), and FC1 writes
+// H in 32-column blocks over all rows (c_kblock) that FC2 reads the same
+// way (a_kblock).  Prefill FC1 / FC2: 1.68 / 1.64 ms row-major, 1.59 /
+// 1.34 ms with both.
+//
 // Each lane ends with 4 consecutive output columns per block row (the
 // MFMA computes the block transposed); one 32-row block row of the wave's
 // columns at a time is activated, rounded to bf16, staged in LDS and
@@ -39,6 +48,8 @@
 // 16 bytes to each of 32 rows per instruction, took several times longer).
 // The epilogue is kept short: buffer stores whose range ends at the tile's
 // last row (no per-row test) and a one-instruction ReLU.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -169,7 +180,10 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
     } else {
       const int n = (q - ACH) / kGgBKC;
       const int c = ((q - ACH) % kGgBKC) ^ gg_swz(n);
-      d_off[j] = static_cast<uint32_t>((int64_t)(t.col0 + n) * p.ldb * 2) + c * 16u;
+      // row-major B: stage 0 of row col0 + n; banded B: the tile's band,
+      // its first block, row n
+      d_off[j] = p.b_bands ? static_cast<uint32_t>((int64_t)t.col0 * p.K * 2 + n * 64) + c * 16u
+                           : static_cast<uint32_t>((int64_t)(t.col0 + n) * p.ldb * 2) + c * 16u;
     }
   }
   // stage kt -> ring buffer kt % kGgNS; stages past the end load zeros
@@ -177,9 +191,10 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)gg_ring)));
   // bytes between K stages: 32 elements of a row, or (blocked A) a block
   const uint32_t a_step = GATHER || p.a_kblock == 0 ? kGgBK * 2u : static_cast<uint32_t>(p.a_kblock) * 64u;
+  const uint32_t b_step = p.b_bands ? kGgBN * kGgBK * 2u : kGgBK * 2u;
   auto issue_part = [&](int kt, int j0, int j1) {
     const uint32_t s_ = ring_lds + static_cast<uint32_t>((kt % kGgNS) * kGgStage * 16);
-    const uint32_t kb = static_cast<uint32_t>(kt) * (kGgBK * 2);
+    const uint32_t kb = static_cast<uint32_t>(kt) * b_step;
     const uint32_t ka = static_cast<uint32_t>(kt) * a_step;
     const bool live = kt < nk;
 #pragma unroll
@@ -449,6 +464,39 @@ bool gemm_grouped_fits(int N, int K, int G) {
   return N > 0 && K > 0 && N % kGgBN == 0 && K % kGgBK == 0 && G >= 1 && G <= kGgMaxG;
 }
 
+namespace {
+
+// One 16-byte chunk (8 elements) per thread, grid-stride: source chunk i of
+// the row-major matrices is row n = (i / (K / 8)) % N of matrix g, chunk kc
+// = i % (K / 8); it goes to band n / 256, block kc / 4, row n % 256, chunk
+// kc % 4 of that block.
+__global__ __launch_bounds__(256) void pack_bands_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t chunks,
+                                                         int N, int K) {
+  const int64_t cpr = K / 8;                 // chunks per row
+  const int64_t per_g = static_cast<int64_t>(N) * cpr;
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < chunks;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t g = i / per_g, rem = i % per_g;
+    const int64_t n = rem / cpr, kc = rem % cpr;
+    const int64_t o = g * per_g + ((n / 256) * (K / 32) + kc / 4) * 1024 + (n % 256) * 4 + kc % 4;
+    dst[o] = src[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int K, hipStream_t s) {
+  if (!src || !dst || G < 1 || N < 1 || K < 1 || N % 256 || K % 32 ||
+      ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u))
+    return hipErrorInvalidValue;
+  const int64_t chunks = static_cast<int64_t>(G) * N * (K / 8);
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 65536);
+  pack_bands_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks, N, K);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   if (a.g_off == nullptr || !gemm_grouped_fits(a.N, a.K, a.G) || a.b_scale || a.B2 || a.R ||
       a.b_mx || a.a_nrows <= 0 || a.max_rows <= 0)
@@ -458,7 +506,8 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   // blocked A: not gathered, every row of A in the blocks; blocked C: every
   // row the launch writes in the blocks, whole 32-column blocks
   if (a.a_kblock < 0 || a.c_kblock < 0 || (a.a_kblock > 0 && (a.a_rows || a.a_kblock < a.a_nrows)) ||
-      (a.c_kblock > 0 && (a.c_kblock < a.max_rows || out_cols % 32)))
+      (a.c_kblock > 0 && (a.c_kblock < a.max_rows || out_cols % 32)) ||
+      (a.b_bands && a.ldb != a.K))
     return hipErrorInvalidValue;
   // 32-bit buffer offsets: A, one expert's B, C (max_rows bounds its rows)
   const uint64_t a_bytes = a.a_kblock ? (uint64_t)a.a_kblock * a.K * 2 : (uint64_t)a.a_nrows * a.lda * 2;

@@ -56,6 +56,9 @@ struct GemmArgs {
   // bytes per row, lda / ldc unused); 0 = row-major
   int a_kblock = 0;
   int c_kblock = 0;
+  // grouped kernel: B in bands of 256 rows, a band as its 32-column blocks
+  // one after another (256 x 32 elements each); ldb == K
+  int b_bands = 0;
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
@@ -80,6 +83,9 @@ int fp8w_block_m();
 // an expert's last row tile is 256, 128 or 64 rows high.  Needs N a multiple
 // of 256, K of 32, at most 2048 groups; g_tiles is not read.
 bool gemm_grouped_fits(int N, int K, int G);
+// The band layout of gemm_grouped's b_bands for G matrices of N x K
+// (row-major, contiguous): N a multiple of 256, K of 32.
+hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int K, hipStream_t s);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);
 
 // Compute units of the current device (queried once per device; 256 on

@@ -70,12 +70,16 @@ def to_f64(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu(spec, w_np, x_np, device="cuda:0", layer=None, overlap=None):
+def run_gpu(spec, w_np, x_np, device="cuda:0", layer=None, overlap=None, packed=False):
+    """One forward call through the C ABI; packed: with the banded copy of
+    the expert weights (latentmoe_pack_expert_weights) as well."""
     import torch
     import mixture_experts_layer_32_amd as pkg
     layer = layer or pkg.LatentMoELayer(spec)
     T = x_np.shape[0]
     dev = pkg.to_device(pkg.pack_gated(dict(w_np, x=x_np)), device)
+    if packed:
+        dev["experts_packed"] = layer.pack_expert_weights(dev)
     dbg = pkg.debug_buffers(spec, T, device)
     out = layer.forward(dev["x"], dev, debug=dbg, overlap=overlap)
     torch.cuda.synchronize()

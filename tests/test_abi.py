@@ -106,6 +106,36 @@ def test_create_rejects_unsupported_dtypes_and_sizes():
     assert _create(std)[0] == -1
 
 
+def test_packed_weights_size_and_argument_checks():
+    """The banded expert-weight copy exists for bf16 layers whose expert
+    GEMMs fit the grouped kernel (W1 and W2 row counts multiples of 256, l
+    and m of 32), as large as W1 + W2; its pack call checks its arguments on
+    the host before enqueuing anything."""
+    L = pkg.lib()
+    pre = workload("latent_prefill_zipf").spec
+    st, h = _create(pkg.make_config(pre))
+    assert st == 0
+    n = L.latentmoe_packed_weights_size(h)
+    assert n == 2 * pre.n_experts * (pre.m * pre.l + pre.l * pre.m)
+    w = pkg.LmoeWeights()
+    buf = ctypes.c_void_p(256)   # never dereferenced: each call fails before any launch
+    assert L.latentmoe_pack_expert_weights(h, ctypes.byref(w), None, n, None) == -1
+    assert L.latentmoe_pack_expert_weights(h, ctypes.byref(w), buf, n - 1, None) == -3
+    assert L.latentmoe_pack_expert_weights(h, ctypes.byref(w), buf, n, None) == -1  # NULL w1, w2
+    L.latentmoe_destroy(h)
+    glu = pre.replace(activation="swiglu")
+    st, h = _create(pkg.make_config(glu))
+    assert L.latentmoe_packed_weights_size(h) == 2 * glu.n_experts * (2 * glu.m * glu.l + glu.l * glu.m)
+    L.latentmoe_destroy(h)
+    for spec in (workload("latent_fp8_sparse").spec, workload("latent_mxfp4_decode").spec,
+                 workload("tiny").spec, pre.replace(m=2000), pre.replace(l=1008)):
+        st, h = _create(pkg.make_config(spec))
+        assert st == 0, spec
+        assert L.latentmoe_packed_weights_size(h) == 0, spec
+        assert L.latentmoe_pack_expert_weights(h, ctypes.byref(w), buf, 1 << 30, None) == -2
+        L.latentmoe_destroy(h)
+
+
 def test_create_checks_mxfp4_constraints():
     mx = LayerSpec(d=256, l=64, m=128, n_experts=16, top_k=4, expert_dtype="mxfp4_e2m1")
     st, h = _create(pkg.make_config(mx))

@@ -308,6 +308,38 @@ def test_grouped_kernel_matches_oracle(name):
     print(name, st, flush=True)
 
 
+@pytest.mark.parametrize("name", ["grouped_zipf", "grouped_swiglu", "grouped_std_moe",
+                                  "grouped_many_experts_zipf"])
+def test_grouped_packed_weights_bit_identical(name):
+    """The banded copy of W1 and W2 (latentmoe_pack_expert_weights) changes
+    only where the grouped kernel reads each weight stage: the outputs are
+    bit-identical to the row-major run, and match the oracle."""
+    import mixture_experts_layer_32_amd as pkg
+    spec, T = GROUPED[name]
+    layer = pkg.LatentMoELayer(spec)
+    assert layer.packed_weights_size() > 0 and layer.expert_regime(T) == "grouped"
+    w, x = _case(spec, T, seed=4)
+    a, _ = run_gpu(spec, w, x, layer=layer)
+    b, _ = run_gpu(spec, w, x, layer=layer, packed=True)
+    assert np.array_equal(a["out"], b["out"])
+    tok = None if T * spec.top_k * spec.m * spec.l <= 2e9 else _sample_tokens(T, n=200, seed=7)
+    st = check_against_oracle(spec, w, x, b, tokens=tok)
+    print(name, st, flush=True)
+
+
+def test_full_size_prefill_packed_weights_bit_identical():
+    """The prefill layer with the banded expert weights, as the benchmark
+    runs it: bit-identical to the row-major run (which the full-size test
+    above checks against the oracle)."""
+    wl = workload("latent_prefill_zipf")
+    spec, T = wl.spec, wl.T
+    w, x = _case(spec, T, seed=0)
+    a, layer = run_gpu(spec, w, x)
+    assert layer.expert_regime(T) == "grouped"
+    b, _ = run_gpu(spec, w, x, layer=layer, packed=True)
+    assert np.array_equal(a["out"], b["out"])
+
+
 # Sizes that select (256 x 256 dense, 128 x 256 grouped,
 # 128 x 128 dense) with ragged row and column tails, on sampled tokens.
 MID = {
