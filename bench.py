@@ -150,9 +150,10 @@ def measure(name, args, tokens=0, cpu=True, cpu_budget=10.0):
     log("bench: inputs on device in %.1f s" % (time.perf_counter() - t0))
 
     layer = pkg.LatentMoELayer(spec, expert_kernel=args.expert_kernel)
-    # the grouped expert kernel reads its weights from the banded copy, made
-    # once here like any weight preparation before serving (not timed)
-    packed = layer.expert_regime(T) == "grouped" and layer.packed_weights_size() > 0
+    # the grouped expert kernels (bf16, fp8) read their weights from the
+    # banded copy, made once here like any weight preparation before serving
+    # (not timed)
+    packed = layer.expert_regime(T) in ("grouped", "fp8w") and layer.packed_weights_size() > 0
     if packed:
         d_all["experts_packed"] = layer.pack_expert_weights(d_all)
         torch.cuda.synchronize()

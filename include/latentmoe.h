@@ -151,7 +151,7 @@ typedef struct {
   const uint8_t *w1_mx;     /* MXFP4 experts: E8M0 scales [N][m][l/32] of w1 ([N][m][l/2] bytes) */
   const uint8_t *w2_mx;     /* MXFP4 experts: E8M0 scales [N][l][m/32] of w2 ([N][l][m/2] bytes) */
   const void *experts_packed; /* optional: w1 and w2 as latentmoe_pack_expert_weights wrote
-                                 them; read by the grouped prefill kernel, NULL = w1, w2 */
+                                 them; read by the grouped bf16 and fp8 kernels, NULL = w1, w2 */
 } lmoe_weights;
 
 /* Per-stage GPU timing: an opaque object holding HIP events.  Attach one to
@@ -205,23 +205,28 @@ lmoe_status latentmoe_create(const lmoe_config *cfg, lmoe_handle **out);
 lmoe_status latentmoe_workspace_size(const lmoe_handle *h, int64_t T, size_t *bytes);
 
 /* Expert weights in a second layout, for the grouped expert GEMMs of large
- * batches (FC1 and FC2 of bf16 layers with N, l, m as the grouped kernel
- * takes them: W1's and W2's row counts multiples of 256, l and m multiples
- * of 32).  Each expert matrix is stored in bands of 256 rows, a band as its
- * 32-column blocks one after another, a block as 256 rows of 64 bytes: a
- * K stage of a 256-row weight tile is then one contiguous 16 KB block (the
- * row-major layout spreads it over 256 rows).  The expert FFN of Eq. (2) is
- * unchanged: results are bit-identical with and without the packed copy.
+ * batches: each expert matrix is stored in bands of rows, a band as its
+ * 64-byte column blocks one after another, a block as the band's rows of
+ * 64 bytes each.  bf16 experts (prefill; W1's and W2's row counts multiples
+ * of 256, l and m of 32): 256-row bands, so that a K stage of a 256-row
+ * weight tile is one contiguous 16 KB block instead of 256 row pieces.
+ * fp8 experts (l and m multiples of 64): 16-row bands, the rows that one
+ * wave of the fp8 kernel streams, so that each of its loads reads 1 KB in
+ * one piece.  The row scales stay where they are.  The expert FFN of
+ * Eq. (2) is unchanged: results are bit-identical with and without the
+ * packed copy.
  *
  * latentmoe_packed_weights_size: bytes of the packed copy (W1 then W2, as
- * large as the two matrices), or 0 when the layer's expert GEMMs never run
- * in the grouped kernel (then there is nothing to pack).
+ * large as the two matrices), or 0 when the layer's experts have no packed
+ * form (f32 or MXFP4 experts, or shapes the kernels above do not take).
  *
  * latentmoe_pack_expert_weights: writes the packed copy of w->w1 and w->w2
  * into `packed` (device memory owned by the caller, >= the size above,
  * 16-byte aligned, not overlapping them), enqueued on `stream`.  Pass it
  * as lmoe_weights.experts_packed to forward calls, together with w1 and w2
- * (the other expert kernels read those); keep it in step with w1 and w2.
+ * (the other expert kernels read those: the packed copy is read where a
+ * batch runs the grouped bf16 or the fp8 tiled expert kernel, see
+ * latentmoe_expert_regime); keep it in step with w1 and w2.
  * Returns UNSUPPORTED when the size is 0, WORKSPACE when packed_bytes is
  * too small, INVALID_ARG for NULL or misaligned pointers, HIP on a launch
  * error. */

@@ -419,15 +419,35 @@ lmoe_status latentmoe_workspace_size(const lmoe_handle* h, int64_t T, size_t* by
   return LMOE_OK;
 }
 
-size_t latentmoe_packed_weights_size(const lmoe_handle* h) {
-  if (!h) return 0;
-  const lmoe_config& c = h->cfg;
-  if (c.act_dtype != LMOE_BF16 || c.expert_dtype != LMOE_BF16) return 0;
+namespace {
+// Band height of the packed expert weights: 256 rows (bf16, the grouped
+// kernel's weight tile) or 16 (fp8, one n-block of the fp8 kernel); 0 = no
+// packed copy for this layer
+int packed_band_rows(const lmoe_config& c) {
+  if (c.act_dtype != LMOE_BF16) return 0;
   const int64_t n1 = c.activation == LMOE_ACT_SWIGLU ? 2 * c.m : c.m;
-  if (!lmoe::gemm_grouped_fits(static_cast<int>(n1), static_cast<int>(c.l), static_cast<int>(c.n_experts)) ||
-      !lmoe::gemm_grouped_fits(static_cast<int>(c.l), static_cast<int>(c.m), static_cast<int>(c.n_experts)))
-    return 0;
-  return size_t(c.n_experts) * size_t(n1 * c.l + c.l * c.m) * 2;
+  const int G = static_cast<int>(c.n_experts);
+  if (c.expert_dtype == LMOE_BF16)
+    return lmoe::gemm_grouped_fits(static_cast<int>(n1), static_cast<int>(c.l), G) &&
+                   lmoe::gemm_grouped_fits(static_cast<int>(c.l), static_cast<int>(c.m), G)
+               ? 256 : 0;
+  if (c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE)
+    return lmoe::gemm_fp8w_fits(static_cast<int>(n1), static_cast<int>(c.l), G) &&
+                   lmoe::gemm_fp8w_fits(static_cast<int>(c.l), static_cast<int>(c.m), G) &&
+                   c.l % 64 == 0 && c.m % 64 == 0
+               ? 16 : 0;
+  return 0;
+}
+size_t packed_elem_bytes(const lmoe_config& c) {
+  return c.expert_dtype == LMOE_FP8_E4M3_ROWSCALE ? 1 : 2;
+}
+}  // namespace
+
+size_t latentmoe_packed_weights_size(const lmoe_handle* h) {
+  if (!h || packed_band_rows(h->cfg) == 0) return 0;
+  const lmoe_config& c = h->cfg;
+  const int64_t n1 = c.activation == LMOE_ACT_SWIGLU ? 2 * c.m : c.m;
+  return size_t(c.n_experts) * size_t(n1 * c.l + c.l * c.m) * packed_elem_bytes(c);
 }
 
 lmoe_status latentmoe_pack_expert_weights(const lmoe_handle* h, const lmoe_weights* w, void* packed,
@@ -445,11 +465,12 @@ lmoe_status latentmoe_pack_expert_weights(const lmoe_handle* h, const lmoe_weigh
   const lmoe_config& c = h->cfg;
   const int N = static_cast<int>(c.n_experts), l = static_cast<int>(c.l), m = static_cast<int>(c.m);
   const int n1 = c.activation == LMOE_ACT_SWIGLU ? 2 * m : m;
+  const int eb = static_cast<int>(packed_elem_bytes(c)), R = packed_band_rows(c);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* dst = static_cast<char*>(packed);
-  hipError_t e = lmoe::launch_pack_bands(w->w1, dst, N, n1, l, s);
+  hipError_t e = lmoe::launch_pack_bands(w->w1, dst, N, n1, l * eb, R, s);
   if (e != hipSuccess) return hip_fail(e, "pack W1");
-  e = lmoe::launch_pack_bands(w->w2, dst + size_t(N) * n1 * l * 2, N, l, m, s);
+  e = lmoe::launch_pack_bands(w->w2, dst + size_t(N) * n1 * l * eb, N, l, m * eb, R, s);
   if (e != hipSuccess) return hip_fail(e, "pack W2");
   return LMOE_OK;
 }
@@ -761,7 +782,10 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.g_active = active;
     a.act = act1;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC1 (stream)");
-    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC1 (grouped, fp8)");
+    else if (edt == lmoe::Dt::FP8) {
+      if (w->experts_packed) { a.B = w->experts_packed; a.b_bands = 1; }
+      LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC1 (grouped, fp8)");
+    }
     else if (p.grouped) {
       // H in 32-column blocks, so that FC2 loads each K stage of its rows as
       // one contiguous block; W1 in 256-row bands when a packed copy is given
@@ -788,7 +812,14 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.g_active = active;
     a.act = lmoe::kActNone;
     if (p.stream) LMOE_TRY(lmoe::launch_gemm_stream(a, adt, edt, adt, p.mb_max, s), "FC2 (stream)");
-    else if (edt == lmoe::Dt::FP8) LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC2 (grouped, fp8)");
+    else if (edt == lmoe::Dt::FP8) {
+      if (w->experts_packed) {
+        const int n1 = glu ? 2 * m : m;
+        a.B = static_cast<const char*>(w->experts_packed) + size_t(N) * n1 * l;
+        a.b_bands = 1;
+      }
+      LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC2 (grouped, fp8)");
+    }
     else if (p.grouped) {
       a.a_kblock = static_cast<int>(p.copies);   // H as FC1 wrote it
       if (w->experts_packed) {                   // W2 follows W1 in the packed copy

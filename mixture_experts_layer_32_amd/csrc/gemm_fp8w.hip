@@ -110,12 +110,16 @@ __global__ __launch_bounds__(kF8NT, 2) void gemm_fp8w_kernel(GemmArgs p) {
     a_off[j] = arow >= 0 ? static_cast<uint32_t>(arow * p.lda * 2) + 16u * c : kOutOfRange;
   }
   // weight rows of this lane: n-block j, row nrow; bytes 16 q4 .. of a stage
+  // (banded B: the n-block's 16 rows x 64 bytes of a stage are one block)
   uint32_t b_off[kF8NB];
 #pragma unroll
   for (int j = 0; j < kF8NB; ++j) {
     const int n = col0 + 64 * wave + 16 * j + nrow;
-    b_off[j] = n < p.N ? static_cast<uint32_t>(n * p.ldb) + 16u * q4 : kOutOfRange;
+    const uint32_t o = p.b_bands ? static_cast<uint32_t>((n - nrow) * p.ldb) + 64u * nrow + 16u * q4
+                                 : static_cast<uint32_t>(n * p.ldb) + 16u * q4;
+    b_off[j] = n < p.N ? o : kOutOfRange;
   }
+  const int b_step = p.b_bands ? 16 * kF8KS : kF8KS;   // bytes between K stages
 
   u32x4 areg[2][kF8ANum];       // token chunks, two stages
   u32x4 breg[kF8DB][kF8NB];     // weights [stage slot][n-block]
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kF8NT, 2) void gemm_fp8w_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < kF8NB; ++j) {
       const bool in = b_off[j] != kOutOfRange && kb + 16 * q4 < K;
-      dst[j] = buffer_load_chunk(b_rsrc, in ? b_off[j] + kb : kOutOfRange, 0u);
+      dst[j] = buffer_load_chunk(b_rsrc, in ? b_off[j] + kt * b_step : kOutOfRange, 0u);
     }
   };
   auto store_a = [&](const u32x4 (&src)[kF8ANum], int buf) {
@@ -272,6 +276,7 @@ hipError_t launch_gemm_fp8w(const GemmArgs& a, hipStream_t s) {
   if (a.g_off == nullptr || a.g_tiles == nullptr || !gemm_fp8w_fits(a.N, a.K, a.G) || a.B2 || a.R ||
       a.b_mx || a.a_nrows <= 0 || a.max_rows <= 0 || a.G < 1)
     return hipErrorInvalidValue;
+  if (a.b_bands && (a.ldb != a.K || a.K % kF8KS)) return hipErrorInvalidValue;
   if (a.act == kActSwiGlu && (a.N % 32 || a.ldc < a.N / 2)) return hipErrorInvalidValue;
   if (a.act != kActSwiGlu && a.ldc < a.N) return hipErrorInvalidValue;
   // 32-bit buffer offsets: A, one expert's weights, C (max_rows bounds its rows)

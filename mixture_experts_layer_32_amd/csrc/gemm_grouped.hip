@@ -466,34 +466,35 @@ bool gemm_grouped_fits(int N, int K, int G) {
 
 namespace {
 
-// One 16-byte chunk (8 elements) per thread, grid-stride: source chunk i of
-// the row-major matrices is row n = (i / (K / 8)) % N of matrix g, chunk kc
-// = i % (K / 8); it goes to band n / 256, block kc / 4, row n % 256, chunk
-// kc % 4 of that block.
+// One 16-byte chunk per thread, grid-stride: source chunk i of the
+// row-major matrices is row n = (i / cpr) % N of matrix g, chunk kc = i %
+// cpr (cpr chunks per row); it goes to band n / R, 64-byte block kc / 4,
+// row n % R, chunk kc % 4 of that block.
 __global__ __launch_bounds__(256) void pack_bands_kernel(const u32x4* __restrict__ src,
                                                          u32x4* __restrict__ dst, int64_t chunks,
-                                                         int N, int K) {
-  const int64_t cpr = K / 8;                 // chunks per row
+                                                         int N, int cpr, int R) {
   const int64_t per_g = static_cast<int64_t>(N) * cpr;
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < chunks;
        i += int64_t(gridDim.x) * blockDim.x) {
     const int64_t g = i / per_g, rem = i % per_g;
     const int64_t n = rem / cpr, kc = rem % cpr;
-    const int64_t o = g * per_g + ((n / 256) * (K / 32) + kc / 4) * 1024 + (n % 256) * 4 + kc % 4;
+    const int64_t o = g * per_g + ((n / R) * (cpr / 4) + kc / 4) * (4 * R) + (n % R) * 4 + kc % 4;
     dst[o] = src[i];
   }
 }
 
 }  // namespace
 
-hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int K, hipStream_t s) {
-  if (!src || !dst || G < 1 || N < 1 || K < 1 || N % 256 || K % 32 ||
-      ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u))
+hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int row_bytes, int band_rows,
+                             hipStream_t s) {
+  if (!src || !dst || G < 1 || N < 1 || row_bytes < 64 || band_rows < 1 || N % band_rows ||
+      row_bytes % 64 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u))
     return hipErrorInvalidValue;
-  const int64_t chunks = static_cast<int64_t>(G) * N * (K / 8);
+  const int64_t chunks = static_cast<int64_t>(G) * N * (row_bytes / 16);
   const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 65536);
   pack_bands_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks, N, K);
+      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks, N, row_bytes / 16,
+      band_rows);
   return hipGetLastError();
 }
 

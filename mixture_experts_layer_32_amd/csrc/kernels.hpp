@@ -56,8 +56,9 @@ struct GemmArgs {
   // bytes per row, lda / ldc unused); 0 = row-major
   int a_kblock = 0;
   int c_kblock = 0;
-  // grouped kernel: B in bands of 256 rows, a band as its 32-column blocks
-  // one after another (256 x 32 elements each); ldb == K
+  // grouped kernels: B in bands of rows, a band as its 64-byte column blocks
+  // one after another (launch_pack_bands; 256-row bands for the bf16
+  // grouped kernel, 16-row bands for the fp8 one); ldb == K
   int b_bands = 0;
 };
 
@@ -75,6 +76,8 @@ int tiled_block_m(int tile);
 // weights streamed into registers.  Needs N and K multiples of 16, at most
 // 2048 groups.
 bool gemm_fp8w_fits(int N, int K, int G);
+// b_bands: B in 16-row bands of 64-byte blocks (launch_pack_bands), K a
+// multiple of 64
 hipError_t launch_gemm_fp8w(const GemmArgs& a, hipStream_t s);
 int fp8w_block_m();
 
@@ -83,9 +86,13 @@ int fp8w_block_m();
 // an expert's last row tile is 256, 128 or 64 rows high.  Needs N a multiple
 // of 256, K of 32, at most 2048 groups; g_tiles is not read.
 bool gemm_grouped_fits(int N, int K, int G);
-// The band layout of gemm_grouped's b_bands for G matrices of N x K
-// (row-major, contiguous): N a multiple of 256, K of 32.
-hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int K, hipStream_t s);
+// Band layout of G row-major matrices of N rows x row_bytes: bands of
+// band_rows rows, a band as its 64-byte column blocks one after another (a
+// block = band_rows rows x 64 bytes).  gemm_grouped's b_bands: bf16, 256-row
+// bands; gemm_fp8w's: E4M3, 16-row bands.  N a multiple of band_rows,
+// row_bytes of 64.
+hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int row_bytes, int band_rows,
+                             hipStream_t s);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);
 
 // Compute units of the current device (queried once per device; 256 on

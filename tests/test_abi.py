@@ -109,8 +109,9 @@ def test_create_rejects_unsupported_dtypes_and_sizes():
 def test_packed_weights_size_and_argument_checks():
     """The banded expert-weight copy exists for bf16 layers whose expert
     GEMMs fit the grouped kernel (W1 and W2 row counts multiples of 256, l
-    and m of 32), as large as W1 + W2; its pack call checks its arguments on
-    the host before enqueuing anything."""
+    and m of 32) and for fp8 layers with l and m multiples of 64, as large
+    as W1 + W2; its pack call checks its arguments on the host before
+    enqueuing anything."""
     L = pkg.lib()
     pre = workload("latent_prefill_zipf").spec
     st, h = _create(pkg.make_config(pre))
@@ -127,7 +128,11 @@ def test_packed_weights_size_and_argument_checks():
     st, h = _create(pkg.make_config(glu))
     assert L.latentmoe_packed_weights_size(h) == 2 * glu.n_experts * (2 * glu.m * glu.l + glu.l * glu.m)
     L.latentmoe_destroy(h)
-    for spec in (workload("latent_fp8_sparse").spec, workload("latent_mxfp4_decode").spec,
+    f8 = workload("latent_fp8_sparse").spec           # fp8: 16-row bands, one byte each
+    st, h = _create(pkg.make_config(f8))
+    assert L.latentmoe_packed_weights_size(h) == f8.n_experts * (f8.m * f8.l + f8.l * f8.m)
+    L.latentmoe_destroy(h)
+    for spec in (f8.replace(l=2016), workload("latent_mxfp4_decode").spec,
                  workload("tiny").spec, pre.replace(m=2000), pre.replace(l=1008)):
         st, h = _create(pkg.make_config(spec))
         assert st == 0, spec

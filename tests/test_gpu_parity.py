@@ -327,15 +327,36 @@ def test_grouped_packed_weights_bit_identical(name):
     print(name, st, flush=True)
 
 
-def test_full_size_prefill_packed_weights_bit_identical():
-    """The prefill layer with the banded expert weights, as the benchmark
-    runs it: bit-identical to the row-major run (which the full-size test
-    above checks against the oracle)."""
-    wl = workload("latent_prefill_zipf")
+@pytest.mark.parametrize("spec,T", [
+    (LayerSpec(d=512, l=256, m=384, n_experts=8, top_k=2, gating="softmax_all",
+               expert_dtype="fp8_e4m3_rowscale"), 400),
+    (LayerSpec(d=256, l=128, m=192, n_experts=6, top_k=2, gating="softmax_topk",
+               activation="swiglu", expert_dtype="fp8_e4m3_rowscale"), 500),
+], ids=["fp8", "fp8_swiglu"])
+def test_fp8_packed_weights_bit_identical(spec, T):
+    """fp8 experts with the banded copy (16-row bands) in the fp8 kernel:
+    bit-identical to the row-major run, and matching the oracle."""
+    import mixture_experts_layer_32_amd as pkg
+    layer = pkg.LatentMoELayer(spec)
+    assert layer.packed_weights_size() > 0 and layer.expert_regime(T) == "fp8w"
+    w, x = _case(spec, T, seed=6)
+    a, _ = run_gpu(spec, w, x, layer=layer)
+    b, _ = run_gpu(spec, w, x, layer=layer, packed=True)
+    assert np.array_equal(a["out"], b["out"])
+    st = check_against_oracle(spec, w, x, b)
+    print(spec.activation, st, flush=True)
+
+
+@pytest.mark.parametrize("name", ["latent_prefill_zipf", "latent_fp8_sparse"])
+def test_full_size_packed_weights_bit_identical(name):
+    """The prefill and fp8 layers with the banded expert weights, as the
+    benchmark runs them: bit-identical to the row-major run (which the
+    full-size test above checks against the oracle)."""
+    wl = workload(name)
     spec, T = wl.spec, wl.T
     w, x = _case(spec, T, seed=0)
     a, layer = run_gpu(spec, w, x)
-    assert layer.expert_regime(T) == "grouped"
+    assert layer.expert_regime(T) in ("grouped", "fp8w")
     b, _ = run_gpu(spec, w, x, layer=layer, packed=True)
     assert np.array_equal(a["out"], b["out"])
 
