@@ -193,8 +193,8 @@ struct Plan {
   bool front = false;
   DensePlan front_plan;
   DensePlan sh1, sh2;   // shared experts: x Ws1^T (+ sqrelu), Hs Ws2^T (fp32 out)
-  size_t u, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v, partial,
-      Hs, R, partial_sh, active, total;
+  size_t u, ublk, logits, idx, gate, masks, base, counts, offsets, tiles, slot, token, H, Y, v,
+      partial, Hs, R, partial_sh, active, total;
 };
 
 Plan make_plan(const lmoe_config& c, int64_t T) {
@@ -295,6 +295,9 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.u = take(c.has_projections ? size_t(T) * c.l * ab : 0);
+  // grouped regime: u (or x) in 32-column blocks over all T rows, which
+  // FC1 gathers from (consecutive tokens of an expert then lie side by side)
+  p.ublk = take(p.grouped ? size_t(T) * c.l * ab : 0);
   p.logits = take(size_t(T) * c.n_experts * 4);
   p.idx = take(size_t(p.copies) * 4);
   p.gate = take(size_t(p.copies) * 4);
@@ -787,6 +790,12 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
       LMOE_TRY(lmoe::launch_gemm_fp8w(a, s), "FC1 (grouped, fp8)");
     }
     else if (p.grouped) {
+      // u in 32-column blocks over its T rows: the rows FC1 gathers for an
+      // expert are mostly consecutive tokens, whose K-stage pieces then sit
+      // side by side
+      void* ub = ws + p.ublk;
+      LMOE_TRY(lmoe::launch_pack_bands(u, ub, 1, Ti, l * ab, Ti, s), "u in blocks");
+      a.A = ub; a.a_kblock = Ti;
       // H in 32-column blocks, so that FC2 loads each K stage of its rows as
       // one contiguous block; W1 in 256-row bands when a packed copy is given
       a.c_kblock = static_cast<int>(p.copies);

@@ -158,9 +158,8 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* B = static_cast<const uint16_t*>(p.B) + (int64_t)t.g * p.b_gstride;
   const uint64_t a_rows_total = static_cast<uint64_t>(p.a_nrows);
-  const BufRsrc a_rsrc = make_rsrc(A, !GATHER && p.a_kblock > 0
-                                         ? static_cast<uint64_t>(p.a_kblock) * p.K * 2
-                                         : a_rows_total * p.lda * 2);
+  const BufRsrc a_rsrc = make_rsrc(A, p.a_kblock > 0 ? static_cast<uint64_t>(p.a_kblock) * p.K * 2
+                                                    : a_rows_total * p.lda * 2);
   const BufRsrc b_rsrc = make_rsrc(B, (uint64_t)p.N * p.ldb * 2);
 
   // this lane's chunk of each of its loads at K stage 0 (padding rows: an
@@ -175,7 +174,7 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
       int64_t arow = -1;
       if (r < t.rows) arow = GATHER ? gg_rows[buf][r] : t.row0 + r;
       // row-major A: stage 0 of row arow; blocked A: the row's 64 bytes in block 0
-      const int64_t rb = GATHER || p.a_kblock == 0 ? p.lda * 2 : 64;
+      const int64_t rb = p.a_kblock == 0 ? p.lda * 2 : 64;
       d_off[j] = arow >= 0 ? static_cast<uint32_t>(arow * rb) + c * 16u : kOutOfRange;
     } else {
       const int n = (q - ACH) / kGgBKC;
@@ -190,7 +189,7 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)gg_ring)));
   // bytes between K stages: 32 elements of a row, or (blocked A) a block
-  const uint32_t a_step = GATHER || p.a_kblock == 0 ? kGgBK * 2u : static_cast<uint32_t>(p.a_kblock) * 64u;
+  const uint32_t a_step = p.a_kblock == 0 ? kGgBK * 2u : static_cast<uint32_t>(p.a_kblock) * 64u;
   const uint32_t b_step = p.b_bands ? kGgBN * kGgBK * 2u : kGgBK * 2u;
   auto issue_part = [&](int kt, int j0, int j1) {
     const uint32_t s_ = ring_lds + static_cast<uint32_t>((kt % kGgNS) * kGgStage * 16);
@@ -506,7 +505,7 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   if (a.c_kblock == 0 && a.ldc < out_cols) return hipErrorInvalidValue;
   // blocked A: not gathered, every row of A in the blocks; blocked C: every
   // row the launch writes in the blocks, whole 32-column blocks
-  if (a.a_kblock < 0 || a.c_kblock < 0 || (a.a_kblock > 0 && (a.a_rows || a.a_kblock < a.a_nrows)) ||
+  if (a.a_kblock < 0 || a.c_kblock < 0 || (a.a_kblock > 0 && a.a_kblock < a.a_nrows) ||
       (a.c_kblock > 0 && (a.c_kblock < a.max_rows || out_cols % 32)) ||
       (a.b_bands && a.ldb != a.K))
     return hipErrorInvalidValue;

@@ -51,9 +51,9 @@ struct GemmArgs {
   // streaming kernel, sparse batches: g_active[0 .. g_tiles[G]) lists the
   // groups with rows, and only those are visited
   const int32_t* g_active = nullptr;
-  // grouped kernel: A (not gathered) or C stored in blocks of 32 columns,
-  // block b holding columns 32 b .. 32 b + 31 of rows 0 .. kblock - 1 (64
-  // bytes per row, lda / ldc unused); 0 = row-major
+  // grouped kernel: A (gathered or not) or C stored in blocks of 32
+  // columns, block b holding columns 32 b .. 32 b + 31 of rows 0 .. kblock - 1
+  // (64 bytes per row, lda / ldc unused); 0 = row-major
   int a_kblock = 0;
   int c_kblock = 0;
   // grouped kernels: B in bands of rows, a band as its 64-byte column blocks
