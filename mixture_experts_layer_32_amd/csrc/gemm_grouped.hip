@@ -349,8 +349,10 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
           *reinterpret_cast<const u32x4*>(stg + (u * RPS + srow) * kGgOutLd + sch * 8);
       const int r = wm * WM + i * 32 + u * RPS + srow;   // row within the tile
       const uint32_t off = c_off + static_cast<uint32_t>(i * 32 + u * RPS) * ldc2;
+      // non-temporal: the output is read again only by the next kernel
+      // (FC1: 2 % faster)
       __builtin_amdgcn_raw_buffer_store_b128(val, c_rsrc, !cblk || r < t.rows ? off : kOutOfRange,
-                                             0, 0);
+                                             0, kCpolNonTemporal);
     }
   }
 }
