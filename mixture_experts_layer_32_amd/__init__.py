@@ -239,8 +239,8 @@ class LatentMoELayer:
         return lib().latentmoe_expert_regime(self._h, T).decode()
 
     def packed_weights_size(self) -> int:
-        """Bytes of the banded copy of W1 and W2 that the grouped expert
-        kernel reads (0: the layer's expert GEMMs never run there)."""
+        """Bytes of the banded copy of W1 and W2 that the grouped bf16 and
+        fp8 expert kernels read (0: the layer's experts have none)."""
         return int(lib().latentmoe_packed_weights_size(self._h))
 
     def pack_expert_weights(self, weights: dict, stream=None):
@@ -250,11 +250,12 @@ class LatentMoELayer:
         torch = _torch()
         n = self.packed_weights_size()
         if n == 0:
-            raise LatentMoEError(-2, "this layer's expert GEMMs never run in the grouped kernel")
+            raise LatentMoEError(-2, "this layer's experts have no packed form")
         cw = self.weights_struct(weights)
         dev = weights["w1"].device
-        buf = torch.empty((n,), dtype=torch.uint8, device=dev)
         st = stream if stream is not None else torch.cuda.current_stream(dev)
+        with torch.cuda.stream(st):   # the buffer belongs to the stream that writes it
+            buf = torch.empty((n,), dtype=torch.uint8, device=dev)
         _check(lib().latentmoe_pack_expert_weights(self._h, ctypes.byref(cw),
                                                    ctypes.c_void_p(buf.data_ptr()), n,
                                                    ctypes.c_void_p(st.cuda_stream)))
