@@ -111,9 +111,10 @@ size_t act_bytes(const lmoe_config& c) { return c.act_dtype == LMOE_F32 ? 4 : 2;
 // Tile config and K split of one dense GEMM (M x N x K).  Large problems:
 // the 256 x 256 tile (bf16 operands and output) when it still gives one
 // workgroup per compute unit, else 128 x 128 when that gives one (two fit
-// per unit).  Small problems (decode-sized M): 64 x 64 tiles, K split until
-// about two workgroups per compute unit, keeping at least 8 K stages per
-// split.
+// per unit); fp32 output with 128 x 128 tiles for at least half the units:
+// that tile with K split.  Small problems (decode-sized M): 64 x 64 tiles,
+// K split until about two workgroups per compute unit, keeping at least 8 K
+// stages per split.
 struct DensePlan {
   int tile = 1;
   int splits = 1;
@@ -134,9 +135,25 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, size_t elem_bytes, bool bf
     d.tile = 0;
     return d;
   }
+  const int64_t stages = (K * int64_t(elem_bytes) + 127) / 128;
+  if (!bf16_out && 2 * t128 >= kComputeUnits) {
+    // fp32 output (partials that the consumer adds), 128 x 128 tiles short of
+    // one per compute unit: split K to the count that minimises waves x
+    // stages per split at two workgroups per unit (the fewest splits on a
+    // tie), at most 4 (every partial set is written once and read once);
+    // the 64 x 64 tile reads twice the operand bytes per flop here
+    d.tile = 0;
+    int64_t best = -1;
+    for (int64_t s = 1; s <= 4 && (s == 1 || stages / s >= 8); ++s) {
+      const int64_t waves = (t128 * s + 2 * kComputeUnits - 1) / (2 * kComputeUnits);
+      const int64_t cost = waves * ((stages + s - 1) / s);
+      if (best < 0 || cost < best) { best = cost; d.splits = static_cast<int>(s); }
+    }
+    if (N % 4) d.splits = 1;
+    return d;
+  }
   d.tile = 1;
   const int64_t small = ((M + 63) / 64) * ((N + 63) / 64);
-  const int64_t stages = (K * int64_t(elem_bytes) + 127) / 128;
   int64_t s = (2 * kComputeUnits + small - 1) / small;
   s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
   if (N % 4) s = 1;
@@ -184,6 +201,9 @@ struct Plan {
   int expert_tile = 0;  // tiled kernel tile config
   int tile_m = 128;
   DensePlan down, router, up;
+  // W_down / W_up in the persistent grouped kernel as one group of T rows
+  // (bf16, 256 x 256 tiles, at least one tile per compute unit, no residual)
+  bool down_grouped = false, up_grouped = false;
   // split-K partials left for the top-k kernel to add: the router logits,
   // and the down-projection when the router reads x (nothing needs u before)
   bool defer_u = false, defer_z = false;
@@ -249,6 +269,15 @@ Plan make_plan(const lmoe_config& c, int64_t T) {
     partial = std::max(partial, size_t(p.up.splits > 1 ? p.up.splits : 0) * T * c.d * 4);
   }
   p.router = plan_dense(T, c.n_experts, r_in, ab, false);  // fp32 logits
+  if (c.has_projections && ab == 2) {
+    const auto tiles256 = [&](int64_t n) { return ((T + 255) / 256) * (n / 256); };
+    p.down_grouped = p.down.tile == 2 && p.down.splits == 1 &&
+                     lmoe::gemm_grouped_fits(static_cast<int>(c.l), static_cast<int>(c.d), 1) &&
+                     tiles256(c.l) >= kComputeUnits;
+    p.up_grouped = p.up.tile == 2 && p.up.splits == 1 && c.n_shared == 0 &&
+                   lmoe::gemm_grouped_fits(static_cast<int>(c.d), static_cast<int>(c.l), 1) &&
+                   tiles256(c.d) >= kComputeUnits;
+  }
   p.defer_u = c.has_projections && c.router_input == LMOE_ROUTER_ON_X && p.down.splits > 1;
   p.defer_z = p.router.splits > 1;
   if (p.defer_u && p.defer_z) {
@@ -706,8 +735,14 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     lmoe::GemmArgs a;
     a.A = x; a.lda = d; a.B = w->w_down; a.ldb = d; a.C = u; a.ldc = l;
     a.M = Ti; a.N = l; a.K = d;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial, !p.defer_u),
-             "W_down GEMM");
+    if (p.down_grouped) {
+      a.a_nrows = Ti; a.max_rows = Ti;
+      LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "W_down GEMM (grouped)");
+    } else {
+      LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial,
+                                       !p.defer_u),
+               "W_down GEMM");
+    }
   }
   if (!p.front) {
     const bool lat = c.router_input == LMOE_ROUTER_ON_LATENT;
@@ -855,7 +890,12 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.A = v; a.lda = l; a.B = w->w_up; a.ldb = l; a.C = out; a.ldc = d;
     a.M = Ti; a.N = d; a.K = l;
     a.R = R; a.ldr = d;
-    LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.up.tile, s, p.up.splits, partial), "W_up GEMM");
+    if (p.up_grouped) {
+      a.a_nrows = Ti; a.max_rows = Ti;
+      LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "W_up GEMM (grouped)");
+    } else {
+      LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.up.tile, s, p.up.splits, partial), "W_up GEMM");
+    }
   }
   LMOE_MARK(7);
 

@@ -357,7 +357,9 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
   }
 }
 
-template <int ACT, bool GATHER>
+// DENSE: one group of p.M rows, no g_off (a dense GEMM on the same tiles;
+// its own instance, so that profiles tell it from the expert GEMMs)
+template <int ACT, bool GATHER, bool DENSE>
 __global__ __launch_bounds__(kGgNT, 1) void gemm_grouped_kernel(GemmArgs p) {
   __shared__ int s_pre[kGgMaxG + 1];         // items before expert e
   __shared__ int s_off[kGgMaxG + 1];         // g_off
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(kGgNT, 1) void gemm_grouped_kernel(GemmArgs p) {
     const int e = tid * 8 + u;
     v[u] = 0;
     if (e < G) {
-      const int o0 = p.g_off[e], o1 = p.g_off[e + 1];
+      const int o0 = DENSE ? 0 : p.g_off[e], o1 = DENSE ? p.M : p.g_off[e + 1];
       s_off[e] = o0;
       if (e == G - 1) s_off[G] = o1;
       v[u] = (o1 - o0 + kGgBM - 1) / kGgBM * ncol;
@@ -500,8 +502,12 @@ hipError_t launch_pack_bands(const void* src, void* dst, int G, int N, int row_b
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
-  if (a.g_off == nullptr || !gemm_grouped_fits(a.N, a.K, a.G) || a.b_scale || a.B2 || a.R ||
-      a.b_mx || a.a_nrows <= 0 || a.max_rows <= 0)
+  if (!gemm_grouped_fits(a.N, a.K, a.G) || a.b_scale || a.B2 || a.R || a.b_mx || a.a_nrows <= 0 ||
+      a.max_rows <= 0)
+    return hipErrorInvalidValue;
+  // dense: one group of M rows, A not gathered, every row of A and C there
+  if (a.g_off == nullptr &&
+      (a.G != 1 || a.M <= 0 || a.a_rows || a.a_nrows < a.M || a.max_rows < a.M))
     return hipErrorInvalidValue;
   const int out_cols = a.act == kActSwiGlu ? a.N / 2 : a.N;
   if (a.c_kblock == 0 && a.ldc < out_cols) return hipErrorInvalidValue;
@@ -518,15 +524,18 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const int grid = (device_compute_units() + kNumXcd - 1) / kNumXcd * kNumXcd;
   const bool g = a.a_rows != nullptr;
-  if (a.act == kActSqRelu) {
-    if (g) gemm_grouped_kernel<kActSqRelu, true><<<grid, kGgNT, 0, s>>>(a);
-    else gemm_grouped_kernel<kActSqRelu, false><<<grid, kGgNT, 0, s>>>(a);
+  if (a.g_off == nullptr) {
+    if (a.act != kActNone) return hipErrorInvalidValue;
+    gemm_grouped_kernel<kActNone, false, true><<<grid, kGgNT, 0, s>>>(a);
+  } else if (a.act == kActSqRelu) {
+    if (g) gemm_grouped_kernel<kActSqRelu, true, false><<<grid, kGgNT, 0, s>>>(a);
+    else gemm_grouped_kernel<kActSqRelu, false, false><<<grid, kGgNT, 0, s>>>(a);
   } else if (a.act == kActSwiGlu) {
-    if (g) gemm_grouped_kernel<kActSwiGlu, true><<<grid, kGgNT, 0, s>>>(a);
-    else gemm_grouped_kernel<kActSwiGlu, false><<<grid, kGgNT, 0, s>>>(a);
+    if (g) gemm_grouped_kernel<kActSwiGlu, true, false><<<grid, kGgNT, 0, s>>>(a);
+    else gemm_grouped_kernel<kActSwiGlu, false, false><<<grid, kGgNT, 0, s>>>(a);
   } else {
-    if (g) gemm_grouped_kernel<kActNone, true><<<grid, kGgNT, 0, s>>>(a);
-    else gemm_grouped_kernel<kActNone, false><<<grid, kGgNT, 0, s>>>(a);
+    if (g) gemm_grouped_kernel<kActNone, true, false><<<grid, kGgNT, 0, s>>>(a);
+    else gemm_grouped_kernel<kActNone, false, false><<<grid, kGgNT, 0, s>>>(a);
   }
   return hipGetLastError();
 }

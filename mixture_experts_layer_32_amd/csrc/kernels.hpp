@@ -84,7 +84,8 @@ int fp8w_block_m();
 // Grouped GEMM for experts with many rows (prefill), bf16 operands and
 // output: a persistent grid walks (expert, row tile, 256-column tile) items;
 // an expert's last row tile is 256, 128 or 64 rows high.  Needs N a multiple
-// of 256, K of 32, at most 2048 groups; g_tiles is not read.
+// of 256, K of 32, at most 2048 groups; g_tiles is not read.  Without g_off
+// it is a dense GEMM: one group (G = 1) of M rows, A not gathered.
 bool gemm_grouped_fits(int N, int K, int G);
 // Band layout of G row-major matrices of N rows x row_bytes: bands of
 // band_rows rows, a band as its 64-byte column blocks one after another (a

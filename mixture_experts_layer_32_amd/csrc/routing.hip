@@ -5,14 +5,16 @@
 // T_{K,N'} of each token, dispatch of the latent token copies to their
 // experts and the gate-weighted aggregation sum_{i in T} p'_i E_i(u).
 //
-//  topk_gate     one wave per token: K rounds of a wave-wide arg-max over
-//                (logit desc, expert id asc) with DPP reductions, then the
-//                gate rule.
+//  topk_gate     one wave per token: the K-th largest logit by a bitwise
+//                search over order-preserving keys (ballot counts), the set
+//                (ties at the K-th place to the lower ids), each member's
+//                rank under (logit desc, expert id asc), then the gate rule.
 //  route_masks   per block of 64 tokens, one 64-bit mask per expert of the
 //                tokens that chose it (LDS 64-bit atomic OR; integer, exact).
-//  route_scan    one workgroup: expert counts = popcounts, exclusive prefix
-//                sum over experts (offsets), and for every (block, expert)
-//                the copies of that expert in earlier blocks.
+//  route_scan    per (block, expert) the copies of that expert in earlier
+//                blocks and the expert counts (popcounts, a column scan over
+//                the blocks spread over workgroups of 64 experts), then one
+//                workgroup: exclusive prefix sum over experts (offsets).
 //  route_assign  one thread per copy (t, j): its row is the expert's offset
 //                plus the copies of the expert in earlier blocks plus the
 //                earlier tokens of its own block that chose the expert, so
@@ -119,37 +121,84 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(TopkArgs a, int tok_bloc
   }
   const int gating = a.gating;
 
-  uint32_t taken = 0;  // bit i: value i already selected
-  float my_z = 0.f;
-  int my_e = 0;
-  for (int j = 0; j < K; ++j) {
-    // lane-local best untaken value; on equal keys the smaller i (lower id)
-    uint32_t bk = 0;
-    int bi = 0;
-    float bz = -INFINITY;
+  // ---- the selected set: tau = the K-th largest key, the largest v with
+  // #{keys >= v} >= K, found bit by bit from the top (counts are ballot
+  // popcounts); a candidate with exactly K keys at or above it ends the
+  // search, those keys being the set.  Otherwise the set is every key above
+  // tau and, of the keys equal to tau, the lowest ids (id = 64 i + lane:
+  // value index first, then lane).
+  auto count_ge = [&](uint32_t v) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) c += __popcll(__ballot(key[i] >= v));
+    return c;
+  };
+  uint32_t tau = 0;
+  bool exact = false;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    const int c = count_ge(cand);
+    if (c >= K) {
+      tau = cand;
+      if (c == K) { exact = true; break; }
+    }
+  }
+  bool sel[NPL];
+  if (exact) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) sel[i] = key[i] >= tau;
+  } else {
+    int r = K - (tau == 0xffffffffu ? 0 : count_ge(tau + 1u));  // ties still to take
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-      const uint32_t kk = ((taken >> i) & 1u) ? 0u : key[i];
-      if (kk > bk) { bk = kk; bi = i; bz = z[i]; }
+      const bool eq = key[i] == tau;
+      const uint64_t m = __ballot(eq);
+      const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+      sel[i] = key[i] > tau || (eq && below < r);
+      r -= __popcll(m);
     }
-    const uint32_t wk = wave_max_u32(bk);
-    const uint64_t holders = __ballot(bk == wk);
-    int wl;
-    if (__popcll(holders) == 1) {
-      wl = __ffsll(static_cast<unsigned long long>(holders)) - 1;
-    } else {  // equal logits on several lanes: the lowest expert id wins
-      const uint32_t myid = bk == wk ? static_cast<uint32_t>(bi * 64 + lane) : 0xffffffffu;
-      wl = static_cast<int>(wave_min_u32(myid) & 63u);
+  }
+  // ---- the K selected values to lanes 0..K-1 (in id order, through this
+  // wave's LDS row; one wave's LDS operations complete in order)
+  __shared__ uint32_t s_key[4][64];
+  __shared__ int s_id[4][64];
+  __shared__ float s_z[4][64];
+  const int w = threadIdx.x >> 6;
+  {
+    int pos = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const uint64_t m = __ballot(sel[i]);
+      if (sel[i]) {
+        const int q = pos + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                static_cast<uint32_t>(m >> 32),
+                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+        s_key[w][q] = key[i];
+        s_id[w][q] = i * 64 + lane;
+        s_z[w][q] = z[i];
+      }
+      pos += __popcll(m);
     }
-    if (lane == wl) taken |= 1u << bi;
-    const int we = __builtin_amdgcn_readlane(bi * 64 + lane, wl);
-    const float wz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bz), wl));
-    if (lane == j) { my_z = wz; my_e = we; }
+  }
+  const bool mine = lane < K;
+  const uint32_t my_key = mine ? s_key[w][lane] : 0u;
+  const int my_e = mine ? s_id[w][lane] : 0;
+  const float my_z = mine ? s_z[w][lane] : 0.f;
+  // rank under (key desc, id asc): the selected values that come before
+  const uint64_t my_c = (static_cast<uint64_t>(my_key) << 32) | (0xffffffffu - static_cast<uint32_t>(my_e));
+  int rank = 0;
+  for (int q = 0; q < K; ++q) {
+    const uint64_t c = (static_cast<uint64_t>(__builtin_amdgcn_readlane(my_key, q)) << 32) |
+                       (0xffffffffu - static_cast<uint32_t>(__builtin_amdgcn_readlane(my_e, q)));
+    rank += c > my_c ? 1 : 0;
   }
 
-  // ---- gates (rule from the layer configuration)
-  const bool mine = lane < K;
-  const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), 0));
+  // ---- gates (rule from the layer configuration); zmax is the first
+  // selected logit
+  const uint64_t first = __ballot(mine && rank == 0);
+  const int l0 = __ffsll(static_cast<unsigned long long>(first)) - 1;
+  const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), l0));
   float g;
   if (gating == 2) {  // sigmoid, normalised over the selected set
     const float sgm = mine ? 1.f / (1.f + expf(-my_z)) : 0.f;
@@ -169,8 +218,8 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(TopkArgs a, int tok_bloc
     g = ex / tot;
   }
   if (mine) {
-    a.idx[(int64_t)t * K + lane] = my_e;
-    a.gate[(int64_t)t * K + lane] = g;
+    a.idx[(int64_t)t * K + rank] = my_e;
+    a.gate[(int64_t)t * K + rank] = g;
   }
 }
 
@@ -232,41 +281,64 @@ __device__ void expert_scan(const int (&cnt)[2], int N, int tile_m, int* s_cnt, 
   __syncthreads();
 }
 
-// One workgroup of 1024 threads; N <= 2048.
-__global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __restrict__ masks,
-                                                          int nblk, int N, int tile_m,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ base,
-                                                          int32_t* __restrict__ tiles,
-                                                          int32_t* __restrict__ active) {
+// Per expert, the copies in earlier routing blocks (base) and the total
+// (counts): a column scan of the [nblk][N] mask popcounts.  Workgroup x
+// takes experts 64 x .. 64 x + 63 (one per lane, so each load instruction
+// reads 512 contiguous bytes) and its 16 waves split the blocks into 16
+// ranges: a range's sum, the sums of the earlier ranges through LDS, then
+// the range again (from L2) for the running values.
+__global__ __launch_bounds__(1024) void route_colscan_kernel(const uint64_t* __restrict__ masks,
+                                                             int nblk, int N,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ base) {
+  __shared__ int s_part[16][64];
+  const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int per = (nblk + 15) / 16;
+  const int b0 = min(nblk, r * per), b1 = min(nblk, b0 + per);
+  const int ec = e < N ? e : N - 1;  // loads stay in bounds; results of e >= N are dropped
+  int sum = 0;
+  for (int b = b0; b < b1; b += 8) {  // 8 independent loads in flight
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? masks[(int64_t)(b + u) * N + ec] : 0ull;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += __popcll(v[u]);
+  }
+  s_part[r][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int i = 0; i < r; ++i) run += s_part[i][lane];
+  if (e >= N) return;
+  if (r == 15) counts[e] = run + sum;
+  for (int b = b0; b < b1; b += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? masks[(int64_t)(b + u) * N + e] : 0ull;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b + u < b1) base[(int64_t)(b + u) * N + e] = run;
+      run += __popcll(v[u]);
+    }
+  }
+}
+
+// Exclusive prefix of the counts over the experts (offsets, tiles, the
+// list of experts with copies): one workgroup of 1024 threads; N <= 2048.
+__global__ __launch_bounds__(1024) void route_offsets_kernel(const int32_t* __restrict__ counts,
+                                                             int N, int tile_m,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tiles,
+                                                             int32_t* __restrict__ active) {
   __shared__ int s_cnt[2048];
   __shared__ int s_til[2048];
   __shared__ int s_wsum[2][16];
   const int tid = threadIdx.x;
-  int cnt[2] = {0, 0};
+  int cnt[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int e = tid + h * 1024;
-    if (e < N) {
-      int run = 0;
-      int b = 0;
-      for (; b + 8 <= nblk; b += 8) {  // 8 independent loads in flight
-        uint64_t v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = masks[(int64_t)(b + u) * N + e];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          base[(int64_t)(b + u) * N + e] = run;
-          run += __popcll(v[u]);
-        }
-      }
-      for (; b < nblk; ++b) {
-        base[(int64_t)b * N + e] = run;
-        run += __popcll(masks[(int64_t)b * N + e]);
-      }
-      cnt[h] = run;
-    }
+    cnt[h] = e < N ? counts[e] : 0;
   }
   int total_c, total_t;
   expert_scan(cnt, N, tile_m, s_cnt, s_til, s_wsum, total_c, total_t);
@@ -274,7 +346,6 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const uint64_t* __rest
   for (int h = 0; h < 2; ++h) {
     const int e = tid + h * 1024;
     if (e < N) {
-      counts[e] = cnt[h];
       offsets[e] = s_cnt[e];
       if (tiles) tiles[e] = s_til[e];
       // one "tile" per expert with copies: s_til is its rank among them
@@ -393,7 +464,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
 }
 
 // One workgroup per token; thread c handles 16 bytes of the output row.  The
-// K expert rows are fetched U (8, 16 or 32, the smallest >= K) at a time
+// K expert rows are fetched U (8, 16, 24 or 32, the smallest >= K) at a time
 // (independent loads in flight) and added in j order.
 template <typename T, int U>
 __global__ __launch_bounds__(512) void combine_kernel(const T* __restrict__ Y,
@@ -473,6 +544,8 @@ void launch_topk_npl(const TopkArgs& a, int spl, dim3 grid, int tok_blocks, hipS
     if (spl == 8) return topk_gate_kernel<NPL, 8><<<grid, block, 0, s>>>(a, tok_blocks);
   if constexpr (NPL * 4 <= 128)
     if (spl == 4) return topk_gate_kernel<NPL, 4><<<grid, block, 0, s>>>(a, tok_blocks);
+  if constexpr (NPL * 2 <= 128)
+    if (spl == 2) return topk_gate_kernel<NPL, 2><<<grid, block, 0, s>>>(a, tok_blocks);
   topk_gate_kernel<NPL, 1><<<grid, block, 0, s>>>(a, tok_blocks);
 }
 
@@ -492,7 +565,11 @@ hipError_t launch_topk_gate(const TopkArgs& a, hipStream_t s) {
   const int npl = (N + 63) / 64;
   // partial sets loaded at once: a power of two >= lsplits, at most 128
   // values per lane
-  int spl = a.lsplits <= 1 ? 1 : a.lsplits <= 4 ? 4 : a.lsplits <= 8 ? 8 : a.lsplits <= 16 ? 16 : 1;
+  int spl = a.lsplits <= 1   ? 1
+            : a.lsplits <= 2 ? 2
+            : a.lsplits <= 4 ? 4
+            : a.lsplits <= 8 ? 8
+            : a.lsplits <= 16 ? 16 : 1;
   const int npl_c = npl <= 1 ? 1 : npl <= 2 ? 2 : npl <= 4 ? 4 : npl <= 8 ? 8 : npl <= 14 ? 14
                     : npl <= 16 ? 16 : 32;
   if (spl * npl_c > 128) spl = 1;
@@ -521,8 +598,9 @@ hipError_t launch_route_scan(const uint64_t* masks, int nblk, int N, int tile_m,
                              int32_t* active) {
   if (N > 2048 || tile_m <= 0) return hipErrorInvalidValue;
   if (active && (!tiles || tile_m < kActiveTile)) return hipErrorInvalidValue;
-  route_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(masks, nblk, N, tile_m, counts, offsets, base,
-                                                   tiles, active);
+  if (N < 1 || nblk < 0) return hipErrorInvalidValue;
+  route_colscan_kernel<<<dim3((N + 63) / 64), dim3(1024), 0, s>>>(masks, nblk, N, counts, base);
+  route_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(counts, N, tile_m, offsets, tiles, active);
   return hipGetLastError();
 }
 
@@ -552,11 +630,12 @@ template <typename T>
 void launch_combine_t(const T* Y, const int32_t* slot_of, const float* gate, int T_, int K, int l,
                       const float* R, T* v, hipStream_t s) {
   // one thread per 16-byte chunk of the row (up to 512 threads, then a
-  // loop); as many expert rows in flight as the token has (8, 16 or 32)
+  // loop); as many expert rows in flight as the token has (8, 16, 24 or 32)
   const int chunks = l / (16 / static_cast<int>(sizeof(T)));
   const dim3 grid(T_), block(std::min(512, (chunks + 63) / 64 * 64));
   if (K <= 8) combine_kernel<T, 8><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
   else if (K <= 16) combine_kernel<T, 16><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
+  else if (K <= 24) combine_kernel<T, 24><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
   else combine_kernel<T, 32><<<grid, block, 0, s>>>(Y, slot_of, gate, K, l, R, v);
 }
 

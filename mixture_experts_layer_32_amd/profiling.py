@@ -71,7 +71,10 @@ def expert_kernel_kind(name: str) -> str | None:
     if "ffn_stream_kernel" in name:
         return "ffn_stream"
     if "gemm_grouped_kernel<" in name:
-        return "gemm_grouped"
+        # the third template argument (DENSE) marks the dense projections
+        # run on the same tiles
+        args = [a.strip() for a in name.split("<", 1)[1].split(">(")[0].split(",")]
+        return None if len(args) > 2 and args[2] == "true" else "gemm_grouped"
     if "gemm_fp8w_kernel<" in name:
         return "gemm_fp8w"
     if "gemm_stream_kernel<" in name:

@@ -363,18 +363,23 @@ def test_full_size_packed_weights_bit_identical(name):
 
 # Sizes that select (256 x 256 dense, 128 x 256 grouped,
 # 128 x 128 dense) with ragged row and column tails, on sampled tokens.
+# ragged_dense_grouped: enough rows for W_down and W_up to run in the
+# persistent grouped kernel as one group (256 x 256 tiles, at least one per
+# compute unit), the last row tile 188 rows high; the experts run grouped too.
 MID = {
     "ragged_large_tiles": (LayerSpec(d=2064, l=1040, m=528, n_experts=64, top_k=4,
-                                     gating="softmax_topk"), 8200),
+                                     gating="softmax_topk"), 8200, "tiled"),
+    "ragged_dense_grouped": (LayerSpec(d=2048, l=512, m=512, n_experts=32, top_k=4,
+                                       gating="softmax_topk"), 32700, "grouped"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MID))
 def test_mid_size_large_tiles_sampled_tokens(name):
-    spec, T = MID[name]
+    spec, T, regime = MID[name]
     w, x = _case(spec, T, seed=3)
     g, layer = run_gpu(spec, w, x)
-    assert layer.expert_regime(T) == "tiled"
+    assert layer.expert_regime(T) == regime
     check_routing_structure(spec, g, T)
     st = check_against_oracle(spec, w, x, g, tokens=_sample_tokens(T, n=40, seed=9))
     print(name, st, flush=True)

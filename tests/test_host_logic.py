@@ -49,12 +49,15 @@ NAMES = {
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 1>"
     "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc1"),
-    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<1, true>(lmoe::GemmArgs)":
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<1, true, false>(lmoe::GemmArgs)":
         ("gemm_grouped", "fc1"),
-    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<2, true>(lmoe::GemmArgs)":
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<2, true, false>(lmoe::GemmArgs)":
         ("gemm_grouped", "fc1"),
-    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<0, false>(lmoe::GemmArgs)":
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<0, false, false>(lmoe::GemmArgs)":
         ("gemm_grouped", "fc2"),
+    # the same kernel as a dense GEMM (W_down, W_up) is not an expert kernel
+    "void lmoe::(anonymous namespace)::gemm_grouped_kernel<0, false, true>(lmoe::GemmArgs)":
+        (None, None),
     # the same tile without activation is shared with the dense projections
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 0>"
