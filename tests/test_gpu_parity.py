@@ -371,6 +371,12 @@ MID = {
                                      gating="softmax_topk"), 8200, "tiled"),
     "ragged_dense_grouped": (LayerSpec(d=2048, l=512, m=512, n_experts=32, top_k=4,
                                        gating="softmax_topk"), 32700, "grouped"),
+    # expert GEMMs only on the grouped kernel (W_down / W_up too small for it)
+    # with several items per compute unit: FC1 about 580, FC2 about 290
+    # (expert, row tile, column tile) items over the 256 workgroups, so each
+    # workgroup walks more than one tile and tile heights change along a walk
+    "grouped_many_items": (LayerSpec(d=512, l=512, m=1024, n_experts=16, top_k=4,
+                                     gating="softmax_all", has_router_bias=True), 8191, "grouped"),
 }
 
 
