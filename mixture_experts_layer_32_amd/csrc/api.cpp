@@ -737,6 +737,9 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
     a.M = Ti; a.N = l; a.K = d;
     if (p.down_grouped) {
       a.a_nrows = Ti; a.max_rows = Ti;
+      // grouped experts: the blocked copy of u that FC1 gathers from, stored
+      // beside u by the same launch
+      if (p.grouped) a.C2 = ws + p.ublk;
       LMOE_TRY(lmoe::launch_gemm_grouped(a, s), "W_down GEMM (grouped)");
     } else {
       LMOE_TRY(lmoe::launch_gemm_tiled(a, adt, adt, p.down.tile, s, p.down.splits, partial,
@@ -828,8 +831,10 @@ lmoe_status latentmoe_forward_overlap(const lmoe_handle* h, const lmoe_weights* 
       // u in 32-column blocks over its T rows: the rows FC1 gathers for an
       // expert are mostly consecutive tokens, whose K-stage pieces then sit
       // side by side
+      // (written by the W_down launch when it runs on the grouped kernel)
       void* ub = ws + p.ublk;
-      LMOE_TRY(lmoe::launch_pack_bands(u, ub, 1, Ti, l * ab, Ti, s), "u in blocks");
+      if (!p.down_grouped)
+        LMOE_TRY(lmoe::launch_pack_bands(u, ub, 1, Ti, l * ab, Ti, s), "u in blocks");
       a.A = ub; a.a_kblock = Ti;
       // H in 32-column blocks, so that FC2 loads each K stage of its rows as
       // one contiguous block; W1 in 256-row bands when a packed copy is given

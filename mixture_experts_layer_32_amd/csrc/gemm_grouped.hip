@@ -132,7 +132,7 @@ __device__ __forceinline__ void gg_fetch_rows(const GemmArgs& p, int total_rows,
 // One tile of height 64 * MI: main loop over K, then the epilogue.  The
 // tile's source rows are in gg_rows[buf] (when A is gathered); next_row0 >= 0
 // asks for the next tile's to be fetched into the other buffer.
-template <int MI, int ACT, bool GATHER>
+template <int MI, int ACT, bool GATHER, bool DENSE>
 __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int wave, int lane_in,
                                         GgAcc& acc, int buf, int next_row0, int total_rows) {
   // the lane index, opaque to the compiler per tile: the index arithmetic of
@@ -353,6 +353,17 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& p, const GgTile& t, int 
       // (FC1: 2 % faster)
       __builtin_amdgcn_raw_buffer_store_b128(val, c_rsrc, !cblk || r < t.rows ? off : kOutOfRange,
                                              0, kCpolNonTemporal);
+      // dense: the optional blocked copy (C2, M rows per block), rows past
+      // the tile offset out of range per lane
+      if constexpr (DENSE) {
+        if (p.C2 != nullptr) {
+          const BufRsrc c2_rsrc = make_rsrc(p.C2, static_cast<uint64_t>(p.M) * p.N * 2);
+          const uint32_t off2 =
+              static_cast<uint32_t>((ccol >> 5) * p.M + t.row0 + r) * 64u +
+              static_cast<uint32_t>(ccol & 31) * 2u;
+          __builtin_amdgcn_raw_buffer_store_b128(val, c2_rsrc, r < t.rows ? off2 : kOutOfRange, 0, 0);
+        }
+      }
     }
   }
 }
@@ -455,9 +466,9 @@ __global__ __launch_bounds__(kGgNT, 1) void gemm_grouped_kernel(GemmArgs p) {
       for (int b = 0; b < kGgNJ; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-    if (t.rows > 128) gg_tile<4, ACT, GATHER>(p, t, wave, lane, acc, buf, next_row0, total_rows);
-    else if (t.rows > 64) gg_tile<2, ACT, GATHER>(p, t, wave, lane, acc, buf, next_row0, total_rows);
-    else gg_tile<1, ACT, GATHER>(p, t, wave, lane, acc, buf, next_row0, total_rows);
+    if (t.rows > 128) gg_tile<4, ACT, GATHER, DENSE>(p, t, wave, lane, acc, buf, next_row0, total_rows);
+    else if (t.rows > 64) gg_tile<2, ACT, GATHER, DENSE>(p, t, wave, lane, acc, buf, next_row0, total_rows);
+    else gg_tile<1, ACT, GATHER, DENSE>(p, t, wave, lane, acc, buf, next_row0, total_rows);
   }
 }
 
@@ -508,6 +519,11 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) {
   // dense: one group of M rows, A not gathered, every row of A and C there
   if (a.g_off == nullptr &&
       (a.G != 1 || a.M <= 0 || a.a_rows || a.a_nrows < a.M || a.max_rows < a.M))
+    return hipErrorInvalidValue;
+  // the blocked copy: dense, no activation, whole 32-column blocks, 32-bit offsets
+  if (a.C2 && (a.g_off != nullptr || a.act != kActNone || a.N % 32 ||
+               (uint64_t)a.M * a.N * 2 >= (1ull << 31) ||
+               (reinterpret_cast<uintptr_t>(a.C2) & 15u)))
     return hipErrorInvalidValue;
   const int out_cols = a.act == kActSwiGlu ? a.N / 2 : a.N;
   if (a.c_kblock == 0 && a.ldc < out_cols) return hipErrorInvalidValue;

@@ -60,6 +60,10 @@ struct GemmArgs {
   // one after another (launch_pack_bands; 256-row bands for the bf16
   // grouped kernel, 16-row bands for the fp8 one); ldb == K
   int b_bands = 0;
+  // dense grouped kernel only (no g_off, no activation): a second copy of C
+  // in 32-column blocks over the M rows (block b: columns 32 b .. 32 b + 31
+  // of rows 0 .. M - 1, 64 bytes per row), written beside the row-major C
+  void* C2 = nullptr;
 };
 
 // LDS-tiled MFMA GEMM.  tile: 0 = 128x128, 1 = 64x64, 2 = 256x256,
