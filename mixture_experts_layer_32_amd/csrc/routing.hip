@@ -464,6 +464,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
 }
 
 // One workgroup per token; thread c handles 16 bytes of the output row.  The
+// Y rows are read once, non-temporally (prefill: 144 -> 136 us per call).  The
 // K expert rows are fetched U (8, 16, 24 or 32, the smallest >= K) at a time
 // (independent loads in flight) and added in j order.
 template <typename T, int U>
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const T* __restrict__ Y,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = min(j0 + u, K - 1);
-        y[u] = load_chunk(Y + (int64_t)so[j] * l + c * EPC);
+        y[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Y + (int64_t)so[j] * l + c * EPC));
         gw[u] = j0 + u < K ? gt[j] : 0.f;
       }
       __builtin_amdgcn_sched_barrier(0);

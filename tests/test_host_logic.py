@@ -42,9 +42,9 @@ NAMES = {
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, lmoe::TileCfg<128, 256, 2, 2, 4, 3, 2>, 2>"
     "(lmoe::GemmArgs, int, float*)": ("gemm_tiled", "fc1"),
-    "void lmoe::(anonymous namespace)::gemm_fp8w_kernel<0, true>(lmoe::GemmArgs)":
+    "void lmoe::(anonymous namespace)::gemm_fp8w_kernel<0, true, true>(lmoe::GemmArgs)":
         ("gemm_fp8w", "fc2"),
-    "void lmoe::(anonymous namespace)::gemm_fp8w_kernel<1, true>(lmoe::GemmArgs)":
+    "void lmoe::(anonymous namespace)::gemm_fp8w_kernel<1, true, false>(lmoe::GemmArgs)":
         ("gemm_fp8w", "fc1"),
     "void lmoe::(anonymous namespace)::gemm_tiled_kernel<lmoe::MmaBf16x32, unsigned short, "
     "unsigned short, lmoe::TileCfg<256, 256, 2, 4, 4, 4, 1>, 1>"
