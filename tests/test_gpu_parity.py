@@ -68,6 +68,17 @@ SMALL = {
     "single_expert": (LayerSpec(d=128, l=64, m=64, n_experts=1, top_k=1), 50),
     "k64_n128": (LayerSpec(d=128, l=64, m=64, n_experts=128, top_k=64, gating="sigmoid_topk_norm"), 30),
     "n2048": (LayerSpec(d=128, l=64, m=64, n_experts=2048, top_k=16), 64),
+    # the largest N with the largest K: the top-k search fills all 64 lanes
+    "n2048_k64": (LayerSpec(d=128, l=64, m=64, n_experts=2048, top_k=64,
+                            gating="sigmoid_topk_norm"), 70),
+    # dispatch in three kernels, the column scan over 300 experts (a last
+    # workgroup of 44) and 32 token blocks
+    "route_scan_n300": (LayerSpec(d=256, l=64, m=128, n_experts=300, top_k=6,
+                                  gating="softmax_all", has_router_bias=True), 2000),
+    # the column scan over 313 token blocks (its waves take 20 blocks each:
+    # two full batches of 8 and a remainder of 4)
+    "route_scan_313_blocks": (LayerSpec(d=256, l=256, m=256, n_experts=40, top_k=2,
+                                        gating="softmax_topk"), 20000),
 }
 
 
