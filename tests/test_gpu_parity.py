@@ -71,6 +71,11 @@ SMALL = {
     # the largest N with the largest K: the top-k search fills all 64 lanes
     "n2048_k64": (LayerSpec(d=128, l=64, m=64, n_experts=2048, top_k=64,
                             gating="sigmoid_topk_norm"), 70),
+    # W_down and the router in one launch over x on 128 x 128 tiles with K
+    # split in two (the fp32-output plan for 128-255 such tiles), the top-k
+    # kernel finishing u from the partials
+    "front_tile128_split": (LayerSpec(d=1024, l=512, m=128, n_experts=2048, top_k=8,
+                                      gating="softmax_all"), 832),
     # dispatch in three kernels, the column scan over 300 experts (a last
     # workgroup of 44) and 32 token blocks
     "route_scan_n300": (LayerSpec(d=256, l=64, m=128, n_experts=300, top_k=6,
