@@ -344,6 +344,21 @@ def _read_kv(path):
     return kv
 
 
+def _expert_weight_bytes(cfg, touched):
+    """Expert-weight bytes that FC1 + FC2 of one layer call must read: both
+    matrices of every expert with tokens (SwiGLU: FC1 holds up and gate
+    rows; fp8: with the row scales), the benchmark's algorithmic bytes of the
+    two expert GEMMs.  Token rows, H and Y are intermediates."""
+    l, m = cfg["l"], cfg["m"]
+    m1 = 2 * m if cfg.get("activation") == "swiglu" else m
+    dt = cfg["expert_dtype"]
+    if dt == "bf16":
+        return float(touched * l * (m1 + m) * 2)
+    if dt == "fp8_e4m3_rowscale":
+        return float(touched * (l * (m1 + m) + 4 * (m1 + l)))
+    raise ValueError("sweep summary: expert dtype %s not handled" % dt)
+
+
 def write_sweep_md(entries, out):
     """Table of the alpha sweep: per (workload, T) the step time, the expert
     stages' event times, their algorithmic bytes (from the bench line) and
@@ -368,7 +383,7 @@ def write_sweep_md(entries, out):
         with open(bj) as f:
             b = json.loads(f.read().strip().splitlines()[-1])
         cfg = b["config"]
-        alg = sum(b["experts"]["algorithmic_bytes"].values())
+        alg = _expert_weight_bytes(cfg, b["experts"]["touched"])
         kind = REGIME_KERNEL[cfg["expert_kernel"]]
         name = wl + ("" if int(T) == 512 else "_T%s" % T)
         kv = _read_kv(hbm_file(name, kind))

@@ -94,3 +94,20 @@ def test_shared_experts_add_their_weights_and_flops():
     b1, f1 = bench.layer_work(sh, 512, c)
     assert b1 - b0 == 2 * 4096 * (2 * 1536) * 2         # Ws1 and Ws2, bf16
     assert f1 - f0 == 4 * 512 * 4096 * (2 * 1536)
+
+
+@pytest.mark.parametrize("name", ["t2_std", "t2_eff_a4", "t2_acc_a4", "latent_swiglu_decode",
+                                  "latent_fp8_sparse"])
+def test_sweep_summary_bytes_equal_the_bench_definition(name):
+    """The alpha-sweep summary recomputes FC1 + FC2's algorithmic bytes
+    from a bench line's config and touched-expert count; they equal the
+    benchmark's own expert-weight bytes of the two GEMMs."""
+    from mixture_experts_layer_32_amd import profiling
+    spec = workload(name).spec
+    counts = np.zeros(spec.n_experts, np.int64)
+    counts[::3] = 5                                    # a third of the experts touched
+    touched = int((counts > 0).sum())
+    cfg = {"l": spec.l, "m": spec.m, "activation": spec.activation,
+           "expert_dtype": spec.expert_dtype}
+    want = bench.expert_weight_bytes(spec, counts, "fc1") + bench.expert_weight_bytes(spec, counts, "fc2")
+    assert profiling._expert_weight_bytes(cfg, touched) == want
